@@ -1,0 +1,11 @@
+"""The CPU oracle against its pins (hand-worked fixtures, library routines, brute force,
+closed forms and invariants).  CPU only."""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.default())
