@@ -1,0 +1,176 @@
+/*
+ * qmm.h -- C ABI of libqmm: block-quantized weight x q8_1 activation products on MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [PF] #2356 "pf_wmma: a second Volta prompt-expert kernel for IQ2_S gate/up and IQ4_NL down"
+ *   [DQ] #1525 "prefill: dense IQ4_XS / Q8_0 to FP16 with 16-byte stores, swiglu + q8_1 and the
+ *        MoE combine + hyper-connection write fused"
+ *   [IQ] #242  "IQ kernels: decode each weight part once for every column and entry, bitwise identical"
+ *   [GP] #1424 "Pascal GP100: a Q8_0 decode GEMV ... and IQ3_XXS / IQ3_S tables in shared memory"
+ *
+ * General rules for every entry point:
+ *   - All pointers are DEVICE pointers unless a comment says "host".  The caller owns every
+ *     buffer; the library allocates nothing and keeps no state between calls (reentrant).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
+ *     asynchronous on that stream; outputs are ready when the stream reaches the call.
+ *   - Argument errors are reported synchronously by the return value, before anything is
+ *     launched; a launch error is reported as QMM_EHIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.
+ *   - Weight formats (little-endian, every block starts with its fp16 scale d):
+ *       QMM_Q8_0   34 B per 32 values : d, int8 q[32]                    value = d*q
+ *       QMM_IQ4_NL 18 B per 32 values : d, 16 bytes of 4-bit indices into the sixteen IQ4_NL
+ *                                       levels; value j<16 = low nibble of byte j, j>=16 = high
+ *                                       nibble of byte j-16                value = d*level
+ *       QMM_CB3   110 B per 256 values: d, qs[64], qh[8], signs[32], scales[4] (IQ3_S-like
+ *                                       codebook: 9-bit index = qs[i] | bit i%8 of qh[i/8] << 8
+ *                                       selects 4 magnitudes from `grid`; sign bit v%8 of
+ *                                       signs[v/8]; sub-block s of 32 values has multiplier
+ *                                       1 + 2*((scales[s/2] >> 4*(s%2)) & 15))
+ *     A weight matrix is row-major: nrows rows of qmm_row_bytes(wtype, k) bytes each.
+ *     `grid` (CB3 only) is 512 entries x 4 uint8 magnitudes (2048 bytes), each in [1, 63].
+ *   - q8_1 activations: 36 B per 32 values = fp16 d, fp16 s, int8 q[32]; a column of k values
+ *     is k/32 consecutive blocks, columns are consecutive ([ncols][k/32][36]).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* weight formats */
+#define QMM_Q8_0 1
+#define QMM_IQ4_NL 2
+#define QMM_CB3 3
+
+/* status codes */
+#define QMM_OK 0
+#define QMM_EINVAL (-1)       /* bad argument: null pointer, size out of range, ... */
+#define QMM_EUNSUPPORTED (-2) /* a shape or format the kernels decline (caller keeps another path) */
+#define QMM_EALIGN (-3)       /* a pointer or stride is not aligned as documented */
+#define QMM_EHIP (-4)         /* the HIP runtime reported an error at launch */
+#define QMM_ESPACE (-5)       /* workspace smaller than the *_workspace() query returned */
+
+/* flags */
+#define QMM_FLAG_DEBUG_INTERMEDIATES 1u /* also write fp32 intermediates into the workspace */
+
+/* Version of this ABI (major*100 + minor). */
+int qmm_version(void);
+
+/* Host-only.  Human-readable text of a status code (never NULL). */
+const char* qmm_status_str(int status);
+
+/* Host-only.  Bytes of one weight row of k values, or 0 when k is not a positive multiple of
+ * the format's block (32 values; 256 for CB3) or wtype is unknown. */
+int64_t qmm_row_bytes(int wtype, int64_t k);
+
+/* q8_1 quantization of activations [DQ, Change: the q8_1 quantizer's 32-value blocks; GP, What
+ * changed: q8_1 activations].  Per 32-value block: amax = max |x|; d = amax/127 (binary32);
+ * q_j = x_j/d (binary32 division) rounded half away from zero; an all-zero block gives
+ * d = q = s = 0; stored d = fp16(d), s = fp16(d * sum q).
+ *   x   : float [ncols][ldx], column c's k values at x + c*ldx; ldx >= k; 4-byte aligned.
+ *   xq  : output, ncols*(k/32)*36 bytes, 4-byte aligned.
+ *   k   : multiple of 32, > 0.  ncols >= 1.
+ * Errors: QMM_EINVAL (null, k, ncols, ldx), QMM_EALIGN. */
+int qmm_quantize_q8_1(const float* x, int64_t k, int ncols, int64_t ldx, void* xq, void* stream);
+
+/* FP16 dequantization [DQ, Change: dequant to FP16 with 16-byte stores; PF, Summary: the FP16
+ * weights the tensor cores get].  out[r*ld + j] = binary16 nearest-even rounding of the exact
+ * value of weight (r, j); columns k..ld-1 are not written.
+ *   w    : nrows * qmm_row_bytes(wtype, k) bytes, 2-byte aligned.
+ *   grid : CB3 codebook (2048 bytes), ignored (may be NULL) for other formats.
+ *   out  : uint16 (binary16 bits) [nrows][ld], ld >= k, 2-byte aligned.  When out is 16-byte
+ *          aligned and ld % 8 == 0 every thread writes 8 values with one 16-byte store.
+ * Errors: QMM_EINVAL, QMM_EALIGN. */
+int qmm_dequant_f16(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
+                    uint16_t* out, int64_t ld, void* stream);
+
+/* Dense multi-column decode GEMV [IQ, What it does: the weight side is loaded and decoded once
+ * and applied to every column, 1/2/4/8 columns per pass, 8 at a time beyond 8; GP, What
+ * changed: 16-byte weight loads, activations staged once per workgroup].
+ *   y[c*ldy + r] = sum over 32-value blocks b of  (d_w(r,b) * d_a(c,b)) * isum(r,b,c)
+ * in binary32, isum the exact integer dot of the block's integer weight factors with the q8_1
+ * int8 values (for CB3 the sub-block multiplier is folded into isum).  Every column of an
+ * n-column call is bitwise equal to a one-column call on that column.
+ *   w    : nrows x qmm_row_bytes(wtype, k) bytes, 4-byte aligned.
+ *   grid : CB3 codebook or NULL.
+ *   xq   : q8_1 [ncols][k/32][36], 4-byte aligned.   y: float, ldy >= nrows, 4-byte aligned.
+ *   k    : multiple of 64 for Q8_0 / IQ4_NL (blocks are read in 4-byte aligned pairs), of 256
+ *          for CB3; at most 32768.  ncols >= 1 (any count; passes of 8).
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (k not a multiple of 64 / 256, k too large). */
+int qgemv_dense(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
+                const void* xq, int ncols, float* y, int64_t ldy, void* stream);
+
+/* Test hook: the per-block integer sums isum(r, b, c) of qgemv_dense, computed by the same
+ * device decode and dot code.  sums: int32 [ncols][nrows][k/32].  Same argument rules as
+ * qgemv_dense. */
+int qmm_debug_block_sums(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
+                         const void* xq, int ncols, int32_t* sums, void* stream);
+
+/* Workspace bytes qgemv_grouped_experts needs (host). */
+size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned flags);
+
+/* Grouped MoE-expert decode [IQ, What it does: native_gu / native_down decode each weight part
+ * once for every entry of a group; DQ, Change: swiglu then q8_1 of H for the down product].
+ * Groups are experts; entries are the (token, slot) pairs routed to them.  For group g (expert
+ * e = group_expert[g]) and every entry j in [group_entry_off[g], group_entry_off[g+1]):
+ *   x  = q8_1 column entry_col[j] of xq (width hidden)
+ *   gv = W_gate[e] x,  uv = W_up[e] x          (qgemv_dense arithmetic, inter rows)
+ *   h  = silu(gv) * uv,  silu(z) = z / (1 + exp(-z)), binary32
+ *   H  = q8_1(h) per 32 consecutive intermediate values          (workspace)
+ *   y[j*hidden + r] = (W_down[e] H)[r]                            (binary32; unweighted)
+ *   w_gate, w_up : expert e's matrix at byte offset e*gu_expert_stride, inter rows of width
+ *                  hidden, format wtype_gu;  w_down: offset e*down_expert_stride, hidden rows of
+ *                  width inter, format wtype_down.  All 4-byte aligned; strides multiples of 4.
+ *   group_expert[ngroups], group_entry_off[ngroups+1], entry_col[nentries]: int32, device.
+ *                  Offsets must be non-decreasing and within [0, nentries]; entries outside
+ *                  every group are not written.
+ *   ws   : workspace of qgemv_grouped_experts_workspace() bytes, 16-byte aligned.  Layout:
+ *          H q8_1 [nentries][inter/32][36] first; with QMM_FLAG_DEBUG_INTERMEDIATES then
+ *          gv, uv as float [nentries][inter] (each starting 16-byte aligned).
+ *   hidden: multiple of 256 (CB3) or 64;  inter: multiple of 64 (256 for CB3 down).
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_ESPACE. */
+int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up,
+                          int64_t gu_expert_stride, int wtype_down, const void* w_down,
+                          int64_t down_expert_stride, const uint8_t* grid, int64_t hidden,
+                          int64_t inter, const void* xq, const int32_t* group_expert,
+                          const int32_t* group_entry_off, int ngroups, const int32_t* entry_col,
+                          int nentries, float* y, void* ws, size_t ws_bytes, unsigned flags,
+                          void* stream);
+
+/* Workspace bytes qgemm_prefill_experts needs (host). */
+size_t qgemm_prefill_experts_workspace(int nexperts, int64_t inter, int64_t nentries,
+                                       unsigned flags);
+
+/* Prefill grouped expert GEMM [PF, Summary: weights of one expert dequantized to FP16 in the
+ * workgroup's shared memory, FP16 matrix-core math with FP32 sums, over the rows sorted per
+ * expert].  For expert e, entries p in [expert_off[e], expert_off[e+1]), token t = sorted_tok[p]:
+ *   G = X16[t] . Wg16[e]^T,  U = X16[t] . Wu16[e]^T     (FP16 products, FP32 sums; Wg16/Wu16 are
+ *                                                        the qmm_dequant_f16 values)
+ *   H16 = fp16(silu(G) * U)                              (workspace)
+ *   y[p*hidden + j] = (H16 . Wd16[e]^T)[j]               (FP32, one row per sorted entry)
+ *   x_f16      : binary16 [ntok][hidden], 16-byte aligned.
+ *   sorted_tok : int32 [nentries] (each in [0, ntok)); expert_off: int32 [nexperts+1],
+ *                non-decreasing, expert_off[nexperts] == nentries.
+ *   w_gate, w_up (format wtype_gu, inter rows of width hidden) and w_down (wtype_down, hidden
+ *   rows of width inter) at e * stride; 4-byte aligned.
+ *   ws : qgemm_prefill_experts_workspace() bytes, 16-byte aligned.  Layout: H16 [nentries][inter]
+ *        binary16 first, then the tile schedule; with QMM_FLAG_DEBUG_INTERMEDIATES then G, U
+ *        float [nentries][inter].
+ *   hidden, inter: multiples of 256.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_ESPACE. */
+int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const void* w_up,
+                          int64_t gu_expert_stride, int wtype_down, const void* w_down,
+                          int64_t down_expert_stride, int nexperts, int64_t hidden, int64_t inter,
+                          const uint16_t* x_f16, int64_t ntok, const int32_t* sorted_tok,
+                          const int32_t* expert_off, int64_t nentries, float* y, void* ws,
+                          size_t ws_bytes, unsigned flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,108 @@
+"""GPU parity of the dense decode GEMV: per-block integer sums bit-exact, one-hot rows
+bit-exact, fp32 outputs within 1e-4 * sum|terms| of the oracle, every column of an n-column
+call bitwise equal to a one-column call."""
+import numpy as np
+import pytest
+
+import moe_expert_amd as M
+import oracle
+import synth
+from tests.gpu_util import check_tol, dev, host
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [M.QMM_Q8_0, M.QMM_IQ4_NL, M.QMM_CB3]
+
+
+def case(wtype, nrows, k, ncols, seed):
+    rng = synth.rng_for(seed)
+    grid = synth.cb3_grid(rng) if wtype == M.QMM_CB3 else None
+    w = synth.weights(wtype, rng, nrows, k)
+    x = synth.activations(rng, ncols, k)
+    return w, grid, x
+
+
+def gpu_gemv(wtype, w, grid, x, nrows, k, ncols):
+    xq = M.qmm_quantize_q8_1(dev(x))
+    y = M.qgemv_dense(wtype, dev(w), nrows, k, xq, ncols, grid=None if grid is None else dev(grid))
+    return host(y), host(xq)
+
+
+@pytest.mark.parametrize("wtype", FORMATS)
+@pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 3), (64, 1024, 1), (100, 2560, 8), (33, 768, 5)])
+def test_block_sums_exact(wtype, nrows, k, ncols):
+    if wtype == M.QMM_CB3 and k % 256:
+        pytest.skip("CB3 needs k % 256 == 0")
+    print(f"block sums wtype={wtype} nrows={nrows} k={k} ncols={ncols}", flush=True)
+    w, grid, x = case(wtype, nrows, k, ncols, 300 + nrows + wtype)
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.block_sums(wtype, w, k, xq, grid)
+    got = host(M.qmm_debug_block_sums(wtype, dev(w), nrows, k, dev(xq), ncols, grid=None if grid is None else dev(grid)))
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} sums differ"
+
+
+@pytest.mark.parametrize("wtype", FORMATS)
+@pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 3), (129, 2560, 8), (64, 1024, 2), (31, 6144, 7),
+                                           (1, 256, 1), (300, 1536, 11)])
+def test_gemv_tolerance(wtype, nrows, k, ncols):
+    print(f"gemv wtype={wtype} nrows={nrows} k={k} ncols={ncols}", flush=True)
+    w, grid, x = case(wtype, nrows, k, ncols, 400 + nrows + wtype)
+    y, xq = gpu_gemv(wtype, w, grid, x, nrows, k, ncols)
+    assert np.array_equal(xq, oracle.quantize_q8_1(x))
+    ref, a = oracle.gemv(wtype, w, k, xq, grid)
+    check_tol(y, ref, a, what=f"gemv {wtype}")
+
+
+@pytest.mark.parametrize("wtype", FORMATS)
+def test_column_invariance(wtype):
+    """Each column of an n-column call equals the one-column call bitwise (n = 1..8, 11)."""
+    nrows, k = 200, 2560
+    print(f"column invariance wtype={wtype}", flush=True)
+    w, grid, x = case(wtype, nrows, k, 11, 500 + wtype)
+    wd = dev(w)
+    gd = None if grid is None else dev(grid)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    nb36 = (k // 32) * 36
+    single = [host(M.qgemv_dense(wtype, wd, nrows, k, xq[c:c + 1].contiguous(), 1, grid=gd))[0] for c in range(11)]
+    for n in list(range(1, 9)) + [11]:
+        y = host(M.qgemv_dense(wtype, wd, nrows, k, xq[:n].contiguous(), n, grid=gd))
+        for c in range(n):
+            assert np.array_equal(y[c].view(np.uint32), single[c].view(np.uint32)), (n, c)
+    assert nb36 == xq.shape[1]
+
+
+@pytest.mark.parametrize("wtype", FORMATS)
+def test_onehot_rows_exact(wtype):
+    """Rows whose every block scale but one is 0: y equals that block's binary32 term bitwise."""
+    bv, bb = synth.BLOCK_VALUES[wtype], synth.BLOCK_BYTES[wtype]
+    k = 2560
+    nb = k // bv
+    print(f"one-hot rows wtype={wtype}", flush=True)
+    w, grid, x = case(wtype, nb, k, 3, 600 + wtype)
+    w = w.reshape(nb, nb, bb).copy()
+    for r in range(nb):
+        for b in range(nb):
+            if b != r:
+                w[r, b, 0:2] = 0
+    w = w.reshape(nb, nb * bb)
+    if wtype == M.QMM_CB3:
+        # a super-block holds 8 sub-block terms: zero the activations outside sub-block 0 of
+        # every super-block so each row keeps a single non-zero term
+        x = x.copy()
+        x[:, (np.arange(k) % 256) >= 32] = 0.0
+    y, xq = gpu_gemv(wtype, w, grid, x, nb, k, 3)
+    ref, _ = oracle.gemv(wtype, w, k, xq, grid)
+    assert np.array_equal(y, ref.astype(np.float32)), np.abs(y - ref).max()
+
+
+def test_ldy_padding():
+    print("ldy padding", flush=True)
+    import torch
+    w, grid, x = case(M.QMM_IQ4_NL, 50, 512, 3, 700)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    y = torch.full((3, 64), 7.0, device="cuda")
+    M.qgemv_dense(M.QMM_IQ4_NL, dev(w), 50, 512, xq, 3, y=y, ldy=64)
+    yh = host(y)
+    assert (yh[:, 50:] == 7.0).all()
+    ref, a = oracle.gemv(M.QMM_IQ4_NL, w, 512, host(xq))
+    check_tol(yh[:, :50], ref, a)
