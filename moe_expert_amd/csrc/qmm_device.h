@@ -27,6 +27,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
+// Range rounded up to whole dwords, for buffers whose data ends inside a dword (weight blocks
+// of 34 or 18 bytes): the hardware drops a dword that is partly past the range, and the dword
+// holding the last byte of a 4-byte aligned buffer lies in the same page as that byte.
+__device__ __forceinline__ rsrc_t make_rsrc_dw(const void* p, uint32_t nbytes) {
+    const uint64_t r = ((uint64_t)nbytes + 3u) & ~(uint64_t)3u;
+    return make_rsrc(p, r > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)r);
+}
+
 __device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
@@ -91,79 +99,90 @@ constexpr uint32_t kv_word(int j) {
            ((uint32_t)(uint8_t)kIQ4NLLevels[4 * j + 3] << 24);
 }
 
-// Four 4-bit indices (one per byte, low 3 bits in `i7`, bit 3 moved to bit 2 in `i8`) ->
-// four int8 levels.  Two v_perm pick from the low and high halves of the table, a third
-// picks per byte between them.
+// Constants of the IQ4_NL decode, held in VGPRs: gfx9 VOP3 instructions take no literal
+// and at most one SGPR, so register-resident constants let v_and_or_b32 fold two operations.
+struct IQ4Consts {
+    uint32_t m7, m4, c0123;
+    __device__ __forceinline__ IQ4Consts() : m7(opaque_u(0x07070707u)), m4(opaque_u(0x04040404u)), c0123(opaque_u(0x03020100u)) {}
+    __device__ static __forceinline__ uint32_t opaque_u(uint32_t v) {
+        asm volatile("" : "+v"(v));
+        return v;
+    }
+};
+
+// Four 4-bit indices, one per byte, given as their low 3 bits `i7` and the selector `i8` of the
+// byte-wise choice between the two table halves (byte k = k, or k + 4 when bit 3 is set) ->
+// four int8 levels: two v_perm pick from each half of the table, a third picks per byte.
 __device__ __forceinline__ uint32_t iq4nl_lookup(uint32_t i7, uint32_t i8) {
     const uint32_t lo = perm(kv_word(1), kv_word(0), i7);
     const uint32_t hi = perm(kv_word(3), kv_word(2), i7);
-    return perm(hi, lo, i8 | 0x03020100u);
+    return perm(hi, lo, i8);
 }
 
 // One dword of IQ4_NL index bytes (elements j..j+3 in the low nibbles, j+16..j+19 in the
-// high nibbles) -> the int8 levels of both element groups.
-__device__ __forceinline__ void iq4nl_decode_word(uint32_t q, uint32_t& lo, uint32_t& hi) {
-    lo = iq4nl_lookup(q & 0x07070707u, (q >> 1) & 0x04040404u);
-    hi = iq4nl_lookup((q >> 4) & 0x07070707u, (q >> 5) & 0x04040404u);
+// high nibbles) -> the int8 levels of both element groups (13 VALU).
+__device__ __forceinline__ void iq4nl_decode_word(uint32_t q, uint32_t& lo, uint32_t& hi, const IQ4Consts& k) {
+    lo = iq4nl_lookup(q & k.m7, ((q >> 1) & k.m4) | k.c0123);
+    hi = iq4nl_lookup((q >> 4) & k.m7, ((q >> 5) & k.m4) | k.c0123);
 }
 
 // ------------------------------------------------------------------ weight units
 //
-// A "unit" is what one lane loads and decodes in one step; it covers BLK 32-value blocks,
-// each delivered as 8 dwords of int8 factors (values 4i..4i+3 in dword i) plus its fp16
-// scale and an integer multiplier (1 except CB3).
-//   Q8_0   : a pair of blocks (68 bytes, 17 dwords, 4-byte aligned when the row is)
-//   IQ4_NL : a pair of blocks (36 bytes, 9 dwords)
+// A "unit" is one 32-value block of a row: what one lane loads and decodes in one step.  It is
+// delivered as 8 dwords of int8 factors (values 4i..4i+3 in dword i), the fp16 scale of its
+// block and an integer multiplier (1 except CB3).
+//   Q8_0   : 34-byte block, read as the 9 aligned dwords around it
+//   IQ4_NL : 18-byte block, read as the 5 aligned dwords around it
 //   CB3    : one 32-value sub-block of a 256-value super-block
+// Blocks of 34 and 18 bytes start on a 4-byte or a 2-byte boundary; the loads start at the
+// enclosing 4-byte boundary and one v_perm per dword realigns them (selector 0x05040302 when
+// the block is 4-byte aligned, 0x07060504 when it is 2 bytes past one).
 
 template <int WT>
 struct Unit;
 
+__device__ __forceinline__ uint32_t realign_sel(uint32_t off) { return (off & 2u) ? 0x07060504u : 0x05040302u; }
+__device__ __forceinline__ uint32_t realign_scale(uint32_t w0, uint32_t off) { return (off & 2u) ? (w0 >> 16) : (w0 & 0xFFFFu); }
+
 template <>
 struct Unit<kQ8_0> {
-    static constexpr int BLK = 2;
-    static constexpr int RAW = 17;
-    static constexpr int UNIT_BYTES = 68;
+    using Consts = IQ4Consts;  // unused
+    static constexpr int RAW = 9;
+    static constexpr int BYTES = 34;
     __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
-        const u32x4 a = ld128(r, off), b = ld128(r, off + 16), c = ld128(r, off + 32), d = ld128(r, off + 48);
-        raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
-        raw[4] = b.x; raw[5] = b.y; raw[6] = b.z; raw[7] = b.w;
-        raw[8] = c.x; raw[9] = c.y; raw[10] = c.z; raw[11] = c.w;
-        raw[12] = d.x; raw[13] = d.y; raw[14] = d.z; raw[15] = d.w;
-        raw[16] = ld32(r, off + 64);
+        const uint32_t a = off & ~3u;
+        const u32x4 x = ld128(r, a), y = ld128(r, a + 16);
+        raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
+        raw[4] = y.x; raw[5] = y.y; raw[6] = y.z; raw[7] = y.w;
+        raw[8] = ld32(r, a + 32);
     }
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t (*W)[8], uint32_t* dw,
-                                                  int* mult) {
-        dw[0] = raw[0] & 0xFFFFu;
+    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
+                                                  const IQ4Consts&) {
+        const uint32_t sel = realign_sel(off);
+        dw = realign_scale(raw[0], off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) W[0][i] = align8(raw[i + 1], raw[i], 2);
-        dw[1] = raw[8] >> 16;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) W[1][i] = raw[9 + i];
-        mult[0] = mult[1] = 1;
+        for (int i = 0; i < 8; ++i) W[i] = perm(raw[i + 1], raw[i], sel);
+        mult = 1;
     }
 };
 
 template <>
 struct Unit<kIQ4_NL> {
-    static constexpr int BLK = 2;
-    static constexpr int RAW = 9;
-    static constexpr int UNIT_BYTES = 36;
+    static constexpr int RAW = 5;
+    static constexpr int BYTES = 18;
     __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
-        const u32x4 a = ld128(r, off), b = ld128(r, off + 16);
-        raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
-        raw[4] = b.x; raw[5] = b.y; raw[6] = b.z; raw[7] = b.w;
-        raw[8] = ld32(r, off + 32);
+        const uint32_t a = off & ~3u;
+        const u32x4 x = ld128(r, a);
+        raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
+        raw[4] = ld32(r, a + 16);
     }
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t (*W)[8], uint32_t* dw,
-                                                  int* mult) {
-        dw[0] = raw[0] & 0xFFFFu;
+    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
+                                                  const IQ4Consts& k) {
+        const uint32_t sel = realign_sel(off);
+        dw = realign_scale(raw[0], off);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) iq4nl_decode_word(align8(raw[i + 1], raw[i], 2), W[0][i], W[0][i + 4]);
-        dw[1] = raw[4] >> 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) iq4nl_decode_word(raw[5 + i], W[1][i], W[1][i + 4]);
-        mult[0] = mult[1] = 1;
+        for (int i = 0; i < 4; ++i) iq4nl_decode_word(perm(raw[i + 1], raw[i], sel), W[i], W[i + 4], k);
+        mult = 1;
     }
 };
 
@@ -186,7 +205,6 @@ __device__ __forceinline__ uint32_t cb3_signed(uint32_t g, uint32_t nib) {
 
 template <>
 struct Unit<kCB3> {
-    static constexpr int BLK = 1;
     static constexpr int RAW = 8;
     // raw: [0..2] qs window, [3..4] signs window, [5] qh byte, [6] scales byte, [7] d
     // `off` = byte offset of the super-block, `ss` = sub-block 0..7.
@@ -201,12 +219,11 @@ struct Unit<kCB3> {
         raw[6] = ld8(r, off + kCB3Scales + (ss >> 1));
         raw[7] = ld16(r, off);
     }
-    // grid: 512 codebook words in LDS.  `off` and `ss` as in load (the low bits of the field
-    // offsets give the alignment shifts).
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, int ss,
-                                                  const uint32_t* grid, uint32_t (*W)[8], uint32_t* dw,
-                                                  int* mult) {
-        const uint32_t shq = (off + kCB3Qs) & 3u;        // 8*ss keeps the low bits
+    // grid: the 512 codebook words in LDS.  `off` and `ss` as in load (the low bits of the
+    // field offsets give the realignment).
+    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, int ss, const uint32_t* grid,
+                                                  uint32_t* W, uint32_t& dw, int& mult) {
+        const uint32_t shq = (off + kCB3Qs) & 3u;  // 8*ss keeps the low bits
         const uint32_t shs = (off + kCB3Signs) & 3u;
         const uint32_t q0 = align8(raw[1], raw[0], shq);
         const uint32_t q1 = align8(raw[2], raw[1], shq);
@@ -216,10 +233,10 @@ struct Unit<kCB3> {
         for (int e = 0; e < 8; ++e) {
             const uint32_t qb = ((e < 4 ? q0 : q1) >> (8 * (e & 3))) & 0xFFu;
             const uint32_t idx = qb | (((qh >> e) & 1u) << 8);
-            W[0][e] = cb3_signed(grid[idx], (sg >> (4 * e)) & 15u);
+            W[e] = cb3_signed(grid[idx], (sg >> (4 * e)) & 15u);
         }
-        dw[0] = raw[7];
-        mult[0] = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
+        dw = raw[7];
+        mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
     }
 };
 
@@ -245,6 +262,62 @@ __device__ __forceinline__ void stage_block(rsrc_t xr, uint32_t src_block, ActLd
     *(u32x4*)dst = q0;
     *(u32x4*)(dst + 4) = q1;
     a.d[c * a.nb + b] = h2f(h);
+}
+
+// ------------------------------------------------------------------ q8_1 quantization
+
+// x / d rounded half away from zero (exact: v - trunc(v) is exact in binary32).
+__device__ __forceinline__ int round_away(float v) {
+    const float t = __builtin_truncf(v);
+    const float r = __builtin_fabsf(v - t) >= 0.5f ? t + __builtin_copysignf(1.0f, v) : t;
+    return (int)r;
+}
+
+// q8_1 of one 32-value block held by 32 consecutive lanes (an aligned half wave), lane j
+// holding value j [DQ, Change: the q8_1 quantizer's 32-value blocks]: amax over the half wave,
+// d = amax / 127 (IEEE binary32 division), q_j = x_j / d rounded half away from zero,
+// s = fp16(d * sum q) with the product in binary32; an all-zero block is all zeros.  Returns
+// q_j; `hdr` (d | s << 16) is the same in all 32 lanes.  Every lane of the wave must call it.
+__device__ __forceinline__ int quantize_lanes32(float v, uint32_t& hdr) {
+    float amax = __builtin_fabsf(v);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float d = amax / 127.0f;
+    const bool zero = amax == 0.0f || d == 0.0f;
+    int q = 0;
+    if (!zero) {
+        q = round_away(v / d);
+        q = q > 127 ? 127 : (q < -127 ? -127 : q);
+    }
+    int sum = q;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) sum += __shfl_xor(sum, m, 64);
+    hdr = zero ? 0u : (f2h(d) | (f2h(opaque(d * (float)sum)) << 16));
+    return q;
+}
+
+// Pack the int8 q of lanes j..j+3 (j a multiple of 4) into one dword, valid in lane j.
+__device__ __forceinline__ uint32_t pack4_lanes(int q) {
+    const uint32_t b = (uint32_t)q & 0xFFu;
+    const uint32_t b1 = __shfl_down(b, 1, 64), b2 = __shfl_down(b, 2, 64), b3 = __shfl_down(b, 3, 64);
+    return b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// ------------------------------------------------------------------ cross-lane sums
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15); every lane of the row gets the same
+// value (each step adds a lane's value to its partner's, so partners compute identical sums).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
 }
 
 }  // namespace qmm

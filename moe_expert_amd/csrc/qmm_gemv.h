@@ -1,0 +1,213 @@
+// qmm_gemv.h -- the decode-GEMV row engine shared by the dense GEMV and the grouped-expert
+// kernels: per-lane block loads, decode once, apply to every column of the pass.
+#pragma once
+
+#include "qmm_device.h"
+#include "qmm_host.h"
+
+namespace qmm {
+
+constexpr int kGemvLanesPerRow = 16;  // one DPP row
+constexpr int kGemvThreads = 512;     // 8 waves, two per SIMD
+constexpr int kGemvRowsPerWG = 32;    // 8 waves x 4 rows
+constexpr int kGemvChunk = 6;         // blocks per lane whose loads are issued together
+constexpr size_t kLdsCap = 65536;     // LDS a workgroup may use
+
+template <int WT>
+__host__ __device__ constexpr int row_bytes_dev(int K) {
+    return WT == kQ8_0 ? (K / 32) * 34 : WT == kIQ4_NL ? (K / 32) * 18 : (K / 256) * kCB3Bytes;
+}
+
+// LDS of a pass of ncp columns: int8 plane + float scales, plus the CB3 codebook.
+__host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int ncp) {
+    return (size_t)ncp * ((size_t)k + (size_t)(k / 32) * 4) + (wt == kCB3 ? 2048 : 0);
+}
+inline int gemv_max_pass(int wt, int64_t k) {
+    const size_t per = (size_t)k + (size_t)(k / 32) * 4;
+    const size_t fixed = wt == kCB3 ? 2048 : 0;
+    if (kLdsCap < fixed + per) return 0;
+    const int m = (int)((kLdsCap - fixed) / per);
+    return m > 8 ? 8 : m;
+}
+
+__device__ __forceinline__ ActLds act_lds_layout(uint32_t* lds, int K, int ncp) {
+    ActLds a;
+    a.kw = K / 4;
+    a.nb = K / 32;
+    a.q = lds;
+    a.d = (float*)(lds + ncp * a.kw);
+    return a;
+}
+__device__ __forceinline__ uint32_t* act_lds_end(ActLds a, int ncp) { return (uint32_t*)(a.d + ncp * a.nb); }
+
+__device__ __forceinline__ void stage_grid(const uint8_t* grid, uint32_t* lds_grid) {
+    const rsrc_t gr = make_rsrc(grid, 2048);
+    for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_grid[i] = ld32(gr, 4u * i);
+}
+
+// The 512-word codebook staged by a 512-thread workgroup, one word per thread, split into an
+// early load and a late LDS write like the activations.
+struct GridStage {
+    uint32_t v;
+    __device__ __forceinline__ void load(const uint8_t* grid) {
+        v = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x & 511u));
+    }
+    __device__ __forceinline__ void store(uint32_t* lds_grid) const { lds_grid[threadIdx.x & 511u] = v; }
+};
+
+// Activation staging in two halves so that its global loads can be issued before the weight
+// loads and its LDS writes after them: a thread stages up to kStageSlots q8_1 blocks, the pass's
+// (column, block) pairs being numbered column * 2^ceil(log2(blocks)) + block.
+constexpr int kStageSlots = 4;
+
+template <int NS>
+struct ActStage {
+    uint32_t h[NS];
+    u32x4 q0[NS], q1[NS];
+    int lsh;   // log2 of the block count rounded up to a power of two
+    int last;  // last valid (column, block) slot index
+
+    // Slot index i -> column i >> lsh, block i & (2^lsh - 1); indices past the pass or past a
+    // column's blocks are clamped to the pass's last block.  Loads are unconditional so the
+    // code stays straight-line.
+    __device__ __forceinline__ int slot(int j, const ActLds& act, int ncp) const {
+        const int i = (int)threadIdx.x + j * (int)blockDim.x;
+        const int c = i >> lsh, b = i & ((1 << lsh) - 1);
+        return (c < ncp && b < act.nb) ? i : last;
+    }
+    __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp) {
+        lsh = 32 - __builtin_clz((unsigned)act.nb - 1u);
+        if (act.nb == 1) lsh = 0;
+        last = ((ncp - 1) << lsh) | (act.nb - 1);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int i = slot(j, act, ncp);
+            const uint32_t off = __umul24((uint32_t)((col0 + (i >> lsh)) * act.nb + (i & ((1 << lsh) - 1))), 36u);
+            h[j] = ld32(xr, off);
+            q0[j] = ld128(xr, off + 4);
+            q1[j] = ld128(xr, off + 20);
+        }
+    }
+    // Unconditional too: a slot past the pass rewrites the pass's last block with the same
+    // bytes (identical values, so the overlapping writes are benign).  Keeping the stores
+    // unconditional keeps the loads where they are written (otherwise the compiler sinks them
+    // into the store's branch, behind the weight loads).
+    __device__ __forceinline__ void store(const ActLds& act, int ncp) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int i = slot(j, act, ncp);
+            const int c = i >> lsh, b = i & ((1 << lsh) - 1);
+            uint32_t* dst = act.q + __umul24((uint32_t)c, (uint32_t)act.kw) + b * 8;
+            *(u32x4*)dst = q0[j];
+            *(u32x4*)(dst + 4) = q1[j];
+            act.d[__umul24((uint32_t)c, (uint32_t)act.nb) + b] = h2f(h[j]);
+        }
+    }
+};
+
+// One lane's share of one row: blocks s = l16 + 16 i, i = 0, 1, ...  U blocks are loaded per
+// chunk; MULTI = the row has more than U blocks per lane (double-buffered chunks), otherwise U
+// is exactly the lane's block count.  Loads are unconditional (a block past the row is read at
+// the row's last block and not used), so the code between the loads and their uses stays
+// straight-line and each use waits only for its own load.
+template <int WT, int NC, bool SUMS, int U, bool MULTI>
+struct RowEngine {
+    static constexpr int RAW = Unit<WT>::RAW;
+    rsrc_t wr;
+    uint32_t row_off;
+    int nunits, niter, l16;
+    uint32_t A[U][RAW], B[MULTI ? U : 1][RAW];
+    IQ4Consts kc;
+
+    __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l16_)
+        : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + 15) / 16), l16(l16_) {}
+
+    __device__ __forceinline__ uint32_t unit_off(int s) const {
+        // 32-bit multiply-add (a 64-bit one would tie a dead high half to a pending load)
+        if constexpr (WT == kCB3) return row_off + __umul24((uint32_t)(s >> 3), (uint32_t)kCB3Bytes);
+        else return row_off + __umul24((uint32_t)s, (uint32_t)Unit<WT>::BYTES);
+    }
+
+    template <int N>
+    __device__ __forceinline__ void load(uint32_t (&buf)[N][RAW], int i0) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            int s = l16 + 16 * (i0 + u);
+            s = s < nunits ? s : nunits - 1;
+            if constexpr (WT == kCB3) Unit<WT>::load(wr, unit_off(s), s & 7, buf[u]);
+            else Unit<WT>::load(wr, unit_off(s), buf[u]);
+        }
+    }
+
+    __device__ __forceinline__ void load_first() { load(A, 0); }
+
+    template <int N>
+    __device__ __forceinline__ void compute(const uint32_t (&buf)[N][RAW], int i0, const ActLds& act, int ncp,
+                                            const uint32_t* grid, float (&acc)[NC], int32_t* srow, int64_t scol,
+                                            bool row_ok) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int s = l16 + 16 * (i0 + u);
+            if (s < nunits) {
+                uint32_t W[8];
+                uint32_t dw;
+                int mult;
+                if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(s), s & 7, grid, W, dw, mult);
+                else Unit<WT>::decode(buf[u], unit_off(s), W, dw, mult, kc);
+                const float dwf = h2f(dw);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    if (c < ncp) {
+                        const uint32_t* a = act.q + __umul24((uint32_t)c, (uint32_t)act.kw) + s * 8;
+                        const u32x4 a0 = *(const u32x4*)a;
+                        const u32x4 a1 = *(const u32x4*)(a + 4);
+                        int v = dot4(W[0], a0.x, 0);
+                        v = dot4(W[1], a0.y, v);
+                        v = dot4(W[2], a0.z, v);
+                        v = dot4(W[3], a0.w, v);
+                        v = dot4(W[4], a1.x, v);
+                        v = dot4(W[5], a1.y, v);
+                        v = dot4(W[6], a1.z, v);
+                        v = dot4(W[7], a1.w, v);
+                        const int isum = v * mult;
+                        if constexpr (SUMS) {
+                            if (row_ok) srow[c * scol + s] = isum;
+                        } else {
+                            const float dd = dwf * act.d[__umul24((uint32_t)c, (uint32_t)act.nb) + s];
+                            acc[c] = __builtin_fmaf(dd, (float)isum, acc[c]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // All of the lane's blocks; the first chunk must already be loaded (load_first).
+    __device__ __forceinline__ void run(const ActLds& act, int ncp, const uint32_t* grid, float (&acc)[NC],
+                                        int32_t* srow, int64_t scol, bool row_ok) {
+        if constexpr (!MULTI) {
+            compute(A, 0, act, ncp, grid, acc, srow, scol, row_ok);
+        } else {
+            for (int i0 = 0; i0 < niter; i0 += 2 * U) {
+                const bool more = i0 + U < niter;
+                if (more) load(B, i0 + U);
+                compute(A, i0, act, ncp, grid, acc, srow, scol, row_ok);
+                if (more) {
+                    if (i0 + 2 * U < niter) load(A, i0 + 2 * U);
+                    compute(B, i0 + U, act, ncp, grid, acc, srow, scol, row_ok);
+                }
+            }
+        }
+    }
+};
+
+// Blocks per lane of a row of k values (16 lanes per row).
+inline int lane_blocks(int64_t k) { return (int)((k / 32 + 15) / 16); }
+
+// Staging slots per thread for a pass of ncp columns of k values.
+inline int stage_slots(int64_t k, int ncp, int threads) {
+    const int64_t n = (int64_t)ncp * pow2_ceil(k / 32);
+    return n <= threads ? 1 : n <= 2 * threads ? 2 : 4;
+}
+
+}  // namespace qmm

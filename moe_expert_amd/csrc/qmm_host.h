@@ -24,6 +24,12 @@ inline int launch_status() {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 constexpr int64_t kMaxK = 32768;
+
+inline int64_t pow2_ceil(int64_t v) {
+    int64_t p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
 constexpr uint64_t kMaxBufferBytes = 0xFFFFFFFFull;  // raw-buffer record range (32-bit offsets)
 
 }  // namespace qmm

@@ -12,65 +12,26 @@
 
 namespace qmm {
 
-// x / d rounded half away from zero (exact: v - trunc(v) is exact in binary32).
-__device__ __forceinline__ int round_away(float v) {
-    const float t = __builtin_truncf(v);
-    const float r = __builtin_fabsf(v - t) >= 0.5f ? t + __builtin_copysignf(1.0f, v) : t;
-    return (int)r;
-}
-
-// Quantize 32 values to one q8_1 block: returns the packed header (d | s << 16) and the 8
-// dwords of int8 q.
-__device__ __forceinline__ uint32_t quantize_block(const float* x, uint32_t* qw) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
-    const float d = amax / 127.0f;
-    if (amax == 0.0f || d == 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qw[i] = 0;
-        return 0;
-    }
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int q = round_away(x[4 * i + j] / d);
-            q = q > 127 ? 127 : (q < -127 ? -127 : q);
-            sum += q;
-            word |= ((uint32_t)q & 0xFFu) << (8 * j);
-        }
-        qw[i] = word;
-    }
-    return f2h(d) | (f2h(opaque(d * (float)sum)) << 16);
-}
-
-// One thread per q8_1 block.  x: [ncols][ldx] floats.
+// One lane per value, one aligned half wave per q8_1 block.  x: [ncols][ldx] floats.
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float* __restrict__ x, int64_t ldx, int nb,
-                                                            int ncols, uint32_t* __restrict__ xq) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)nb * ncols) return;
-    const int c = (int)(i / nb), b = (int)(i - (int64_t)c * nb);
-    const float* src = x + c * ldx + 32 * b;
-    float v[32];
-    if (((uintptr_t)src & 15) == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float4 t = ((const float4*)src)[j];
-            v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = src[j];
+                                                            int ncols, uint8_t* __restrict__ xq) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t blk = g >> 5;
+    const int j = (int)(g & 31);
+    const bool ok = blk < (int64_t)nb * ncols;
+    float v = 0.0f;
+    if (ok) {
+        const int c = (int)(blk / nb), b = (int)(blk - (int64_t)c * nb);
+        v = x[c * ldx + 32 * b + j];
     }
-    uint32_t qw[8];
-    const uint32_t hdr = quantize_block(v, qw);
-    uint32_t* dst = xq + i * 9;
-    dst[0] = hdr;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[1 + j] = qw[j];
+    uint32_t hdr;
+    const int q = quantize_lanes32(v, hdr);
+    const uint32_t word = pack4_lanes(q);
+    if (ok) {
+        uint32_t* dst = (uint32_t*)(xq + blk * 36);
+        if (j == 0) dst[0] = hdr;
+        if ((j & 3) == 0) dst[1 + (j >> 2)] = word;
+    }
 }
 
 // Integer factors of values [j0, j0+8) of a row (j0 a multiple of 8), and the fp16 scale of
@@ -169,9 +130,9 @@ extern "C" int qmm_quantize_q8_1(const float* x, int64_t k, int ncols, int64_t l
     if (!aligned(x, 4) || !aligned(xq, 4)) return QMM_EALIGN;
     if (k > (int64_t)1 << 30 || (int64_t)ncols * (k / 32) > ((int64_t)1 << 31)) return QMM_EUNSUPPORTED;
     const int nb = (int)(k / 32);
-    const int64_t n = (int64_t)nb * ncols;
+    const int64_t n = (int64_t)nb * ncols * 32;
     hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), x, ldx,
-                       nb, ncols, (uint32_t*)xq);
+                       nb, ncols, (uint8_t*)xq);
     return launch_status();
 }
 

@@ -29,7 +29,7 @@ def gpu_gemv(wtype, w, grid, x, nrows, k, ncols):
 
 
 @pytest.mark.parametrize("wtype", FORMATS)
-@pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 3), (64, 1024, 1), (100, 2560, 8), (33, 768, 5)])
+@pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 3), (64, 1024, 1), (100, 2560, 8), (33, 768, 5), (21, 2592, 2)])
 def test_block_sums_exact(wtype, nrows, k, ncols):
     if wtype == M.QMM_CB3 and k % 256:
         pytest.skip("CB3 needs k % 256 == 0")
@@ -43,8 +43,11 @@ def test_block_sums_exact(wtype, nrows, k, ncols):
 
 @pytest.mark.parametrize("wtype", FORMATS)
 @pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 3), (129, 2560, 8), (64, 1024, 2), (31, 6144, 7),
-                                           (1, 256, 1), (300, 1536, 11)])
+                                           (1, 256, 1), (300, 1536, 11), (45, 2592, 4), (7, 96, 2),
+                                           (33, 12544, 5)])
 def test_gemv_tolerance(wtype, nrows, k, ncols):
+    if wtype == M.QMM_CB3 and k % 256:
+        pytest.skip("CB3 rows are whole 256-value super-blocks")
     print(f"gemv wtype={wtype} nrows={nrows} k={k} ncols={ncols}", flush=True)
     w, grid, x = case(wtype, nrows, k, ncols, 400 + nrows + wtype)
     y, xq = gpu_gemv(wtype, w, grid, x, nrows, k, ncols)

@@ -52,8 +52,8 @@ ODD = C.c_void_p(0x100002)
     ((7, FAKE, None, 64, 2560, FAKE, 1, FAKE, 64, None), -1),                # unknown format
     ((M.QMM_Q8_0, FAKE, None, 64, 2560, FAKE, 0, FAKE, 64, None), -1),       # no columns
     ((M.QMM_Q8_0, FAKE, None, 64, 2561, FAKE, 1, FAKE, 64, None), -1),       # k not a block multiple
-    ((M.QMM_Q8_0, FAKE, None, 64, 2592, FAKE, 1, FAKE, 64, None), -2),       # odd block count: declined
-    ((M.QMM_CB3, FAKE, FAKE, 64, 2560 + 64, FAKE, 1, FAKE, 64, None), -2),   # CB3 needs 256-multiples
+    ((M.QMM_Q8_0, FAKE, None, 0, 2592, FAKE, 1, FAKE, 64, None), -1),        # no rows
+    ((M.QMM_CB3, FAKE, FAKE, 64, 2560 + 64, FAKE, 1, FAKE, 64, None), -1),   # CB3 needs 256-multiples
     ((M.QMM_CB3, FAKE, None, 64, 2560, FAKE, 1, FAKE, 64, None), -1),        # CB3 without a grid
     ((M.QMM_Q8_0, ODD, None, 64, 2560, FAKE, 1, FAKE, 64, None), -3),        # misaligned weights
     ((M.QMM_Q8_0, FAKE, None, 64, 2560, FAKE, 1, FAKE, 63, None), -1),       # ldy < nrows
