@@ -119,27 +119,32 @@ size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned fla
  * e = group_expert[g]) and every entry j in [group_entry_off[g], group_entry_off[g+1]):
  *   x  = q8_1 column entry_col[j] of xq (width hidden)
  *   gv = W_gate[e] x,  uv = W_up[e] x          (qgemv_dense arithmetic, inter rows)
- *   h  = silu(gv) * uv,  silu(z) = z / (1 + exp(-z)), binary32
+ *   h  = silu(gv) * uv,  silu(z) = z / (1 + exp(-z)): exp in binary64 rounded to binary32,
+ *        the rest binary32
  *   H  = q8_1(h) per 32 consecutive intermediate values          (workspace)
  *   y[j*hidden + r] = (W_down[e] H)[r]                            (binary32; unweighted)
  *   w_gate, w_up : expert e's matrix at byte offset e*gu_expert_stride, inter rows of width
  *                  hidden, format wtype_gu;  w_down: offset e*down_expert_stride, hidden rows of
- *                  width inter, format wtype_down.  All 4-byte aligned; strides multiples of 4.
+ *                  width inter, format wtype_down; nexperts matrices each.  4-byte aligned;
+ *                  strides multiples of 4 and at least one matrix.
+ *   xq, xq_cols  : q8_1 activations [xq_cols][hidden/32][36]; an entry whose column is outside
+ *                  [0, xq_cols) reads zeros.
  *   group_expert[ngroups], group_entry_off[ngroups+1], entry_col[nentries]: int32, device.
- *                  Offsets must be non-decreasing and within [0, nentries]; entries outside
- *                  every group are not written.
+ *                  A group whose expert is outside [0, nexperts) is skipped; its entry range is
+ *                  clamped to [0, nentries).  Entries of no group are not written.
  *   ws   : workspace of qgemv_grouped_experts_workspace() bytes, 16-byte aligned.  Layout:
- *          H q8_1 [nentries][inter/32][36] first; with QMM_FLAG_DEBUG_INTERMEDIATES then
- *          gv, uv as float [nentries][inter] (each starting 16-byte aligned).
- *   hidden: multiple of 256 (CB3) or 64;  inter: multiple of 64 (256 for CB3 down).
+ *          H q8_1 [nentries][inter/32][36] first; with QMM_FLAG_DEBUG_INTERMEDIATES then gv, uv
+ *          as float [nentries][inter] (starting at the next 16-byte boundary).
+ *   hidden, inter: multiples of 32 (256 where the format is CB3); a pass of 8 entries must fit
+ *          the workgroup's 64 KiB of LDS (hidden, inter <= 6144 in practice).
  * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_ESPACE. */
 int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up,
                           int64_t gu_expert_stride, int wtype_down, const void* w_down,
-                          int64_t down_expert_stride, const uint8_t* grid, int64_t hidden,
-                          int64_t inter, const void* xq, const int32_t* group_expert,
-                          const int32_t* group_entry_off, int ngroups, const int32_t* entry_col,
-                          int nentries, float* y, void* ws, size_t ws_bytes, unsigned flags,
-                          void* stream);
+                          int64_t down_expert_stride, int nexperts, const uint8_t* grid,
+                          int64_t hidden, int64_t inter, const void* xq, int xq_cols,
+                          const int32_t* group_expert, const int32_t* group_entry_off, int ngroups,
+                          const int32_t* entry_col, int nentries, float* y, void* ws,
+                          size_t ws_bytes, unsigned flags, void* stream);
 
 /* Workspace bytes qgemm_prefill_experts needs (host). */
 size_t qgemm_prefill_experts_workspace(int nexperts, int64_t inter, int64_t nentries,

@@ -32,8 +32,8 @@ SIGNATURES = {
     "qgemv_dense": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qmm_debug_block_sums": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "qgemv_grouped_experts_workspace": (_SZ, [_I64, _I32, _U32]),
-    "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _P, _I64, _I64, _P, _P, _P,
-                                     _I32, _P, _I32, _P, _P, _SZ, _U32, _P]),
+    "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
+                                     _P, _P, _I32, _P, _I32, _P, _P, _SZ, _U32, _P]),
     "qgemm_prefill_experts_workspace": (_SZ, [_I32, _I64, _I64, _U32]),
     "qgemm_prefill_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _I64, _I64, _P, _I64,
                                      _P, _P, _I64, _P, _P, _SZ, _U32, _P]),
@@ -150,24 +150,27 @@ def qgemv_grouped_experts_workspace(inter, nentries, flags=0):
 def qgemv_grouped_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, hidden, inter, xq, group_expert,
                           group_entry_off, entry_col, grid=None, y=None, ws=None, flags=0, stream=None):
     """Grouped MoE decode.  w_gate / w_up: [nexperts, inter * row_bytes(gu, hidden)] bytes,
-    w_down: [nexperts, hidden * row_bytes(down, inter)] bytes; returns (y [nentries, hidden], ws)."""
+    w_down: [nexperts, hidden * row_bytes(down, inter)] bytes, xq: [xq_cols, hidden/32*36] q8_1;
+    returns (y [nentries, hidden] float32, ws)."""
     import torch
     for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (xq, "xq"), (group_expert, "group_expert"),
                  (group_entry_off, "group_entry_off"), (entry_col, "entry_col")):
         _dev(t, n)
     nentries = entry_col.numel()
     ngroups = group_expert.numel()
-    gu_stride = inter * row_bytes(wtype_gu, hidden)
-    d_stride = hidden * row_bytes(wtype_down, inter)
+    nexperts = w_gate.shape[0]
+    xq_cols = xq.numel() // ((hidden // 32) * 36)
+    gu_stride = w_gate[0].numel()
+    d_stride = w_down[0].numel()
     if y is None:
         y = torch.empty((nentries, hidden), dtype=torch.float32, device=w_gate.device)
     need = qgemv_grouped_experts_workspace(inter, nentries, flags)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=w_gate.device)
     _check("qgemv_grouped_experts", lib().qgemv_grouped_experts(
-        wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, _ptr(grid), hidden,
-        inter, _ptr(xq), _ptr(group_expert), _ptr(group_entry_off), ngroups, _ptr(entry_col), nentries, _ptr(y),
-        _ptr(ws), ws.numel(), flags, _stream(stream)))
+        wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, nexperts, _ptr(grid),
+        hidden, inter, _ptr(xq), xq_cols, _ptr(group_expert), _ptr(group_entry_off), ngroups, _ptr(entry_col),
+        nentries, _ptr(y), _ptr(ws), ws.numel(), flags, _stream(stream)))
     return y, ws
 
 

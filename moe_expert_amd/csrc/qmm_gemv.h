@@ -75,17 +75,38 @@ struct ActStage {
         const int c = i >> lsh, b = i & ((1 << lsh) - 1);
         return (c < ncp && b < act.nb) ? i : last;
     }
-    __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp) {
+    __device__ __forceinline__ void setup(const ActLds& act, int ncp) {
         lsh = 32 - __builtin_clz((unsigned)act.nb - 1u);
         if (act.nb == 1) lsh = 0;
         last = ((ncp - 1) << lsh) | (act.nb - 1);
+    }
+    __device__ __forceinline__ void load_slot(rsrc_t xr, const ActLds& act, int j, int src_col, int i) {
+        const uint32_t off = __umul24((uint32_t)(src_col * act.nb + (i & ((1 << lsh) - 1))), 36u);
+        h[j] = ld32(xr, off);
+        q0[j] = ld128(xr, off + 4);
+        q1[j] = ld128(xr, off + 20);
+    }
+    // Columns col0 .. col0 + ncp - 1 of the activations.
+    __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp) {
+        setup(act, ncp);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             const int i = slot(j, act, ncp);
-            const uint32_t off = __umul24((uint32_t)((col0 + (i >> lsh)) * act.nb + (i & ((1 << lsh) - 1))), 36u);
-            h[j] = ld32(xr, off);
-            q0[j] = ld128(xr, off + 4);
-            q1[j] = ld128(xr, off + 20);
+            load_slot(xr, act, j, col0 + (i >> lsh), i);
+        }
+    }
+    // Pass column c taken from activation column cols[c] (a uniform table).
+    template <int NCOL>
+    __device__ __forceinline__ void load_cols(rsrc_t xr, const ActLds& act, int ncp, const int (&cols)[NCOL]) {
+        setup(act, ncp);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int i = slot(j, act, ncp);
+            const int c = i >> lsh;
+            int col = cols[0];
+#pragma unroll
+            for (int cc = 1; cc < NCOL; ++cc) col = c == cc ? cols[cc] : col;
+            load_slot(xr, act, j, col, i);
         }
     }
     // Unconditional too: a slot past the pass rewrites the pass's last block with the same
@@ -200,6 +221,57 @@ struct RowEngine {
         }
     }
 };
+
+// One workgroup's 32 rows [row0, row0 + 32) of a decode GEMV pass: columns [col0, col0 + ncp)
+// of the q8_1 activations behind `xr` (column c is q8_1 blocks c*K/32 ...), results to
+// y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  Order of work: activation
+// loads, then this lane's weight loads, then the activation LDS writes (they wait only for
+// the activation loads), barrier, decode + apply as the weights arrive, DPP row sums.
+template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS>
+__device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, int col0, int ncp,
+                                          float* y, int64_t ldy, int32_t* sums, int row0, uint32_t* lds) {
+    ActLds act = act_lds_layout(lds, K, ncp);
+    uint32_t* lds_grid = act_lds_end(act, ncp);
+
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int row = row0 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+    const bool row_ok = row < nrows;
+    const int rowc = row_ok ? row : nrows - 1;
+    const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
+
+    ActStage<NS> stage;
+    stage.load(xr, act, col0, ncp);
+    GridStage gstage;
+    if constexpr (WT == kCB3) gstage.load(grid);
+    __builtin_amdgcn_sched_barrier(0);
+    RowEngine<WT, NC, SUMS, U, MULTI> eng(wr, row_off, K, l16);
+    eng.load_first();
+    __builtin_amdgcn_sched_barrier(0);
+    stage.store(act, ncp);
+    if constexpr (WT == kCB3) gstage.store(lds_grid);
+    __syncthreads();
+
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
+    int32_t* srow = nullptr;
+    int64_t scol = 0;
+    if constexpr (SUMS) {
+        srow = sums + ((int64_t)col0 * nrows + rowc) * act.nb;
+        scol = (int64_t)nrows * act.nb;
+    }
+    eng.run(act, ncp, lds_grid, acc, srow, scol, row_ok);
+    if constexpr (!SUMS) {
+        float out = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float s = row16_sum(acc[c]);
+            if (l16 == c) out = s;
+        }
+        if (row_ok && l16 < ncp) y[(int64_t)(col0 + l16) * ldy + row] = out;
+    }
+}
 
 // Blocks per lane of a row of k values (16 lanes per row).
 inline int lane_blocks(int64_t k) { return (int)((k / 32 + 15) / 16); }

@@ -25,51 +25,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
                                                             int ncp, float* __restrict__ y, int64_t ldy,
                                                             int32_t* __restrict__ sums) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    ActLds act = act_lds_layout(lds, K, ncp);
-    uint32_t* lds_grid = act_lds_end(act, ncp);
-
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15;
-    const int row = blockIdx.x * kGemvRowsPerWG + (threadIdx.x >> 6) * 4 + (lane >> 4);
-    const bool row_ok = row < nrows;
-    const int rowc = row_ok ? row : nrows - 1;
-    const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
-    const rsrc_t wr = make_rsrc_dw(w, wbytes);
-
-    // activation loads first, then this lane's weight loads, then the activation LDS writes:
-    // the writes wait only for the activation loads, the weights stay in flight
-    const rsrc_t xr = make_rsrc(xq, xqbytes);
-    ActStage<NS> stage;
-    stage.load(xr, act, col0, ncp);
-    GridStage gstage;
-    if constexpr (WT == kCB3) gstage.load(grid);
-    __builtin_amdgcn_sched_barrier(0);
-    RowEngine<WT, NC, SUMS, U, MULTI> eng(wr, row_off, K, l16);
-    eng.load_first();
-    __builtin_amdgcn_sched_barrier(0);
-    stage.store(act, ncp);
-    if constexpr (WT == kCB3) gstage.store(lds_grid);
-    __syncthreads();
-
-    float acc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
-    int32_t* srow = nullptr;
-    int64_t scol = 0;
-    if constexpr (SUMS) {
-        srow = sums + ((int64_t)col0 * nrows + rowc) * act.nb;
-        scol = (int64_t)nrows * act.nb;
-    }
-    eng.run(act, ncp, lds_grid, acc, srow, scol, row_ok);
-    if constexpr (!SUMS) {
-        float out = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const float s = row16_sum(acc[c]);
-            if (l16 == c) out = s;
-        }
-        if (row_ok && l16 < ncp) y[(int64_t)(col0 + l16) * ldy + row] = out;
-    }
+    gemv_tile<WT, SUMS, NC, U, MULTI, NS>(make_rsrc_dw(w, wbytes), nrows, K, grid, make_rsrc(xq, xqbytes), col0, ncp,
+                                          y, ldy, sums, blockIdx.x * kGemvRowsPerWG, lds);
 }
 
 // Pick the kernel instance for a pass of ncp columns, `lb` blocks per lane and `ns` staging

@@ -1,6 +1,295 @@
-// placeholder until the grouped kernels land
-#include "qmm_host.h"
-extern "C" size_t qgemv_grouped_experts_workspace(int64_t, int, unsigned) { return 0; }
-extern "C" int qgemv_grouped_experts(int, const void*, const void*, int64_t, int, const void*, int64_t, const uint8_t*,
-                                     int64_t, int64_t, const void*, const int32_t*, const int32_t*, int, const int32_t*, int,
-                                     float*, void*, size_t, unsigned, void*) { return QMM_EUNSUPPORTED; }
+// qmm_grouped.hip -- grouped MoE-expert decode for gfx950: gate/up GEMV + SwiGLU + q8_1 of H,
+// then the down GEMV, over groups (experts) x entries (routed token slots).
+//
+// Method [IQ, What it does: native_gu / native_down decode each weight part once for every
+// entry of a group; DQ, Change: swiglu, then q8_1 of H for the down product, H never stored in
+// fp32]:
+//   gate/up kernel : workgroup (t, g) takes intermediate rows [32t, 32t + 32) of expert
+//                    group_expert[g], both its gate and its up row for each index (a DPP row of
+//                    16 lanes per index), and every entry of the group in passes of 8.  Each
+//                    weight block is loaded once and applied to all entries of the pass.  The
+//                    32 x 8 gate and up sums go through LDS to a half wave per entry, which
+//                    forms h = silu(g) * u and quantizes the 32 values to one q8_1 block of H.
+//   down kernel    : the decode GEMV tile over W_down[e] with the group's H blocks (the entries
+//                    of a group are consecutive, so their H blocks are too).
+// silu(z) = z / (1 + e^-z): the exponential is taken in binary64 and rounded to binary32, the
+// rest is binary32 (IEEE division), so h depends only on the binary32 g and u.
+#include "qmm_gemv.h"
+
+namespace qmm {
+
+constexpr int kGroupPass = 8;  // entries per pass
+
+__device__ __forceinline__ float silu_mul(float z, float u) {
+    const float e = (float)exp(-(double)z);
+    const float den = opaque(1.0f + e);
+    const float sl = opaque(z / den);
+    return sl * u;
+}
+
+// Uniform group bounds: expert e and entry range [k0, k1), clamped to the valid ranges.
+struct GroupInfo {
+    int e, k0, k1;
+    __device__ __forceinline__ bool load(const int32_t* group_expert, const int32_t* group_off, int g, int nexperts,
+                                         int nentries) {
+        e = __builtin_amdgcn_readfirstlane(group_expert[g]);
+        k0 = __builtin_amdgcn_readfirstlane(group_off[g]);
+        k1 = __builtin_amdgcn_readfirstlane(group_off[g + 1]);
+        k0 = k0 < 0 ? 0 : k0;
+        k1 = k1 > nentries ? nentries : k1;
+        return e >= 0 && e < nexperts && k1 > k0;
+    }
+};
+
+template <int WT, int U, bool MULTI, int NS>
+__global__ __launch_bounds__(kGemvThreads) void gu_kernel(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
+    int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
+    uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
+    const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
+    float* __restrict__ dbg_u) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    GroupInfo gi;
+    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
+
+    ActLds act = act_lds_layout(lds, hidden, kGroupPass);
+    uint32_t* lds_grid = act_lds_end(act, kGroupPass);
+    float* gl = (float*)(lds_grid + (WT == kCB3 ? 512 : 0));  // [8][32] gate sums
+    float* ul = gl + kGroupPass * 32;                            // [8][32] up sums
+
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int rg = (threadIdx.x >> 6) * 4 + (lane >> 4);  // 0..31
+    const int i = blockIdx.x * 32 + rg;                    // intermediate index
+    const uint32_t rb = (uint32_t)row_bytes_dev<WT>(hidden);
+    const rsrc_t xr = make_rsrc(xq, xqbytes);
+    const rsrc_t rg_w = make_rsrc_dw(wg + gi.e * gu_stride, expert_bytes);
+    const rsrc_t ru_w = make_rsrc_dw(wu + gi.e * gu_stride, expert_bytes);
+    const int nbh = inter / 32;
+
+    RowEngine<WT, kGroupPass, false, U, MULTI> eg(rg_w, (uint32_t)i * rb, hidden, l16);
+    RowEngine<WT, kGroupPass, false, U, MULTI> eu(ru_w, (uint32_t)i * rb, hidden, l16);
+
+    for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
+        const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
+        // the pass's activation columns (uniform); out-of-range columns read as zeros
+        int cols[kGroupPass];
+#pragma unroll
+        for (int c = 0; c < kGroupPass; ++c) {
+            int col = __builtin_amdgcn_readfirstlane(entry_col[c0 + (c < ncp ? c : ncp - 1)]);
+            cols[c] = (col >= 0 && col < xq_cols) ? col : xq_cols;
+        }
+        if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
+        ActStage<NS> stage;
+        stage.load_cols(xr, act, ncp, cols);
+        GridStage gstage;
+        if constexpr (WT == kCB3) gstage.load(grid);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c0 == gi.k0 || MULTI) {
+            eg.load_first();
+            eu.load_first();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stage.store(act, ncp);
+        if constexpr (WT == kCB3) gstage.store(lds_grid);
+        __syncthreads();
+
+        float ag[kGroupPass], au[kGroupPass];
+#pragma unroll
+        for (int c = 0; c < kGroupPass; ++c) ag[c] = au[c] = 0.0f;
+        eg.run(act, ncp, lds_grid, ag, nullptr, 0, true);
+        eu.run(act, ncp, lds_grid, au, nullptr, 0, true);
+        float gsum = 0.0f, usum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kGroupPass; ++c) {
+            const float sg = row16_sum(ag[c]);
+            const float su = row16_sum(au[c]);
+            if (l16 == c) {
+                gsum = sg;
+                usum = su;
+            }
+        }
+        if (l16 < ncp) {
+            gl[l16 * 32 + rg] = gsum;
+            ul[l16 * 32 + rg] = usum;
+            if (dbg_g) {
+                dbg_g[(int64_t)(c0 + l16) * inter + i] = gsum;
+                dbg_u[(int64_t)(c0 + l16) * inter + i] = usum;
+            }
+        }
+        __syncthreads();
+        // SwiGLU -> q8_1: one half wave per entry (waves 0..3), value j = intermediate 32t + j
+        if (threadIdx.x < kGroupPass * 32) {
+            const int c = threadIdx.x >> 5, j = threadIdx.x & 31;
+            const bool ok = c < ncp;
+            const float h = ok ? silu_mul(gl[c * 32 + j], ul[c * 32 + j]) : 0.0f;
+            uint32_t hdr;
+            const int q = quantize_lanes32(h, hdr);
+            const uint32_t word = pack4_lanes(q);
+            if (ok) {
+                uint32_t* dst = (uint32_t*)(hq + ((int64_t)(c0 + c) * nbh + blockIdx.x) * 36);
+                if (j == 0) dst[0] = hdr;
+                if ((j & 3) == 0) dst[1 + (j >> 2)] = word;
+            }
+        }
+    }
+}
+
+template <int WT, int U, bool MULTI, int NS>
+__global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
+                                                            uint32_t expert_bytes, int nexperts,
+                                                            const uint8_t* __restrict__ grid, int hidden, int inter,
+                                                            const uint8_t* __restrict__ hq, uint32_t hqbytes,
+                                                            const int32_t* __restrict__ group_expert,
+                                                            const int32_t* __restrict__ group_off, int nentries,
+                                                            float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    GroupInfo gi;
+    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
+    const rsrc_t wr = make_rsrc_dw(wd + gi.e * d_stride, expert_bytes);
+    const rsrc_t hr = make_rsrc(hq, hqbytes);
+    for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
+        const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
+        if (c0 != gi.k0) __syncthreads();
+        gemv_tile<WT, false, kGroupPass, U, MULTI, NS>(wr, hidden, inter, grid, hr, c0, ncp, y, hidden, nullptr,
+                                                      blockIdx.x * kGemvRowsPerWG, lds);
+    }
+}
+
+template <int WT, typename F>
+static void dispatch_u_ns(int lb, int ns, F&& go) {
+    auto by_u = [&](auto ns_c) {
+        constexpr int NS = decltype(ns_c)::value;
+        if (lb <= 2) go.template operator()<WT, 2, false, NS>();
+        else if (lb <= 5) go.template operator()<WT, 5, false, NS>();
+        else if (lb == 6) go.template operator()<WT, 6, false, NS>();
+        else go.template operator()<WT, 6, true, NS>();
+    };
+    if (ns == 1) by_u(std::integral_constant<int, 1>{});
+    else if (ns == 2) by_u(std::integral_constant<int, 2>{});
+    else by_u(std::integral_constant<int, 4>{});
+}
+
+struct GroupedArgs {
+    int wtype_gu, wtype_down, nexperts, ngroups, nentries, xq_cols;
+    const uint8_t *w_gate, *w_up, *w_down, *grid, *xq;
+    int64_t gu_stride, d_stride, hidden, inter;
+    const int32_t *group_expert, *group_off, *entry_col;
+    float* y;
+    uint8_t* ws;
+    unsigned flags;
+    hipStream_t st;
+};
+
+static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nentries * (size_t)(inter / 32) * 36; }
+static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+static int launch_grouped(const GroupedArgs& a) {
+    const uint32_t gu_bytes = (uint32_t)(a.inter * qmm_row_bytes(a.wtype_gu, a.hidden));
+    const uint32_t d_bytes = (uint32_t)(a.hidden * qmm_row_bytes(a.wtype_down, a.inter));
+    const size_t hbytes = grouped_h_bytes(a.inter, a.nentries);
+    float* dbg_g = nullptr;
+    float* dbg_u = nullptr;
+    if (a.flags & QMM_FLAG_DEBUG_INTERMEDIATES) {
+        dbg_g = (float*)(a.ws + align16(hbytes));
+        dbg_u = dbg_g + (size_t)a.nentries * a.inter;
+    }
+    const uint32_t xqbytes = (uint32_t)((uint64_t)a.xq_cols * (a.hidden / 32) * 36);
+    {
+        const size_t lds = gemv_lds_bytes(a.wtype_gu, a.hidden, kGroupPass) + 2 * kGroupPass * 32 * sizeof(float);
+        const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
+        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
+            hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGemvThreads), lds, a.st, a.w_gate, a.w_up,
+                               a.gu_stride, gu_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes,
+                               a.xq_cols, a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
+        };
+        const int lb = lane_blocks(a.hidden), ns = stage_slots(a.hidden, kGroupPass, kGemvThreads);
+        if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0>(lb, ns, go);
+        else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(lb, ns, go);
+        else dispatch_u_ns<kCB3>(lb, ns, go);
+        const int rc = launch_status();
+        if (rc) return rc;
+    }
+    {
+        const size_t lds = gemv_lds_bytes(a.wtype_down, a.inter, kGroupPass);
+        const dim3 grid_dim((unsigned)((a.hidden + kGemvRowsPerWG - 1) / kGemvRowsPerWG), (unsigned)a.ngroups);
+        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
+            hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGemvThreads), lds, a.st, a.w_down,
+                               a.d_stride, d_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.ws,
+                               (uint32_t)hbytes, a.group_expert, a.group_off, a.nentries, a.y);
+        };
+        const int lb = lane_blocks(a.inter), ns = stage_slots(a.inter, kGroupPass, kGemvThreads);
+        if (a.wtype_down == QMM_Q8_0) dispatch_u_ns<kQ8_0>(lb, ns, go);
+        else if (a.wtype_down == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(lb, ns, go);
+        else dispatch_u_ns<kCB3>(lb, ns, go);
+        return launch_status();
+    }
+}
+
+}  // namespace qmm
+
+using namespace qmm;
+
+extern "C" size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned flags) {
+    if (inter <= 0 || nentries < 0) return 0;
+    size_t b = align16(grouped_h_bytes(inter, nentries));
+    if (flags & QMM_FLAG_DEBUG_INTERMEDIATES) b += 2 * (size_t)nentries * (size_t)inter * sizeof(float);
+    return b;
+}
+
+extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up, int64_t gu_expert_stride,
+                                     int wtype_down, const void* w_down, int64_t down_expert_stride, int nexperts,
+                                     const uint8_t* grid, int64_t hidden, int64_t inter, const void* xq, int xq_cols,
+                                     const int32_t* group_expert, const int32_t* group_entry_off, int ngroups,
+                                     const int32_t* entry_col, int nentries, float* y, void* ws, size_t ws_bytes,
+                                     unsigned flags, void* stream) {
+    if (!valid_wtype(wtype_gu) || !valid_wtype(wtype_down)) return QMM_EINVAL;
+    if (!w_gate || !w_up || !w_down || !xq || !group_expert || !group_entry_off || !entry_col || !y || !ws)
+        return QMM_EINVAL;
+    if ((wtype_gu == QMM_CB3 || wtype_down == QMM_CB3) && !grid) return QMM_EINVAL;
+    if (nexperts < 1 || ngroups < 0 || nentries < 0 || xq_cols < 1 || hidden < 32 || inter < 32) return QMM_EINVAL;
+    if (qmm_row_bytes(wtype_gu, hidden) == 0 || qmm_row_bytes(wtype_down, inter) == 0) return QMM_EINVAL;
+    if (hidden > kMaxK || inter > kMaxK || ngroups > 65535) return QMM_EUNSUPPORTED;
+    const int64_t gu_bytes = inter * qmm_row_bytes(wtype_gu, hidden);
+    const int64_t d_bytes = hidden * qmm_row_bytes(wtype_down, inter);
+    if (gu_expert_stride < gu_bytes || down_expert_stride < d_bytes) return QMM_EINVAL;
+    if (gu_expert_stride % 4 || down_expert_stride % 4) return QMM_EALIGN;
+    if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(xq, 4) || !aligned(y, 4) ||
+        !aligned(ws, 16))
+        return QMM_EALIGN;
+    // a pass of 8 entries must fit the workgroup's LDS and staging slots
+    if (gemv_lds_bytes(wtype_gu, hidden, kGroupPass) + 2 * kGroupPass * 32 * 4 > kLdsCap ||
+        gemv_lds_bytes(wtype_down, inter, kGroupPass) > kLdsCap ||
+        (int64_t)kGroupPass * pow2_ceil(hidden / 32) > (int64_t)kStageSlots * kGemvThreads ||
+        (int64_t)kGroupPass * pow2_ceil(inter / 32) > (int64_t)kStageSlots * kGemvThreads)
+        return QMM_EUNSUPPORTED;
+    if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxBufferBytes ||
+        grouped_h_bytes(inter, nentries) > kMaxBufferBytes)
+        return QMM_EUNSUPPORTED;
+    if (ws_bytes < qgemv_grouped_experts_workspace(inter, nentries, flags)) return QMM_ESPACE;
+    if (ngroups == 0 || nentries == 0) return QMM_OK;
+    GroupedArgs a;
+    a.wtype_gu = wtype_gu;
+    a.wtype_down = wtype_down;
+    a.nexperts = nexperts;
+    a.ngroups = ngroups;
+    a.nentries = nentries;
+    a.xq_cols = xq_cols;
+    a.w_gate = (const uint8_t*)w_gate;
+    a.w_up = (const uint8_t*)w_up;
+    a.w_down = (const uint8_t*)w_down;
+    a.grid = grid;
+    a.xq = (const uint8_t*)xq;
+    a.gu_stride = gu_expert_stride;
+    a.d_stride = down_expert_stride;
+    a.hidden = hidden;
+    a.inter = inter;
+    a.group_expert = group_expert;
+    a.group_off = group_entry_off;
+    a.entry_col = entry_col;
+    a.y = y;
+    a.ws = (uint8_t*)ws;
+    a.flags = flags;
+    a.st = as_stream(stream);
+    return launch_grouped(a);
+}

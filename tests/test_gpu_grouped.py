@@ -1,0 +1,155 @@
+"""GPU parity of the grouped MoE decode (gate/up + SwiGLU + q8_1 + down over groups x entries)
+against the oracle, with the interval check of tests/grouped_check.py for the q8_1 decisions."""
+import numpy as np
+import pytest
+
+import moe_expert_amd as M
+import oracle
+import synth
+from tests.gpu_util import dev, host
+from tests.grouped_check import check_grouped
+
+pytestmark = pytest.mark.gpu
+
+
+class Experts:
+    def __init__(self, seed, nexp, hidden, inter, wt_gu=M.QMM_CB3, wt_down=M.QMM_IQ4_NL):
+        rng = synth.rng_for(seed)
+        self.grid = synth.cb3_grid(synth.rng_for(synth.SEEDS["cb3_grid"]))
+        self.wt_gu, self.wt_down = wt_gu, wt_down
+        self.hidden, self.inter, self.nexp = hidden, inter, nexp
+        self.wg = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
+        self.wu = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
+        self.wd = np.stack([synth.weights(wt_down, rng, hidden, inter) for _ in range(nexp)])
+        self.d = dict(wg=dev(self.wg), wu=dev(self.wu), wd=dev(self.wd), grid=dev(self.grid))
+        self._wd_exact = {}
+
+    def wd_exact(self, e):
+        if e not in self._wd_exact:
+            self._wd_exact[e] = oracle.dequant_f64(self.wt_down, self.wd[e], self.inter, self.grid)
+        return self._wd_exact[e]
+
+    def run_gpu(self, xq, ge, go, ec, flags=M.QMM_FLAG_DEBUG_INTERMEDIATES, y=None):
+        y, ws = M.qgemv_grouped_experts(self.wt_gu, self.d["wg"], self.d["wu"], self.wt_down, self.d["wd"], self.hidden,
+                                        self.inter, xq, dev(ge), dev(go), dev(ec), grid=self.d["grid"], y=y, flags=flags)
+        return y, ws
+
+    def split_ws(self, ws, nentries):
+        w = host(ws)
+        hbytes = nentries * (self.inter // 32) * 36
+        hq = w[:hbytes].reshape(nentries, -1)
+        off = (hbytes + 15) // 16 * 16
+        g = w[off:off + 4 * nentries * self.inter].view(np.float32).reshape(nentries, self.inter)
+        u = w[off + 4 * nentries * self.inter: off + 8 * nentries * self.inter].view(np.float32).reshape(nentries, self.inter)
+        return hq, g, u
+
+    def oracle(self, xq_h, ge, go, ec):
+        return oracle.grouped(self.wt_gu, self.wg, self.wu, self.wt_down, self.wd, self.hidden, self.inter, xq_h,
+                              ge, go, ec, self.grid)
+
+
+def depth_of(k):
+    """Roundings a block term passes through in the GPU reduction: one fma per block a lane
+    holds, then four DPP additions."""
+    return (k // 32 + 15) // 16 + 4
+
+
+def run_case(ex, ge, go, ec, ncols, seed):
+    x = synth.activations(synth.rng_for(seed), ncols, ex.hidden)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    xq_h = host(xq)
+    assert np.array_equal(xq_h, oracle.quantize_q8_1(x))
+    y, ws = ex.run_gpu(xq, ge, go, ec)
+    hq, g, u = ex.split_ws(ws, ec.size)
+    ref = ex.oracle(xq_h, ge, go, ec)
+    entry_expert = np.repeat(ge, np.diff(go))
+    stats = check_grouped(ref, host(y), hq, g.astype(np.float64), u.astype(np.float64),
+                          lambda k: ex.wd_exact(int(entry_expert[k])), ex.inter, depth_of(ex.hidden))
+    print("grouped check:", stats, flush=True)
+    return y, hq, g, u, xq
+
+
+def test_grouped_small():
+    print("grouped small: 5 experts 512->64, 3 groups x 3 entries", flush=True)
+    ex = Experts(800, 5, 512, 64)
+    ge, go, ec = synth.decode_routing(synth.rng_for(801), 5, 3, 3)
+    ec = ec[::-1].copy()
+    run_case(ex, ge, go, ec, 3, 802)
+
+
+def test_grouped_ragged_passes():
+    """Groups of 1, 11 (two passes) and 0 entries; uneven column map."""
+    print("grouped ragged: groups of 1, 11, 0 entries", flush=True)
+    ex = Experts(810, 6, 768, 96, wt_gu=M.QMM_CB3, wt_down=M.QMM_Q8_0)
+    ge = np.array([4, 1, 2], np.int32)
+    go = np.array([0, 1, 12, 12], np.int32)
+    ec = synth.rng_for(811).integers(0, 5, size=12).astype(np.int32)
+    run_case(ex, ge, go, ec, 5, 812)
+
+
+@pytest.mark.parametrize("wt_gu,wt_down", [(M.QMM_IQ4_NL, M.QMM_Q8_0), (M.QMM_Q8_0, M.QMM_IQ4_NL)])
+def test_grouped_other_formats(wt_gu, wt_down):
+    print(f"grouped formats gu={wt_gu} down={wt_down}", flush=True)
+    ex = Experts(820 + wt_gu, 4, 1024, 128, wt_gu=wt_gu, wt_down=wt_down)
+    ge, go, ec = synth.decode_routing(synth.rng_for(821), 4, 4, 2)
+    run_case(ex, ge, go, ec, 2, 822)
+
+
+@pytest.fixture(scope="module")
+def full_experts():
+    """The grouped decode workload: 128 experts, hidden 2560, CB3 gate/up 2560->1024, IQ4_NL
+    down 1024->2560."""
+    print("building 128 experts (2560 -> 1024 -> 2560)", flush=True)
+    return Experts(synth.SEEDS["grouped_decode"], 128, 2560, 1024)
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_grouped_full_size(full_experts, m):
+    print(f"grouped full size: 16 groups x {m} entries", flush=True)
+    ge, go, ec = synth.decode_routing(synth.rng_for(synth.SEEDS["grouped_decode"] + m), 128, 16, m)
+    run_case(full_experts, ge, go, ec, m, synth.SEEDS["grouped_decode"] + 100 + m)
+
+
+def test_grouped_matches_dense_and_entry_invariance(full_experts):
+    """Gate/up sums equal qgemv_dense on the same expert matrix bitwise; an entry's y does not
+    depend on the other entries of its group (m = 1 vs m = 8)."""
+    print("grouped vs dense / entry invariance", flush=True)
+    ex = full_experts
+    ge, go, ec = synth.decode_routing(synth.rng_for(830), 128, 16, 8)
+    x = synth.activations(synth.rng_for(831), 8, ex.hidden)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    y8, ws8 = ex.run_gpu(xq, ge, go, ec)
+    hq8, g8, u8 = ex.split_ws(ws8, ec.size)
+    for gi in (0, 7, 15):
+        e = int(ge[gi])
+        yd = host(M.qgemv_dense(ex.wt_gu, ex.d["wg"][e], ex.inter, ex.hidden, xq, 8, grid=ex.d["grid"]))
+        for j in range(8):
+            k = go[gi] + j
+            assert np.array_equal(g8[k].view(np.uint32), yd[ec[k]].view(np.uint32)), (gi, j)
+    # the same groups with one entry each (entry j = 0 of every group)
+    go1 = np.arange(17, dtype=np.int32)
+    ec1 = np.zeros(16, np.int32)
+    y1, ws1 = ex.run_gpu(xq, ge, go1, ec1)
+    y8h, y1h = host(y8), host(y1)
+    for gi in range(16):
+        k8 = go[gi] + int(np.nonzero(ec[go[gi]:go[gi + 1]] == 0)[0][0])
+        assert np.array_equal(y1h[gi].view(np.uint32), y8h[k8].view(np.uint32)), gi
+
+
+def test_grouped_skips_bad_groups_and_columns():
+    """A group with an expert out of range is skipped (its rows untouched); an entry whose column
+    is out of range reads zero activations (y = 0)."""
+    print("grouped bad expert / column", flush=True)
+    import torch
+    ex = Experts(840, 3, 512, 64)
+    ge = np.array([0, 7, 2], np.int32)            # expert 7 does not exist
+    go = np.array([0, 2, 4, 6], np.int32)
+    ec = np.array([0, 1, 0, 1, 1, 9], np.int32)   # column 9 does not exist (2 columns)
+    x = synth.activations(synth.rng_for(841), 2, ex.hidden)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    y = torch.full((6, ex.hidden), float("nan"), device="cuda")
+    ex.run_gpu(xq, ge, go, ec, flags=0, y=y)
+    yh = host(y)
+    assert np.isnan(yh[2:4]).all()
+    assert (yh[5] == 0).all()
+    assert np.isfinite(yh[[0, 1, 4]]).all()
