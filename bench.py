@@ -1,19 +1,23 @@
-"""Benchmark of the dense decode GEMV on MI355X: IQ4_NL 8192 x 2560 weights x q8_1 activations at
-1, 4 and 8 columns, on cold weights.
+"""Benchmark of the block-quantized hot path on one MI355X.
 
-One step = the hot path once per column count n in (1, 4, 8): q8_1 quantization of the n
-activation columns, then the n-column GEMV over the next weight copy of a rotation.  The
-rotation holds enough copies (44 x 11.8 MB = 519 MB) to exceed twice the 256 MB Infinity Cache,
-so every GEMV reads its weights from HBM.  The six launches of a step are replayed from a HIP
-graph (one graph per rotation slot); inputs are resident in HBM before the timed region.
+Default workload (the headline): dense decode GEMV, IQ4_NL 8192 x 2560 weights x q8_1
+activations at 1, 4 and 8 columns, on cold weights.  One step = the hot path once per column
+count n in (1, 4, 8): q8_1 quantization of the n activation columns, then the n-column GEMV over
+the next weight copy of a rotation whose total (44 copies, 519 MB) exceeds twice the 256 MB
+Infinity Cache, so every GEMV reads its weights from HBM.  The launches of a step are replayed
+from a HIP graph (one per rotation slot); inputs are resident in HBM before the timed region.
 
-Prints one JSON line (see the fields below).  `value` is the step's algorithmic bytes (weights,
-q8_1 activations, fp32 outputs, quantizer reads/writes) divided by the step time.  `roofline` is
-the GEMV kernel's algorithmic bytes per launch over its average launch duration, timed with HIP
-events on the launch stream around graph-batched launches of each column count.
-`cpu_baseline` times the CPU oracle on the same workload.
+Other workloads (--workload): q8_0 (Q8_0 12288 x 2560 at 1-4 columns, and 2560 x 6144 at 7-8
+columns), grouped (grouped MoE decode, 128 experts, 16 groups x m entries, m = 1/4/8), prefill
+(prefill grouped expert GEMM, 8192 tokens x 2560, top-8 of 128 experts).  Each prints its own
+JSON line with the same fields.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-graph] [--no-cpu]
+Fields: `value` = algorithmic bytes (GEMV, grouped) or FLOPs (prefill) of a step / step time;
+`roofline` = the dominant kernel's algorithmic bytes or FLOPs per launch over its average
+launch duration, timed with HIP events on the launch stream around graph-batched launches;
+`cpu_baseline` = the CPU oracle on the same workload (or a stated sample of it).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload W] [--no-graph] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -28,19 +32,309 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-NROWS, K = 8192, 2560
-COLS = (1, 4, 8)
-NCOPIES = 44            # 44 x 11,796,480 B = 519 MB > 2 x 256 MB Infinity Cache
-NDISTINCT = 6           # distinct seeded copies; the rest of the rotation repeats them at other addresses
+FP16_MFMA_PEAK_TFLOPS = 2516.6
+MALL_BYTES = 256 << 20
 
 
-def gemv_bytes(n: int) -> int:
+def timed_graph(torch, fn, reps, use_graph=True):
+    """Average ms of fn() over `reps` runs after one warm run; graph-captured when use_graph."""
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        run = g.replay
+    else:
+        run = fn
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def contract_steps(torch, run_step, steps, warmup):
+    """W untimed steps, then exactly K timed steps between synchronisations; ms per step."""
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        run_step(warmup + i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def capture_slots(torch, step, nslots):
+    """One HIP graph per rotation slot of `step`; returns run_step(i)."""
+    graphs = []
+    for slot in range(nslots):
+        step(slot)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(slot)
+        graphs.append(g)
+    return lambda i: graphs[i % nslots].replay()
+
+
+def base_line(metric, value, unit, args, ms, dtype, config, higher=True):
+    return {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": higher, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config}
+
+
+# ------------------------------------------------------------------ dense decode GEMV
+
+def gemv_bytes(wtype, nrows, k, n):
     """Algorithmic bytes of one n-column GEMV: every weight byte once, n q8_1 columns, n fp32 rows."""
-    return NROWS * (K // 32) * 18 + n * (K // 32) * 36 + n * NROWS * 4
+    import synth
+    return nrows * synth.row_bytes(wtype, k) + n * (k // 32) * 36 + n * nrows * 4
 
 
-def quant_bytes(n: int) -> int:
-    return n * K * 4 + n * (K // 32) * 36
+def quant_bytes(k, n):
+    return n * k * 4 + n * (k // 32) * 36
+
+
+def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndistinct=6):
+    import synth
+    wbytes = nrows * synth.row_bytes(wtype, k)
+    ncopies = max(ndistinct, -(-2 * MALL_BYTES // wbytes) + 1)
+    dev = torch.device("cuda", 0)
+    host_copies = [synth.weights(wtype, synth.rng_for(seed + i), nrows, k) for i in range(ndistinct)]
+    copies = [torch.from_numpy(host_copies[i % ndistinct]).to(dev) for i in range(ncopies)]
+    rng = synth.rng_for(seed + 100)
+    xs = {n: torch.from_numpy(synth.activations(rng, n, k)).to(dev) for n in cols}
+    xqs = {n: torch.empty((n, (k // 32) * 36), dtype=torch.uint8, device=dev) for n in cols}
+    ys = {n: torch.empty((n, nrows), dtype=torch.float32, device=dev) for n in cols}
+    for n in cols:
+        M.qmm_quantize_q8_1(xs[n], out=xqs[n])
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+
+    def step(slot):
+        w = copies[slot % ncopies]
+        for n in cols:
+            M.qmm_quantize_q8_1(xs[n], out=xqs[n])
+            M.qgemv_dense(wtype, w, nrows, k, xqs[n], n, y=ys[n])
+
+    run_step = capture_slots(torch, step, ncopies) if use_graph else step
+    ms = contract_steps(torch, run_step, args.steps, args.warmup)
+    step_bytes = sum(gemv_bytes(wtype, nrows, k, n) + quant_bytes(k, n) for n in cols)
+
+    us, gbps, warm, literal = {}, {}, {}, {}
+    tot_b = tot_us = 0.0
+    for n in cols:
+        def batch(n=n):
+            for w in copies:
+                M.qgemv_dense(wtype, w, nrows, k, xqs[n], n, y=ys[n])
+        t = timed_graph(torch, batch, args.batch_reps, use_graph) * 1e3 / ncopies
+        us[str(n)] = round(t, 3)
+        gbps[str(n)] = round(gemv_bytes(wtype, nrows, k, n) / (t * 1e-6) / 1e9, 1)
+        tot_b += gemv_bytes(wtype, nrows, k, n)
+        tot_us += t
+
+        def warm_batch(n=n):
+            for _ in range(ncopies):
+                M.qgemv_dense(wtype, copies[0], nrows, k, xqs[n], n, y=ys[n])
+        warm[str(n)] = round(timed_graph(torch, warm_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
+
+        def lit_batch(n=n):
+            for i in range(ncopies):
+                M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
+        literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
+    achieved = tot_b / (tot_us * 1e-6) / 1e9
+    out = base_line(metric, step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
+                    {"workload": f"{name}, cold rotation of {ncopies} weight copies "
+                                 f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
+                     "weight_copies": ncopies, "hip_graph": use_graph})
+    out.update({"us_per_call": us, "gbps_per_call": gbps, "warm_us_per_call": warm,
+                f"rotation_{ndistinct}_copies_us_per_call": literal,
+                "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": f"gemv_kernel ({name.split(',')[0]}), columns {list(cols)}"}})
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_gemv(wtype, host_copies[0], nrows, k, cols, seed, step_bytes)
+    return out
+
+
+def cpu_gemv(wtype, w_host, nrows, k, cols, seed, step_bytes, min_s=10.0):
+    """The oracle on the same step, repeated until about min_s seconds of CPU work have run."""
+    import oracle
+    import synth
+    rng = synth.rng_for(seed + 100)
+    xs = {n: synth.activations(rng, n, k) for n in cols}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for n in cols:
+            oracle.gemv(wtype, w_host, k, oracle.quantize_q8_1(xs[n]))
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            break
+    per = dt / reps
+    return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full step ({nrows} rows at {list(cols)} columns + q8_1 of the columns) x {reps} "
+                      f"repetitions, {dt:.1f} s, {per * 1e3:.1f} ms per step"}
+
+
+# ------------------------------------------------------------------ grouped MoE decode
+
+def grouped_bytes(hidden, inter, ngroups, m, expert_bytes):
+    """Algorithmic bytes of one call: the groups' experts once, m q8_1 columns, H written and read,
+    fp32 outputs."""
+    nent = ngroups * m
+    return ngroups * expert_bytes + m * (hidden // 32) * 36 + nent * (inter // 32) * 36 * 2 + nent * hidden * 4
+
+
+def bench_grouped(args, torch, M):
+    import numpy as np
+
+    import synth
+    nexp, hidden, inter, ngroups = 128, 2560, 1024, 16
+    ms_list = (1, 4, 8)
+    seed = synth.SEEDS["grouped_decode"]
+    rng = synth.rng_for(seed)
+    grid = synth.cb3_grid(synth.rng_for(synth.SEEDS["cb3_grid"]))
+    dev = torch.device("cuda", 0)
+    expert_bytes = 2 * synth.row_bytes(synth.CB3, hidden) * inter + synth.row_bytes(synth.IQ4_NL, inter) * hidden
+    nsets = max(2, -(-2 * MALL_BYTES // (nexp * expert_bytes)) + 1)   # expert sets in rotation
+    host = dict(wg=np.stack([synth.cb3_weights(rng, inter, hidden) for _ in range(nexp)]),
+                wu=np.stack([synth.cb3_weights(rng, inter, hidden) for _ in range(nexp)]),
+                wd=np.stack([synth.iq4nl_weights(rng, hidden, inter) for _ in range(nexp)]))
+    sets = [{k: torch.from_numpy(v).to(dev) for k, v in host.items()} for _ in range(nsets)]
+    gd = torch.from_numpy(grid).to(dev)
+    calls = {}
+    for m in ms_list:
+        ge, go, ec = synth.decode_routing(synth.rng_for(seed + m), nexp, ngroups, m)
+        x = synth.activations(synth.rng_for(seed + 100 + m), m, hidden)
+        xd = torch.from_numpy(x).to(dev)
+        xq = M.qmm_quantize_q8_1(xd)
+        y = torch.empty((ngroups * m, hidden), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, M.qgemv_grouped_experts_workspace(inter, ngroups * m)), dtype=torch.uint8, device=dev)
+        calls[m] = dict(ge=torch.from_numpy(ge).to(dev), go=torch.from_numpy(go).to(dev),
+                        ec=torch.from_numpy(ec).to(dev), x=xd, xq=xq, y=y, ws=ws, host=(ge, go, ec, x))
+    use_graph = not args.no_graph
+
+    def call(m, s):
+        c = calls[m]
+        M.qgemv_grouped_experts(synth.CB3, s["wg"], s["wu"], synth.IQ4_NL, s["wd"], hidden, inter, c["xq"], c["ge"],
+                                c["go"], c["ec"], grid=gd, y=c["y"], ws=c["ws"])
+
+    def step(slot):
+        s = sets[slot % nsets]
+        for m in ms_list:
+            M.qmm_quantize_q8_1(calls[m]["x"], out=calls[m]["xq"])
+            call(m, s)
+
+    run_step = capture_slots(torch, step, nsets) if use_graph else step
+    ms = contract_steps(torch, run_step, args.steps, args.warmup)
+    step_bytes = sum(grouped_bytes(hidden, inter, ngroups, m, expert_bytes) + quant_bytes(hidden, m) for m in ms_list)
+    us, gbps = {}, {}
+    tot_b = tot_us = 0.0
+    for m in ms_list:
+        def batch(m=m):
+            for s in sets:
+                call(m, s)
+        t = timed_graph(torch, batch, args.batch_reps, use_graph) * 1e3 / nsets
+        b = grouped_bytes(hidden, inter, ngroups, m, expert_bytes)
+        us[str(m)] = round(t, 3)
+        gbps[str(m)] = round(b / (t * 1e-6) / 1e9, 1)
+        tot_b += b
+        tot_us += t
+    ach = tot_b / (tot_us * 1e-6) / 1e9
+    out = base_line("µs/call and achieved HBM GB/s, grouped MoE decode (16 groups x m entries, 128 experts)",
+                    step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
+                    {"workload": "grouped MoE decode: hidden 2560, 128 experts, CB3 gate/up 2560->1024, IQ4_NL down "
+                                 f"1024->2560, 16 groups x m entries (m = 1/4/8); {nsets} expert sets in rotation "
+                                 f"({nsets * nexp * expert_bytes / 1e6:.0f} MB)", "entries_per_group": list(ms_list),
+                     "hip_graph": use_graph})
+    out.update({"us_per_call": us, "gbps_per_call": gbps,
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": "gu_kernel + down_kernel (one call, m = 1/4/8)"}})
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for m in ms_list:
+                ge, go, ec, x = calls[m]["host"]
+                oracle.grouped(synth.CB3, host["wg"], host["wu"], synth.IQ4_NL, host["wd"], hidden, inter,
+                               oracle.quantize_q8_1(x), ge, go, ec, grid)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0:
+                break
+        out["cpu_baseline"] = {"value": round(step_bytes / (dt / reps) / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"the full step (m = 1/4/8) x {reps}, {dt:.1f} s"}
+    return out
+
+
+# ------------------------------------------------------------------ prefill grouped expert GEMM
+
+def bench_prefill(args, torch, M):
+    import numpy as np
+
+    import synth
+    nexp, ntok, topk, hidden, inter = 128, 8192, 8, 2560, 1024
+    seed = synth.SEEDS["prefill"]
+    rng = synth.rng_for(seed)
+    dev = torch.device("cuda", 0)
+    wg = np.stack([synth.iq4nl_weights(rng, inter, hidden) for _ in range(nexp)])
+    wu = np.stack([synth.iq4nl_weights(rng, inter, hidden) for _ in range(nexp)])
+    wd = np.stack([synth.q8_0_weights(rng, hidden, inter) for _ in range(nexp)])
+    x16 = synth.prefill_tokens(rng, ntok, hidden)
+    st, off = synth.prefill_routing(rng, ntok, nexp, topk)
+    d = dict(wg=torch.from_numpy(wg).to(dev), wu=torch.from_numpy(wu).to(dev), wd=torch.from_numpy(wd).to(dev),
+             x=torch.from_numpy(x16.view(np.uint16)).to(dev), st=torch.from_numpy(st).to(dev),
+             off=torch.from_numpy(off).to(dev))
+    nent = st.size
+    y = torch.empty((nent, hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.qgemm_prefill_experts_workspace(nexp, inter, nent), dtype=torch.uint8, device=dev)
+
+    def call(_i=0):
+        M.qgemm_prefill_experts(synth.IQ4_NL, d["wg"], d["wu"], synth.Q8_0, d["wd"], nexp, hidden, inter, d["x"],
+                                d["st"], d["off"], y=y, ws=ws)
+
+    use_graph = not args.no_graph
+    run_step = capture_slots(torch, call, 1) if use_graph else call
+    ms = contract_steps(torch, run_step, args.steps, args.warmup)
+    flops = 2.0 * nent * 2 * inter * hidden + 2.0 * nent * hidden * inter
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = base_line("µs/call and MFMA TFLOP/s, prefill grouped expert GEMM (8192 tokens x 2560, top-8 of 128)",
+                    tflops, "TFLOP/s", args, ms, "fp16",
+                    {"workload": "prefill grouped expert GEMM: 8192 tokens x hidden 2560, top-8 of 128 experts, "
+                                 "IQ4_NL gate/up 2560->1024, Q8_0 down 1024->2560, FP16 dequant in LDS + fp16 MFMA",
+                     "tokens": ntok, "entries": int(nent), "hip_graph": use_graph})
+    out.update({"us_per_call": round(ms * 1e3, 2),
+                "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": "schedule + pf_gateup_kernel + pf_down_kernel (one call)"}})
+    if not args.no_cpu:
+        import oracle
+        samples = np.arange(off[0], off[0] + 32, dtype=np.int64)   # 32 rows of expert 0
+        t0 = time.perf_counter()
+        oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off, samples)
+        dt = time.perf_counter() - t0
+        per_row = dt / samples.size
+        out["cpu_baseline"] = {"value": round(flops / nent / per_row / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"32 rows of expert 0 (incl. dequantizing its weights), {dt:.2f} s, "
+                                         f"scaled to {nent} rows"}
+    return out
 
 
 def main() -> int:
@@ -48,186 +342,40 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gemv", choices=["gemv", "q8_0", "grouped", "prefill"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--batch-reps", type=int, default=5, help="graph replays per column count for the roofline timing")
+    ap.add_argument("--batch-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode GEMV is measured on one "
-              "GPU's share; see the design notes for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): each workload is measured on one "
+              "GPU's share; the design notes say how it would shard.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import moe_expert_amd as M
     import synth
 
     torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
-    t0 = time.time()
-    host_copies = [synth.iq4nl_weights(synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + i), NROWS, K)
-                   for i in range(NDISTINCT)]
-    copies = [torch.from_numpy(host_copies[i % NDISTINCT]).to(dev) for i in range(NCOPIES)]
-    rng = synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + 100)
-    xs = {n: torch.from_numpy(synth.activations(rng, n, K)).to(dev) for n in COLS}
-    xqs = {n: torch.empty((n, (K // 32) * 36), dtype=torch.uint8, device=dev) for n in COLS}
-    ys = {n: torch.empty((n, NROWS), dtype=torch.float32, device=dev) for n in COLS}
-    torch.cuda.synchronize()
-    setup_s = time.time() - t0
-
-    def step(slot: int):
-        w = copies[slot % NCOPIES]
-        for n in COLS:
-            M.qmm_quantize_q8_1(xs[n], out=xqs[n])
-            M.qgemv_dense(M.QMM_IQ4_NL, w, NROWS, K, xqs[n], n, y=ys[n])
-
-    def gemv_batch(n: int):
-        for i in range(NCOPIES):
-            M.qgemv_dense(M.QMM_IQ4_NL, copies[i], NROWS, K, xqs[n], n, y=ys[n])
-
-    use_graph = not args.no_graph
-    side = torch.cuda.Stream()
-    graphs, batch_graphs = [], {}
-    if use_graph:
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(0)
-            for n in COLS:
-                gemv_batch(n)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        for slot in range(NCOPIES):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(slot)
-            graphs.append(g)
-        for n in COLS:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                gemv_batch(n)
-            batch_graphs[n] = g
-        torch.cuda.synchronize()
-
-    def run_step(i: int):
-        if use_graph:
-            graphs[i % NCOPIES].replay()
-        else:
-            step(i)
-
-    # ---- the contract: W untimed steps, then exactly K timed steps between synchronisations
-    for i in range(args.warmup):
-        run_step(i)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        run_step(args.warmup + i)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
-    step_bytes = sum(gemv_bytes(n) + quant_bytes(n) for n in COLS)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # ---- GEMV launches alone, graph-batched over the cold rotation, HIP events on the launch stream
-    us_per_call, gbps = {}, {}
-    tot_bytes = tot_us = 0.0
-    for n in COLS:
-        run = (batch_graphs[n].replay if use_graph else (lambda n=n: gemv_batch(n)))
-        run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.batch_reps):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (args.batch_reps * NCOPIES)
-        us_per_call[str(n)] = round(us, 3)
-        gbps[str(n)] = round(gemv_bytes(n) / (us * 1e-6) / 1e9, 1)
-        tot_bytes += gemv_bytes(n)
-        tot_us += us
-    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
-
-    # ---- warm context: one copy, repeated (largely served from the Infinity Cache), graph-batched
-    warm = {}
-    for n in COLS:
-        def warm_batch(n=n):
-            for _ in range(NCOPIES):
-                M.qgemv_dense(M.QMM_IQ4_NL, copies[0], NROWS, K, xqs[n], n, y=ys[n])
-        if use_graph:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                warm_batch()
-            run = g.replay
-        else:
-            run = warm_batch
-        run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.batch_reps):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        warm[str(n)] = round(e0.elapsed_time(e1) * 1e3 / (args.batch_reps * NCOPIES), 3)
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(host_copies[0], step_bytes)
-
-    out = {
-        "metric": "µs/call and achieved HBM GB/s, IQ4_NL 8192x2560 GEMV at 1/4/8 columns",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8",
-        "data": "synthetic",
-        "config": {"workload": "IQ4_NL dense decode GEMV 8192x2560 x q8_1, 1/4/8 columns, cold rotation of "
-                               f"{NCOPIES} weight copies ({NCOPIES * NROWS * (K // 32) * 18 / 1e6:.0f} MB)",
-                   "nrows": NROWS, "k": K, "columns": list(COLS), "weight_copies": NCOPIES,
-                   "hip_graph": use_graph},
-        "us_per_call": us_per_call,
-        "gbps_per_call": gbps,
-        "warm_us_per_call": warm,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel<IQ4_NL> (1, 4, 8 columns)"},
-        "cpu_baseline": cpu,
-        "setup_s": round(setup_s, 1),
-    }
-    print(json.dumps(out), flush=True)
+    if args.workload == "gemv":
+        out = bench_gemv(args, torch, M, synth.IQ4_NL, 8192, 2560, (1, 4, 8), synth.SEEDS["iq4nl_8192x2560"],
+                         "µs/call and achieved HBM GB/s, IQ4_NL 8192x2560 GEMV at 1/4/8 columns",
+                         "IQ4_NL dense decode GEMV 8192x2560 x q8_1, 1/4/8 columns")
+        print(json.dumps(out), flush=True)
+    elif args.workload == "q8_0":
+        for nrows, k, cols, seed, name in ((12288, 2560, (1, 2, 3, 4), synth.SEEDS["q8_0_12288x2560"],
+                                            "Q8_0 dense decode GEMV 12288x2560 x q8_1, 1-4 columns"),
+                                           (2560, 6144, (7, 8), synth.SEEDS["q8_0_2560x6144"],
+                                            "Q8_0 dense decode GEMV 2560x6144 x q8_1, 7-8 columns")):
+            out = bench_gemv(args, torch, M, synth.Q8_0, nrows, k, cols, seed,
+                             f"µs/call and achieved HBM GB/s, {name}", name)
+            print(json.dumps(out), flush=True)
+    elif args.workload == "grouped":
+        print(json.dumps(bench_grouped(args, torch, M)), flush=True)
+    else:
+        print(json.dumps(bench_prefill(args, torch, M)), flush=True)
     return 0
-
-
-def cpu_baseline(w_host, step_bytes: int, min_s: float = 10.0) -> dict:
-    """The oracle on the same step (all 8192 rows at 1, 4 and 8 columns, plus the quantizer),
-    repeated until about ``min_s`` seconds of CPU work have run."""
-    import oracle
-    import synth
-    rng = synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + 100)
-    xs = {n: synth.activations(rng, n, K) for n in COLS}
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for n in COLS:
-            xq = oracle.quantize_q8_1(xs[n])
-            oracle.gemv(oracle.IQ4_NL, w_host, K, xq)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_s:
-            break
-    per_step = dt / reps
-    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the full step (8192 rows at 1/4/8 columns + q8_1 of the columns) x {reps} repetitions, "
-                      f"{dt:.1f} s, {per_step * 1e3:.1f} ms per step"}
 
 
 if __name__ == "__main__":
