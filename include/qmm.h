@@ -98,9 +98,10 @@ int qmm_dequant_f16(int wtype, const void* w, const uint8_t* grid, int64_t nrows
  *   w    : nrows x qmm_row_bytes(wtype, k) bytes, 4-byte aligned.
  *   grid : CB3 codebook or NULL.
  *   xq   : q8_1 [ncols][k/32][36], 4-byte aligned.   y: float, ldy >= nrows, 4-byte aligned.
- *   k    : multiple of 64 for Q8_0 / IQ4_NL (blocks are read in 4-byte aligned pairs), of 256
- *          for CB3; at most 32768.  ncols >= 1 (any count; passes of 8).
- * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (k not a multiple of 64 / 256, k too large). */
+ *   k    : multiple of 32 (of 256 for CB3), at most 32768.  ncols >= 1 (any count; passes
+ *          of 8).
+ * Errors: QMM_EINVAL (k not a multiple of 32 / 256, no rows or columns), QMM_EALIGN,
+ *         QMM_EUNSUPPORTED (k above 32768, a buffer of 4 GiB or more). */
 int qgemv_dense(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
                 const void* xq, int ncols, float* y, int64_t ldy, void* stream);
 
@@ -155,17 +156,22 @@ size_t qgemm_prefill_experts_workspace(int nexperts, int64_t inter, int64_t nent
  * expert].  For expert e, entries p in [expert_off[e], expert_off[e+1]), token t = sorted_tok[p]:
  *   G = X16[t] . Wg16[e]^T,  U = X16[t] . Wu16[e]^T     (FP16 products, FP32 sums; Wg16/Wu16 are
  *                                                        the qmm_dequant_f16 values)
- *   H16 = fp16(silu(G) * U)                              (workspace)
- *   y[p*hidden + j] = (H16 . Wd16[e]^T)[j]               (FP32, one row per sorted entry)
+ *   H16 = fp16(silu(G) * U)                              (workspace; silu in binary32 with the
+ *                                                        device expf, error <= 1 ulp)
+ *   y[p*hidden + j] = (H16 . Wd16[e]^T)[j]               (FP32, one row per sorted entry;
+ *                                                        y 16-byte aligned)
  *   x_f16      : binary16 [ntok][hidden], 16-byte aligned.
- *   sorted_tok : int32 [nentries] (each in [0, ntok)); expert_off: int32 [nexperts+1],
- *                non-decreasing, expert_off[nexperts] == nentries.
+ *   sorted_tok : int32 [nentries]; a token outside [0, ntok) reads zeros.  expert_off: int32
+ *                [nexperts+1], non-decreasing, expert_off[nexperts] == nentries (offsets are
+ *                clamped to [0, nentries]; rows of no expert are not written).
  *   w_gate, w_up (format wtype_gu, inter rows of width hidden) and w_down (wtype_down, hidden
- *   rows of width inter) at e * stride; 4-byte aligned.
+ *   rows of width inter) at e * stride; Q8_0 or IQ4_NL (CB3: QMM_EUNSUPPORTED); 4-byte
+ *   aligned, strides multiples of 4.
  *   ws : qgemm_prefill_experts_workspace() bytes, 16-byte aligned.  Layout: H16 [nentries][inter]
  *        binary16 first, then the tile schedule; with QMM_FLAG_DEBUG_INTERMEDIATES then G, U
  *        float [nentries][inter].
- *   hidden, inter: multiples of 256.
+ *   hidden, inter: multiples of 64, at most 32768; ntok * hidden * 2, nentries * inter * 2 and
+ *   each expert matrix below 4 GiB.
  * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_ESPACE. */
 int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const void* w_up,
                           int64_t gu_expert_stride, int wtype_down, const void* w_down,

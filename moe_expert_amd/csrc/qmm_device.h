@@ -126,6 +126,41 @@ __device__ __forceinline__ void iq4nl_decode_word(uint32_t q, uint32_t& lo, uint
     hi = iq4nl_lookup((q >> 4) & k.m7, ((q >> 5) & k.m4) | k.c0123);
 }
 
+// ------------------------------------------------------------------ FP16 dequantization
+//
+// Integer factors q in [-128, 127] held as biased bytes u = q + 128 (q ^ 0x80).  Placing u under
+// the exponent byte 0x64 forms the binary16 value 1024 + u exactly; subtracting 1152 (exact, all
+// integers below 2048) gives q; one binary16 multiply by the block scale d rounds the exact
+// product d*q once to nearest even (fp16 denormals kept).  Two values per packed instruction.
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Biased level table of IQ4_NL (byte i of word j = level 4j+i + 128).
+constexpr uint32_t kvu_word(int j) { return kv_word(j) ^ 0x80808080u; }
+
+// Four biased bytes -> four binary16 values d*q (two dwords, value order kept).
+__device__ __forceinline__ void u8x4_to_f16(uint32_t u, half2_t dd, uint32_t& lo, uint32_t& hi) {
+    const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t a = perm(0x64646464u, u, 0x04010400u);  // [u0, 0x64, u1, 0x64]
+    const uint32_t b = perm(0x64646464u, u, 0x04030402u);  // [u2, 0x64, u3, 0x64]
+    const half2_t qa = __builtin_bit_cast(half2_t, a) + bias;
+    const half2_t qb = __builtin_bit_cast(half2_t, b) + bias;
+    lo = __builtin_bit_cast(uint32_t, qa * dd);
+    hi = __builtin_bit_cast(uint32_t, qb * dd);
+}
+
+__device__ __forceinline__ half2_t splat_h2(uint32_t dbits) {
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(dbits & 0xFFFFu));
+    return half2_t{d, d};
+}
+
+// IQ4_NL: four 4-bit indices (as for iq4nl_lookup) -> four biased levels.
+__device__ __forceinline__ uint32_t iq4nl_lookup_u(uint32_t i7, uint32_t i8) {
+    const uint32_t lo = perm(kvu_word(1), kvu_word(0), i7);
+    const uint32_t hi = perm(kvu_word(3), kvu_word(2), i7);
+    return perm(hi, lo, i8);
+}
+
 // ------------------------------------------------------------------ weight units
 //
 // A "unit" is one 32-value block of a row: what one lane loads and decodes in one step.  It is

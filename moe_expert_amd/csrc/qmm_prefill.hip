@@ -1,32 +1,48 @@
-// qmm_prefill.hip -- prefill grouped expert GEMM for gfx950: weights dequantized to FP16 in LDS,
-// fp16 MFMA with fp32 sums, SwiGLU epilogue, down GEMM.
+// qmm_prefill.hip -- prefill grouped expert GEMM for gfx950: quantized expert weights converted
+// to FP16 in registers, fp16 MFMA with fp32 sums, SwiGLU epilogue, down GEMM.
 //
-// Method [PF, Summary: each K chunk of an expert's weight rows is dequantized into shared memory
-// and fed to FP16 matrix math over the rows sorted per expert; the FP16 weights are the
-// standalone dequantizer's, in the same k order; an expert's last partial tile is masked]:
-//   schedule kernel : expert_off -> a list of (expert, first row, rows) tiles of <= 128 sorted rows
-//   gate/up kernel  : tile x 64 intermediate columns: G, U = X16[tok] . W16^T for the gate and up
-//                     rows of those columns (128 B rows), K in steps of 32; epilogue
-//                     H16 = fp16(silu(G) * U)
-//   down kernel     : tile x 128 output columns: Y = H16 . Wd16^T
-// Every K step: the 128 x 32 activation chunk is copied and the 128 weight blocks dequantized
-// into LDS in the MFMA fragment order (lane l of a fragment holds row l % 32, k 8*(l/32)..+7),
-// then each of the 4 waves runs v_mfma_f32_32x32x16_f16 on its 32 rows x 128 columns.  The
-// next step's global loads are issued before the MFMAs so their latency hides behind them.
-// Dequantized values: the integer factor times the fp16 scale (times the CB3 multiplier) is
-// exact in binary32, one v_cvt_f16_f32 rounds it to nearest even: the same bits as
-// qmm_dequant_f16.
+// Method [PF, Summary: the weights of an expert are dequantized to FP16 chunk by chunk and fed
+// to FP16 matrix math over the token rows sorted per expert; the FP16 weights are the standalone
+// dequantizer's; an expert's partial last tile is masked]:
+//   schedule kernel : expert_off -> (expert, first row, rows) tiles; an expert's rows are split
+//                     into ceil(n/256) tiles of equal size rounded up to 32 rows
+//   gate/up kernel  : tile x 128 intermediate columns: G, U = X16[tok] . W16^T for the gate and
+//                     up rows of those columns; epilogue H16 = fp16(silu(G) * U)
+//   down kernel     : tile x 256 output columns: Y = H16 . Wd16^T
+//
+// Workgroup: 8 waves, two per SIMD, so one wave's conversion work, loads and waits run while
+// the other's MFMAs occupy the matrix unit.  Wave w owns 32 weight rows (one 32-column MFMA
+// block) and every row of the tile (up to 8 blocks of 32 rows, 128 accumulator registers); it
+// converts only its own weights, straight into the B operand of v_mfma_f32_32x32x16_f16, one
+// k16 fragment ahead of its use.  Only the activations are shared, through LDS.  K advances 64
+// values (two quantized blocks) per step:
+//   - activations: 256 rows x 64 fp16 (32 KiB) per step in four LDS stages (128 KiB), loaded
+//     straight into LDS (buffer_load ... lds) three steps ahead, in a row-major layout whose
+//     16-byte chunks are XOR-swizzled by the row (no bank conflicts for the fragment reads);
+//     fragment reads run one k16 slice ahead, across step boundaries; one barrier per step;
+//   - weights: each lane's raw bytes for step s + 3 are loaded during the last slice of step s
+//     into the registers step s has finished with (three sets).
+// Lane l of a 32x32x16 fragment holds row (or column) l % 32 and k = 8 (l / 32) + 0..7; the
+// accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+// Weight values: the integer factor as an exact binary16 integer times the binary16 scale in
+// one packed multiply, i.e. the exact product rounded once to nearest even (qmm_dequant_f16
+// uses the same conversion).
 #include "qmm_gemv.h"
+
+#include <algorithm>
 
 namespace qmm {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPfBM = 128;      // rows per tile
-constexpr int kPfThreads = 256; // 4 waves, 32 rows each
-constexpr int kPfBK = 32;       // k per step (one 32-value block per weight row)
-constexpr int kPfBNRows = 128;  // weight rows per tile (gate 64 + up 64, or 128 down rows)
+constexpr int kPfRows = 256;                      // rows per tile (8 MFMA blocks of 32)
+constexpr int kPfThreads = 512;                   // 8 waves
+constexpr int kPfStepK = 64;                      // k per step: two 32-value blocks
+constexpr int kPfStage = kPfRows * kPfStepK * 2;  // LDS bytes of one activation stage
+constexpr int kPfGuCols = 128;                    // intermediate columns per gate/up workgroup
+constexpr int kPfDownCols = 256;                  // output columns per down workgroup
 
 struct Tile {
     int e, row0, nrows;
@@ -49,7 +65,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
             o0 = o0 < 0 ? 0 : (o0 > nentries ? nentries : o0);
             o1 = o1 < o0 ? o0 : (o1 > nentries ? nentries : o1);
         }
-        const int n = (o1 - o0 + kPfBM - 1) / kPfBM;
+        const int rows = o1 - o0;
+        int per = 0, n = 0;
+        if (rows > 0) {
+            const int t = (rows + kPfRows - 1) / kPfRows;
+            per = ((rows + t - 1) / t + 31) & ~31;  // <= 256, >= rows / t
+            n = (rows + per - 1) / per;             // <= t
+        }
         scan[threadIdx.x] = n;
         __syncthreads();
         for (int s = 1; s < 1024; s <<= 1) {  // inclusive scan
@@ -63,8 +85,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
             const int t = first + i;
             if (t < max_tiles) {
                 tiles[1 + 3 * t] = e;
-                tiles[2 + 3 * t] = o0 + i * kPfBM;
-                tiles[3 + 3 * t] = (o1 - o0 - i * kPfBM) < kPfBM ? (o1 - o0 - i * kPfBM) : kPfBM;
+                tiles[2 + 3 * t] = o0 + i * per;
+                tiles[3 + 3 * t] = rows - i * per < per ? rows - i * per : per;
             }
         }
         __syncthreads();
@@ -74,279 +96,442 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     if (threadIdx.x == 0) tiles[0] = base < max_tiles ? base : max_tiles;
 }
 
-// ---------------------------------------------------------------- dequant of 16 values
-
-// Raw bytes a thread needs for values [16h, 16h+16) of block kb of a weight row.
-template <int WT>
-struct DqRaw;
-
-template <>
-struct DqRaw<kQ8_0> {
-    uint32_t w[5];
-    uint32_t d;
-    __device__ __forceinline__ void load(rsrc_t r, uint32_t row_off, int kb, int h, int) {
-        const uint32_t blk = row_off + (uint32_t)kb * 34u;
-        const uint32_t o = blk + 2u + 16u * h;
-        const u32x4 x = ld128(r, o & ~3u);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-        w[4] = ld32(r, (o & ~3u) + 16u);
-        d = ld16(r, blk);
-    }
-    // int8 factors (4 dwords) and the binary32 multiplier of the integer factor
-    __device__ __forceinline__ void decode(uint32_t row_off, int kb, int h, const uint32_t*, uint32_t* q, float& dm) const {
-        const uint32_t sh = (row_off + (uint32_t)kb * 34u + 2u + 16u * h) & 3u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = align8(w[i + 1], w[i], sh);
-        dm = h2f(d);
-    }
-};
-
-template <>
-struct DqRaw<kIQ4_NL> {
-    uint32_t w[5];
-    __device__ __forceinline__ void load(rsrc_t r, uint32_t row_off, int kb, int, int) {
-        Unit<kIQ4_NL>::load(r, row_off + (uint32_t)kb * 18u, w);
-    }
-    __device__ __forceinline__ void decode(uint32_t row_off, int kb, int h, const uint32_t*, uint32_t* q, float& dm) const {
-        const uint32_t off = row_off + (uint32_t)kb * 18u;
-        const uint32_t sel = realign_sel(off);
-        const IQ4Consts k;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t x = perm(w[i + 1], w[i], sel) >> (4 * h);  // low or high nibbles
-            q[i] = iq4nl_lookup(x & k.m7, ((x >> 1) & k.m4) | k.c0123);
-        }
-        dm = h2f(realign_scale(w[0], off));
-    }
-};
-
-template <>
-struct DqRaw<kCB3> {
-    uint32_t w[Unit<kCB3>::RAW];
-    __device__ __forceinline__ void load(rsrc_t r, uint32_t row_off, int kb, int, int) {
-        Unit<kCB3>::load(r, row_off + (uint32_t)(kb >> 3) * kCB3Bytes, kb & 7, w);
-    }
-    __device__ __forceinline__ void decode(uint32_t row_off, int kb, int h, const uint32_t* grid, uint32_t* q,
-                                           float& dm) const {
-        uint32_t W[8], dw;
-        int mult;
-        Unit<kCB3>::decode(w, row_off + (uint32_t)(kb >> 3) * kCB3Bytes, kb & 7, grid, W, dw, mult);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = W[4 * h + i];
-        dm = h2f(dw) * (float)mult;  // exact: 11 + 5 significant bits
-    }
-};
-
-// 4 dwords of int8 factors times dm -> 16 binary16 values (8 dwords).  (float)(q + 128) is exact,
-// fma(dm, u, -128 dm) = dm * q exactly (at most 24 significant bits), one RNE to binary16.
-__device__ __forceinline__ void to_f16x16(const uint32_t* q, float dm, uint32_t* out) {
-    const float nb = -128.0f * dm;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t u = q[i] ^ 0x80808080u;
-        uint32_t h[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float v = __builtin_fmaf(dm, (float)((u >> (8 * b)) & 0xFFu), nb);
-            h[b] = f2h(opaque(v));
-        }
-        out[2 * i] = h[0] | (h[1] << 16);
-        out[2 * i + 1] = h[2] | (h[3] << 16);
-    }
-}
-
-// LDS fragment offset (in 16-byte units) of (row-or-column block `blk`, k half `kh`, lane).
-__device__ __forceinline__ int frag16(int blk, int kh, int lane) { return (blk * 2 + kh) * 64 + lane; }
-
-// ---------------------------------------------------------------- the GEMM core
-
-// A chunk loader: the 128 x 32 fp16 chunk of step ks; thread t owns rows t/4 and t/4 + 64,
-// 8-value chunk t % 4 of each.
-struct AChunk {
-    u32x4 v[2];
-    __device__ __forceinline__ void load(rsrc_t ar, const uint32_t* row_byte_off, int ks) {
-        const uint32_t koff = (uint32_t)ks * (kPfBK * 2) + (threadIdx.x & 3u) * 16u;
-        v[0] = ld128(ar, row_byte_off[0] + koff);
-        v[1] = ld128(ar, row_byte_off[1] + koff);
-    }
-    __device__ __forceinline__ void store(u32x4* lds_a) const {
-        const int c = threadIdx.x & 3;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int r = (int)(threadIdx.x >> 2) + 64 * s;
-            lds_a[frag16(r >> 5, c >> 1, (r & 31) + 32 * (c & 1))] = v[s];
-        }
-    }
-};
-
-// B chunk: 128 weight rows x 32 values; thread t owns weight row t/2, values 16(t%2)..+15.
-template <int WT>
-struct BChunk {
-    DqRaw<WT> raw;
-    __device__ __forceinline__ void load(rsrc_t wr, uint32_t row_off, int ks) {
-        raw.load(wr, row_off, ks, (int)(threadIdx.x & 1u), 0);
-    }
-    __device__ __forceinline__ void store(uint32_t row_off, int ks, const uint32_t* grid, u32x4* lds_b) const {
-        const int h = threadIdx.x & 1;
-        const int jr = threadIdx.x >> 1;
-        uint32_t q[4], f[8];
-        float dm;
-        raw.decode(row_off, ks, h, grid, q, dm);
-        to_f16x16(q, dm, f);
-        const int cb = jr >> 5, j = jr & 31;
-        lds_b[frag16(cb, h, j)] = u32x4{f[0], f[1], f[2], f[3]};
-        lds_b[frag16(cb, h, j + 32)] = u32x4{f[4], f[5], f[6], f[7]};
-    }
-};
-
-// Runs the K loop of one tile: acc[cb] (cb = 0..3, 32 columns each) of this wave's 32 rows.
-template <int WT>
-__device__ __forceinline__ void gemm_tile(rsrc_t ar, const uint32_t* a_row_off, rsrc_t wr, uint32_t b_row_off, int nk,
-                                          const uint32_t* grid, u32x4* lds_a, u32x4* lds_b, f32x16 (&acc)[4]) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
-    AChunk a;
-    BChunk<WT> b;
-    a.load(ar, a_row_off, 0);
-    b.load(wr, b_row_off, 0);
-    for (int ks = 0; ks < nk; ++ks) {
-        a.store(lds_a);
-        b.store(b_row_off, ks, grid, lds_b);
-        __syncthreads();
-        if (ks + 1 < nk) {
-            a.load(ar, a_row_off, ks + 1);
-            b.load(wr, b_row_off, ks + 1);
-        }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const half8 av = __builtin_bit_cast(half8, lds_a[frag16(w, kh, lane)]);
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const half8 bv = __builtin_bit_cast(half8, lds_b[frag16(cb, kh, lane)]);
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[cb], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-__device__ __forceinline__ bool load_tile(const int32_t* tiles, Tile& t) {
+// Workgroup -> (tile, column tile).  Workgroups are handed to the 8 XCDs round robin; XCD c
+// takes a contiguous run of tiles (mostly of one expert) and all column tiles of each, so an
+// activation tile and an expert's weight slices are reused from that XCD's L2.
+__device__ __forceinline__ bool pf_tile(const int32_t* tiles, int ny, Tile& t, int& y) {
     const int n = __builtin_amdgcn_readfirstlane(tiles[0]);
-    if ((int)blockIdx.x >= n) return false;
-    t.e = __builtin_amdgcn_readfirstlane(tiles[1 + 3 * blockIdx.x]);
-    t.row0 = __builtin_amdgcn_readfirstlane(tiles[2 + 3 * blockIdx.x]);
-    t.nrows = __builtin_amdgcn_readfirstlane(tiles[3 + 3 * blockIdx.x]);
+    const int per_xcd = (n + 7) >> 3;
+    const int c = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
+    const int xi = q / ny;
+    y = q - xi * ny;
+    const int x = c * per_xcd + xi;
+    if (xi >= per_xcd || x >= n) return false;
+    t.e = __builtin_amdgcn_readfirstlane(tiles[1 + 3 * x]);
+    t.row0 = __builtin_amdgcn_readfirstlane(tiles[2 + 3 * x]);
+    t.nrows = __builtin_amdgcn_readfirstlane(tiles[3 + 3 * x]);
     return true;
 }
 
-// Row (within the tile) and column (within the 32-column block) of accumulator register r.
-__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+// ---------------------------------------------------------------- weights -> B fragments
+//
+// A lane's weight row contributes, per step, the values 8 h .. 8 h + 7 (fragment j = 2 bi) and
+// 16 + 8 h .. + 7 (fragment j = 2 bi + 1) of its two quantized blocks bi = 0, 1, h = lane / 32.
+// load(bi) fetches the raw bytes of one block; convert(j, i) produces the 4 values 4 i .. 4 i + 3
+// of fragment j as two binary16 pairs (dwords 2 i, 2 i + 1 of the fragment).
 
 template <int WT>
-__global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
-    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
-    int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint16_t* __restrict__ x16,
-    uint32_t xbytes, int ntok, const int32_t* __restrict__ sorted_tok, const int32_t* __restrict__ tiles,
-    uint16_t* __restrict__ h16, float* __restrict__ dbg_g, float* __restrict__ dbg_u) {
-    __shared__ u32x4 lds_a[kPfBM * kPfBK * 2 / 16];
-    __shared__ u32x4 lds_b[kPfBNRows * kPfBK * 2 / 16];
-    __shared__ uint32_t lds_grid[WT == kCB3 ? 512 : 1];
-    Tile t;
-    if (!load_tile(tiles, t) || t.e < 0 || t.e >= nexperts) return;
-    if constexpr (WT == kCB3) {
-        stage_grid(grid, lds_grid);
-        __syncthreads();
-    }
-    // this thread's two activation rows (token gather; rows past the tile read zeros)
-    uint32_t a_off[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int r = (int)(threadIdx.x >> 2) + 64 * s;
-        int tok = r < t.nrows ? sorted_tok[t.row0 + r] : -1;
-        a_off[s] = (tok >= 0 && tok < ntok) ? (uint32_t)tok * (uint32_t)hidden * 2u : xbytes;
-    }
-    // this thread's weight row: gate rows 0..63, up rows 64..127 of the tile
-    const int jr = threadIdx.x >> 1;
-    const int col = blockIdx.y * 64 + (jr & 63);
-    const uint8_t* wbase = (jr < 64 ? wg : wu) + t.e * gu_stride;
-    const rsrc_t wr = make_rsrc_dw(wbase, expert_bytes);
-    const uint32_t b_row_off = (uint32_t)col * (uint32_t)row_bytes_dev<WT>(hidden);
-    f32x16 acc[4];
-    gemm_tile<WT>(make_rsrc(x16, xbytes), a_off, wr, b_row_off, hidden / kPfBK, lds_grid, lds_a, lds_b, acc);
+struct BRow;
 
-    // epilogue: acc[0..1] gate, acc[2..3] up for columns 64 y + 32 cb + lane % 32
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+// Q8_0: 34-byte blocks (fp16 d, 32 int8).  The lane reads the two 12-byte windows around its
+// 8-byte runs and the scale.
+template <>
+struct BRow<kQ8_0> {
+    static constexpr uint32_t kBytes = 34;
+    u32x3 a[2], b[2];
+    uint32_t d[2];
+    __device__ __forceinline__ void load(int bi, rsrc_t r, uint32_t row, int blk0, uint32_t h8) {
+        const uint32_t off = row + (uint32_t)(blk0 + bi) * kBytes;
+        const uint32_t w = ((off + 2u) & ~3u) + h8;
+        a[bi] = ld96(r, w);
+        b[bi] = ld96(r, w + 16u);
+        d[bi] = ld16(r, off);
+    }
+    __device__ __forceinline__ void convert(int j, int i, uint32_t row, int blk0, const IQ4Consts&, u32x4& f) const {
+        const int bi = j >> 1;
+        const uint32_t sh = (row + (uint32_t)(blk0 + bi) * kBytes + 2u) & 3u;
+        const u32x3 x = (j & 1) ? b[bi] : a[bi];
+        const uint32_t q = i ? align8(x.z, x.y, sh) : align8(x.y, x.x, sh);
+        uint32_t lo, hi;
+        u8x4_to_f16(q ^ 0x80808080u, splat_h2(d[bi]), lo, hi);
+        if (i) { f.z = lo; f.w = hi; } else { f.x = lo; f.y = hi; }
+    }
+};
+
+// IQ4_NL: 18-byte blocks (fp16 d, 16 bytes of indices; value i < 16 in the low nibble of byte
+// i, value 16 + i in its high nibble).  The lane reads the 12-byte window around index bytes
+// 8 h .. 8 h + 7 (its low nibbles feed fragment 2 bi, its high nibbles fragment 2 bi + 1).
+template <>
+struct BRow<kIQ4_NL> {
+    static constexpr uint32_t kBytes = 18;
+    u32x3 a[2];
+    uint32_t d[2];
+    __device__ __forceinline__ void load(int bi, rsrc_t r, uint32_t row, int blk0, uint32_t h8) {
+        const uint32_t off = row + (uint32_t)(blk0 + bi) * kBytes;
+        a[bi] = ld96(r, ((off + 2u) & ~3u) + h8);
+        d[bi] = ld16(r, off);
+    }
+    __device__ __forceinline__ void convert(int j, int i, uint32_t row, int blk0, const IQ4Consts& k, u32x4& f) const {
+        const int bi = j >> 1;
+        const uint32_t sh = (row + (uint32_t)(blk0 + bi) * kBytes + 2u) & 3u;
+        const u32x3 x = a[bi];
+        uint32_t q = i ? align8(x.z, x.y, sh) : align8(x.y, x.x, sh);
+        if (j & 1) q >>= 4;  // high nibbles
+        uint32_t lo, hi;
+        u8x4_to_f16(iq4nl_lookup_u(q & k.m7, ((q >> 1) & k.m4) | k.c0123), splat_h2(d[bi]), lo, hi);
+        if (i) { f.z = lo; f.w = hi; } else { f.x = lo; f.y = hi; }
+    }
+};
+
+// ---------------------------------------------------------------- activations -> LDS
+//
+// Stage layout: row r (0..255) at 128 r bytes, its 16-byte chunk c (k 8c .. 8c + 7) at slot
+// c ^ swz(r), swz(r) = ((r >> 1) & 7) ^ 4 (r & 1).  A fragment read (lanes 0..31: rows r0 + l,
+// one chunk) then puts any 8 consecutive lanes on 8 distinct 16-byte slots of a 128-byte bank
+// window and any 16 consecutive lanes on 16 distinct slots of a 256-byte window.
+// The stages are filled by buffer_load ... lds (16 bytes per lane, lane l's bytes at
+// M0 + 16 l): wave w fills rows 32 w .. 32 w + 31 with 4 loads of 8 rows; lane l of load i
+// moves the chunk that belongs at slot l % 8 of row 32 w + 8 i + l / 8.
+__device__ __forceinline__ uint32_t pf_swz(uint32_t r) { return ((r >> 1) & 7u) ^ ((r & 1u) << 2); }
+
+// Row (within the tile) whose chunk lane t moves with load i.
+__device__ __forceinline__ int pf_arow(int i) { return 32 * (int)(threadIdx.x >> 6) + 8 * i + (int)((threadIdx.x & 63) >> 3); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// ---------------------------------------------------------------- the K loop
+//
+// Step ks reads LDS stage ks % 4: its four k16 slices, then slice 0 of step ks + 1 from the next
+// stage.  In its first slice it starts the loads of step ks + 3's activations into the stage
+// step ks - 1 read; before the barrier that ends it, it waits for step ks + 2's activations
+// (started a step earlier), which slice 3 of step ks + 1 reads first.  During slice j it converts the weight fragment of the next slice;
+// in its last slice it loads step ks + 3's raw weights into the registers step ks has finished
+// with (three register sets, each load two steps ahead of its first use).  One barrier per step
+// orders every wave's stage fills before the reads of the next step and every read of a stage
+// before its refill.  Instruction order is fixed by hand: each M block of a slice is one
+// scheduling region with its MFMA, the next fragment read for that block and a share of the
+// other work.
+template <int WT, int MB>
+struct PfLoop {
+    rsrc_t ar, wr;
+    uint32_t voff[4];  // per load i: activation row offset + swizzled chunk offset
+    uint32_t b_row;
+    uint32_t raddr[4];
+    uint32_t h8, wrow;  // wrow: byte offset of this wave's 32 rows in a stage
+    int last;
+    uint8_t* lds;
+    IQ4Consts kc;
+
+    static constexpr int kBLoads = WT == kQ8_0 ? 6 : 4;  // buffer loads of one BRow step
+    // vmcnt that leaves outstanding only what was issued after step ks + 2's activation loads:
+    // the raw weights of steps ks + 2 and ks + 3 and step ks + 3's activation loads
+    static constexpr int kWait = 2 * kBLoads + 4;
+
+    __device__ __forceinline__ half8 read_a(uint32_t st, int j, int m) const {
+        return __builtin_bit_cast(half8, *(const u32x4*)(lds + st + raddr[j] + 4096 * m));
+    }
+    __device__ __forceinline__ void fill(int i, uint32_t st, uint32_t kbyte) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(lds + st + wrow + 1024 * i), 16, voff[i], kbyte, 0, 0);
+    }
+
+    // one step; Bc: raw weights of this step, Bn: of the next step.  Stage of step ks: ks % 4.
+    __device__ __forceinline__ void step(int ks, BRow<WT>& Bc, const BRow<WT>& Bn, u32x4& Fa, u32x4& Fb,
+                                         half8 (&a0)[MB], half8 (&a1)[MB], f32x16 (&acc)[MB]) const {
+        const int cblk = 2 * min(ks, last);
+        const int nblk = 2 * min(ks + 1, last);
+        const int lblk = 2 * min(ks + 3, last);
+        const uint32_t kbyte = (uint32_t)min(ks + 3, last) * 128u;
+        const uint32_t s_cur = (uint32_t)(ks & 3) * kPfStage;
+        const uint32_t s_next = (uint32_t)((ks + 1) & 3) * kPfStage;
+        const uint32_t s_fill = (uint32_t)((ks + 3) & 3) * kPfStage;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int c = blockIdx.y * 64 + 32 * cb + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            half8 (&cur)[MB] = (j & 1) ? a1 : a0;
+            half8 (&nxt)[MB] = (j & 1) ? a0 : a1;
+            const u32x4& F = (j & 1) ? Fb : Fa;  // fragment j of this step
+            u32x4& Fn = (j & 1) ? Fa : Fb;       // fragment j + 1 (slice 0 of the next step for j = 3)
+            const half8 b = __builtin_bit_cast(half8, F);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * w + acc_row(lane, r);
-            if (row < t.nrows) {
-                const int64_t p = t.row0 + row;
-                const float gv = acc[cb][r], uv = acc[cb + 2][r];
-                const float hv = [&] {
-                    const float e = (float)exp(-(double)gv);
-                    const float den = opaque(1.0f + e);
-                    const float sl = opaque(gv / den);
-                    return opaque(sl * uv);
-                }();
-                h16[p * inter + c] = (uint16_t)f2h(hv);
-                if (dbg_g) {
-                    dbg_g[p * inter + c] = gv;
-                    dbg_u[p * inter + c] = uv;
+            for (int m = 0; m < MB; ++m) {
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[m], b, acc[m], 0, 0, 0);
+                nxt[m] = j < 3 ? read_a(s_cur, j + 1, m) : read_a(s_next, 0, m);
+                if (j == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if ((i * MB) / 4 == m) fill(i, s_fill, kbyte);
                 }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if ((i * MB) / 2 + (MB >= 4 ? 1 : 0) == m) {
+                        if (j < 3) Bc.convert(j + 1, i, b_row, cblk, kc, Fn);
+                        else Bn.convert(0, i, b_row, nblk, kc, Fn);
+                    }
+                if (j == 3) {
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+                        if ((bi * MB) / 2 == m) Bc.load(bi, wr, b_row, lblk, h8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
+        // The barrier: this wave's fragment reads done (lgkmcnt 0) and its fill of step ks + 2's
+        // stage landed (vmcnt kWait; gfx9 s_waitcnt: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+        // 7 = no wait, lgkmcnt [11:8]).  No fence: a workgroup release fence would also wait for
+        // the fill started in this step.  The empty asm statements keep the compiler from moving
+        // memory accesses across.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+};
+
+// acc[m]: rows 32 m .. 32 m + 31 of the tile, this wave's 32 weight rows.  a_off[i]: byte offset
+// of row pf_arow(i) in the activation buffer (past its end for rows beyond the tile, which then
+// read zeros); b_row: byte offset of this lane's weight row in the matrix of resource wr.
+// Steps run in threes so the raw-weight register roles are constants; the last one or two
+// steps run after the loop.
+template <int WT, int MB>
+__device__ __forceinline__ void pf_gemm(rsrc_t ar, const uint32_t (&a_off)[4], rsrc_t wr, uint32_t b_row, int nk,
+                                        uint8_t* lds, f32x16 (&acc)[MB]) {
+    const uint32_t lane = threadIdx.x & 63u;
+    PfLoop<WT, MB> L;
+    L.ar = ar;
+    L.wr = wr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t r = (uint32_t)pf_arow(i);
+        L.voff[i] = a_off[i] + (((lane & 7u) ^ pf_swz(r)) * 16u);
+    }
+    L.b_row = b_row;
+    L.h8 = (lane >> 5) * 8u;
+    L.wrow = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 32u * 128u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.raddr[j] = (lane & 31u) * 128u + ((((uint32_t)(2 * j) + (lane >> 5)) ^ pf_swz(lane & 31u)) * 16u);
+    L.last = nk - 1;
+    L.lds = lds;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+
+    BRow<WT> R0, R1, R2;
+    u32x4 Fa, Fb;
+    half8 a0[MB], a1[MB];
+    // prologue: stages 0, 1, 2 filled, raw weights of steps 0, 1, 2 loaded, fragment 0 of step 0
+    // converted
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.fill(i, s * kPfStage, (uint32_t)min(s, L.last) * 128u);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) R0.load(bi, wr, b_row, 0, L.h8);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) R1.load(bi, wr, b_row, 2 * min(1, L.last), L.h8);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) R2.load(bi, wr, b_row, 2 * min(2, L.last), L.h8);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the stage fills are not tracked
+    R0.convert(0, 0, b_row, 0, L.kc, Fa);
+    R0.convert(0, 1, b_row, 0, L.kc, Fa);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MB; ++m) a0[m] = L.read_a(0, 0, m);
+    int ks = 0;
+    for (; ks + 2 < nk; ks += 3) {
+        L.step(ks, R0, R1, Fa, Fb, a0, a1, acc);
+        L.step(ks + 1, R1, R2, Fa, Fb, a0, a1, acc);
+        L.step(ks + 2, R2, R0, Fa, Fb, a0, a1, acc);
+    }
+    if (ks < nk) L.step(ks, R0, R1, Fa, Fb, a0, a1, acc);
+    if (ks + 1 < nk) L.step(ks + 1, R1, R2, Fa, Fb, a0, a1, acc);
+    // the last steps started (clamped) stage fills: let every wave's land before LDS is reused
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __syncthreads();
+}
+
+// Row (within the 32-row block) of accumulator register r.
+__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// silu(g) * u in binary32 with the library expf (documented maximum error 1 ulp), an IEEE
+// division and a product: within a few ulp of the same expression evaluated exactly.
+__device__ __forceinline__ float silu_mul_f(float g, float u) {
+    const float e = expf(-g);
+    const float den = opaque(1.0f + e);
+    const float sl = opaque(g / den);
+    return opaque(sl * u);
+}
+
+// Byte offsets of this thread's four activation rows pf_arow(i) (gate/up: gathered tokens).
+__device__ __forceinline__ void token_rows(const int32_t* sorted_tok, const Tile& t, int ntok, int hidden,
+                                           uint32_t past_end, uint32_t (&a_off)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = pf_arow(i);
+        const int tok = r < t.nrows ? sorted_tok[t.row0 + r] : -1;
+        a_off[i] = (tok >= 0 && tok < ntok) ? (uint32_t)tok * (uint32_t)hidden * 2u : past_end;
+    }
+}
+
+// ---------------------------------------------------------------- gate/up
+
+struct GuArgs {
+    const uint8_t* wg;
+    const uint8_t* wu;
+    int64_t stride;
+    uint32_t expert_bytes;
+    int nexperts, hidden, inter, ntok;
+    const uint16_t* x16;
+    uint32_t xbytes;
+    const int32_t* sorted_tok;
+    const int32_t* tiles;
+    uint16_t* h16;
+    float* dbg_g;
+    float* dbg_u;
+};
+
+// The accumulators of rows 64 q .. 64 q + 63 (blocks 2q, 2q+1) go to an LDS tile of 64 rows x
+// 256 fp32 columns (row stride 264 floats: the two row groups of one register write land on
+// disjoint banks); the caller's loop then reads it back row-wise.
+constexpr int kPfEpiLd = 264;
+
+template <int MB>
+__device__ __forceinline__ void epi_put(const f32x16 (&acc)[MB], int q, float* tile) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        const int m = 2 * q + mm;
+        if (m < MB) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tile[(32 * mm + acc_row(lane, r)) * kPfEpiLd + 32 * w + (lane & 31)] = acc[m][r];
         }
     }
 }
 
-template <int WT>
-__global__ __launch_bounds__(kPfThreads) void pf_down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
-                                                             uint32_t expert_bytes, int nexperts,
-                                                             const uint8_t* __restrict__ grid, int hidden, int inter,
-                                                             const uint16_t* __restrict__ h16, uint32_t hbytes,
-                                                             const int32_t* __restrict__ tiles, float* __restrict__ y) {
-    __shared__ u32x4 lds_a[kPfBM * kPfBK * 2 / 16];
-    __shared__ u32x4 lds_b[kPfBNRows * kPfBK * 2 / 16];
-    __shared__ uint32_t lds_grid[WT == kCB3 ? 512 : 1];
-    Tile t;
-    if (!load_tile(tiles, t) || t.e < 0 || t.e >= nexperts) return;
-    if constexpr (WT == kCB3) {
-        stage_grid(grid, lds_grid);
+// Waves 0..3 multiply by the gate rows of intermediate columns y*128 + 32 w + 0..31, waves 4..7
+// by the up rows of the same columns.  Epilogue per 64-row quarter: G (tile columns 0..127) and
+// U (128..255) through LDS, then each thread forms 8 consecutive H16 values of a row
+// (H16 = fp16(silu(G) U)) and writes them with one 16-byte store.
+template <int WT, int MB>
+__device__ __forceinline__ void gateup_tile(const GuArgs& p, const Tile& t, int y, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t a_off[4];
+    token_rows(p.sorted_tok, t, p.ntok, p.hidden, p.xbytes, a_off);
+    const int col = y * kPfGuCols + 32 * (w & 3) + (lane & 31);
+    const uint32_t roff = (uint32_t)(col < p.inter ? col : p.inter - 1) * (uint32_t)row_bytes_dev<WT>(p.hidden);
+    const rsrc_t wr = make_rsrc_dw((w >= 4 ? p.wu : p.wg) + (int64_t)t.e * p.stride, p.expert_bytes);
+    f32x16 acc[MB];
+    pf_gemm<WT, MB>(make_rsrc(p.x16, p.xbytes), a_off, wr, roff, p.hidden / kPfStepK, lds, acc);
+
+    float* tile = (float*)lds;
+    const int c8 = (int)(threadIdx.x & 15) * 8;  // 8 columns of the 128
+    const int c0 = y * kPfGuCols + c8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (2 * q >= MB) break;
+        epi_put<MB>(acc, q, tile);
+        __syncthreads();
+#pragma unroll 1
+        for (int rr = (int)(threadIdx.x >> 4); rr < 64; rr += kPfThreads / 16) {
+            const int row = 64 * q + rr;
+            if (row >= t.nrows || c0 >= p.inter) continue;
+            const float* tr = tile + rr * kPfEpiLd;
+            const f32x4 g0 = *(const f32x4*)(tr + c8), g1 = *(const f32x4*)(tr + c8 + 4);
+            const f32x4 u0 = *(const f32x4*)(tr + 128 + c8), u1 = *(const f32x4*)(tr + 128 + c8 + 4);
+            uint32_t h[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[i] = f2h(silu_mul_f(g0[i], u0[i]));
+                h[i + 4] = f2h(silu_mul_f(g1[i], u1[i]));
+            }
+            const int64_t o = (int64_t)(t.row0 + row) * p.inter + c0;
+            *(u32x4*)(p.h16 + o) = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            if (p.dbg_g) {
+                *(f32x4*)(p.dbg_g + o) = g0;
+                *(f32x4*)(p.dbg_g + o + 4) = g1;
+                *(f32x4*)(p.dbg_u + o) = u0;
+                *(f32x4*)(p.dbg_u + o + 4) = u1;
+            }
+        }
         __syncthreads();
     }
-    uint32_t a_off[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int r = (int)(threadIdx.x >> 2) + 64 * s;
-        a_off[s] = r < t.nrows ? (uint32_t)(t.row0 + r) * (uint32_t)inter * 2u : hbytes;
-    }
-    const int jr = threadIdx.x >> 1;
-    const int col = blockIdx.y * 128 + jr;
-    const rsrc_t wr = make_rsrc_dw(wd + t.e * d_stride, expert_bytes);
-    const uint32_t b_row_off = (uint32_t)(col < hidden ? col : hidden - 1) * (uint32_t)row_bytes_dev<WT>(inter);
-    f32x16 acc[4];
-    gemm_tile<WT>(make_rsrc(h16, hbytes), a_off, wr, b_row_off, inter / kPfBK, lds_grid, lds_a, lds_b, acc);
+}
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+template <int WT>
+__global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(GuArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kPfStage];
+    Tile t;
+    int y;
+    if (!pf_tile(p.tiles, (p.inter + kPfGuCols - 1) / kPfGuCols, t, y) || t.e < 0 || t.e >= p.nexperts) return;
+    switch ((t.nrows + 31) >> 5) {
+        case 1: gateup_tile<WT, 1>(p, t, y, lds); break;
+        case 2: gateup_tile<WT, 2>(p, t, y, lds); break;
+        case 3: gateup_tile<WT, 3>(p, t, y, lds); break;
+        case 4: gateup_tile<WT, 4>(p, t, y, lds); break;
+        case 5: gateup_tile<WT, 5>(p, t, y, lds); break;
+        case 6: gateup_tile<WT, 6>(p, t, y, lds); break;
+        case 7: gateup_tile<WT, 7>(p, t, y, lds); break;
+        case 8: gateup_tile<WT, 8>(p, t, y, lds); break;
+        default: break;
+    }
+}
+
+// ---------------------------------------------------------------- down
+
+struct DownArgs {
+    const uint8_t* wd;
+    int64_t stride;
+    uint32_t expert_bytes;
+    int nexperts, hidden, inter;
+    const uint16_t* h16;
+    uint32_t hbytes;
+    const int32_t* tiles;
+    float* y;
+};
+
+template <int WT, int MB>
+__device__ __forceinline__ void down_tile(const DownArgs& p, const Tile& t, int y, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t a_off[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int c = blockIdx.y * 128 + 32 * cb + (lane & 31);
+    for (int i = 0; i < 4; ++i) {
+        const int r = pf_arow(i);
+        a_off[i] = r < t.nrows ? (uint32_t)(t.row0 + r) * (uint32_t)p.inter * 2u : p.hbytes;
+    }
+    // output column y*256 + 32 w + lane % 32
+    const int col = y * kPfDownCols + 32 * w + (lane & 31);
+    const uint32_t roff = (uint32_t)(col < p.hidden ? col : p.hidden - 1) * (uint32_t)row_bytes_dev<WT>(p.inter);
+    f32x16 acc[MB];
+    pf_gemm<WT, MB>(make_rsrc(p.h16, p.hbytes), a_off, make_rsrc_dw(p.wd + (int64_t)t.e * p.stride, p.expert_bytes),
+                    roff, p.inter / kPfStepK, lds, acc);
+
+    // per 64-row quarter through LDS; each thread stores 4 consecutive outputs of a row at once
+    float* tile = (float*)lds;
+    const int c4 = (int)(threadIdx.x & 63) * 4;  // 4 columns of the 256
+    const int c0 = y * kPfDownCols + c4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * w + acc_row(lane, r);
-            if (row < t.nrows && c < hidden) y[(int64_t)(t.row0 + row) * hidden + c] = acc[cb][r];
+    for (int q = 0; q < 4; ++q) {
+        if (2 * q >= MB) break;
+        epi_put<MB>(acc, q, tile);
+        __syncthreads();
+#pragma unroll 1
+        for (int rr = (int)(threadIdx.x >> 6); rr < 64; rr += kPfThreads / 64) {
+            const int row = 64 * q + rr;
+            if (row < t.nrows && c0 < p.hidden)
+                *(f32x4*)(p.y + (int64_t)(t.row0 + row) * p.hidden + c0) = *(const f32x4*)(tile + rr * kPfEpiLd + c4);
         }
+        __syncthreads();
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kPfThreads) void pf_down_kernel(DownArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kPfStage];
+    Tile t;
+    int y;
+    if (!pf_tile(p.tiles, (p.hidden + kPfDownCols - 1) / kPfDownCols, t, y) || t.e < 0 || t.e >= p.nexperts) return;
+    switch ((t.nrows + 31) >> 5) {
+        case 1: down_tile<WT, 1>(p, t, y, lds); break;
+        case 2: down_tile<WT, 2>(p, t, y, lds); break;
+        case 3: down_tile<WT, 3>(p, t, y, lds); break;
+        case 4: down_tile<WT, 4>(p, t, y, lds); break;
+        case 5: down_tile<WT, 5>(p, t, y, lds); break;
+        case 6: down_tile<WT, 6>(p, t, y, lds); break;
+        case 7: down_tile<WT, 7>(p, t, y, lds); break;
+        case 8: down_tile<WT, 8>(p, t, y, lds); break;
+        default: break;
     }
 }
 
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
-static int64_t max_tiles_of(int nexperts, int64_t nentries) { return (nentries + kPfBM - 1) / kPfBM + nexperts; }
+static int64_t max_tiles_of(int nexperts, int64_t nentries) { return (nentries + kPfRows - 1) / kPfRows + nexperts; }
 
 struct PfLayout {
     size_t h_off, tiles_off, g_off, u_off, total;
@@ -384,16 +569,17 @@ extern "C" int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const voi
     if (nexperts < 1 || hidden < 32 || inter < 32 || ntok < 1 || nentries < 0) return QMM_EINVAL;
     if (qmm_row_bytes(wtype_gu, hidden) == 0 || qmm_row_bytes(wtype_down, inter) == 0) return QMM_EINVAL;
     if (wtype_gu == QMM_CB3 || wtype_down == QMM_CB3) return QMM_EUNSUPPORTED;  // no codebook argument here
-    if (hidden % 128 || inter % 64) return QMM_EUNSUPPORTED;
+    if (hidden % kPfStepK || inter % kPfStepK) return QMM_EUNSUPPORTED;
     const int64_t gu_bytes = inter * qmm_row_bytes(wtype_gu, hidden);
     const int64_t d_bytes = hidden * qmm_row_bytes(wtype_down, inter);
     if (gu_expert_stride < gu_bytes || down_expert_stride < d_bytes) return QMM_EINVAL;
     if (gu_expert_stride % 4 || down_expert_stride % 4) return QMM_EALIGN;
-    if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(x_f16, 16) || !aligned(y, 4) ||
+    if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(x_f16, 16) || !aligned(y, 16) ||
         !aligned(ws, 16))
         return QMM_EALIGN;
     if ((uint64_t)ntok * hidden * 2 > kMaxBufferBytes || (uint64_t)nentries * inter * 2 > kMaxBufferBytes ||
-        gu_bytes > (int64_t)kMaxBufferBytes || d_bytes > (int64_t)kMaxBufferBytes || nentries > 0x7FFFFFFF)
+        gu_bytes > (int64_t)kMaxBufferBytes || d_bytes > (int64_t)kMaxBufferBytes || nentries > 0x7FFFFFFF ||
+        hidden > kMaxK || inter > kMaxK)
         return QMM_EUNSUPPORTED;
     const PfLayout lay = pf_layout(nexperts, inter, nentries, flags);
     if (ws_bytes < lay.total) return QMM_ESPACE;
@@ -402,38 +588,55 @@ extern "C" int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const voi
     uint8_t* wsb = (uint8_t*)ws;
     uint16_t* h16 = (uint16_t*)(wsb + lay.h_off);
     int32_t* tiles = (int32_t*)(wsb + lay.tiles_off);
-    float* dbg_g = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.g_off) : nullptr;
-    float* dbg_u = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.u_off) : nullptr;
     const int64_t max_tiles = max_tiles_of(nexperts, nentries);
-    if (max_tiles > 0x7FFFFFFF) return QMM_EUNSUPPORTED;
+    const int64_t per_xcd = (max_tiles + 7) / 8;
+    const int64_t ny_max = std::max((inter + kPfGuCols - 1) / kPfGuCols, (hidden + kPfDownCols - 1) / kPfDownCols);
+    if (8 * per_xcd * ny_max > 0x7FFFFFFF) return QMM_EUNSUPPORTED;
 
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, expert_off, nexperts, (int)nentries, tiles,
                        (int)max_tiles);
     int rc = launch_status();
     if (rc) return rc;
-    const uint32_t xbytes = (uint32_t)(ntok * hidden * 2);
-    const uint32_t hbytes = (uint32_t)(nentries * inter * 2);
     {
-        const dim3 g((unsigned)max_tiles, (unsigned)(inter / 64));
-        auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, g, dim3(kPfThreads), 0, st, (const uint8_t*)w_gate, (const uint8_t*)w_up,
-                               gu_expert_stride, (uint32_t)gu_bytes, nexperts, (const uint8_t*)nullptr, (int)hidden,
-                               (int)inter, x_f16, xbytes, (int)ntok, sorted_tok, tiles, h16, dbg_g, dbg_u);
-        };
-        if (wtype_gu == QMM_Q8_0) go(pf_gateup_kernel<kQ8_0>);
-        else go(pf_gateup_kernel<kIQ4_NL>);
+        GuArgs a;
+        a.wg = (const uint8_t*)w_gate;
+        a.wu = (const uint8_t*)w_up;
+        a.stride = gu_expert_stride;
+        a.expert_bytes = (uint32_t)gu_bytes;
+        a.nexperts = nexperts;
+        a.hidden = (int)hidden;
+        a.inter = (int)inter;
+        a.ntok = (int)ntok;
+        a.x16 = x_f16;
+        a.xbytes = (uint32_t)(ntok * hidden * 2);
+        a.sorted_tok = sorted_tok;
+        a.tiles = tiles;
+        a.h16 = h16;
+        a.dbg_g = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.g_off) : nullptr;
+        a.dbg_u = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.u_off) : nullptr;
+        const int64_t ny = (inter + kPfGuCols - 1) / kPfGuCols;
+        const dim3 g((unsigned)(8 * per_xcd * ny));
+        if (wtype_gu == QMM_Q8_0) hipLaunchKernelGGL(pf_gateup_kernel<kQ8_0>, g, dim3(kPfThreads), 0, st, a);
+        else hipLaunchKernelGGL(pf_gateup_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
         rc = launch_status();
         if (rc) return rc;
     }
     {
-        const dim3 g((unsigned)max_tiles, (unsigned)(hidden / 128));
-        auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, g, dim3(kPfThreads), 0, st, (const uint8_t*)w_down, down_expert_stride,
-                               (uint32_t)d_bytes, nexperts, (const uint8_t*)nullptr, (int)hidden, (int)inter, h16,
-                               hbytes, tiles, y);
-        };
-        if (wtype_down == QMM_Q8_0) go(pf_down_kernel<kQ8_0>);
-        else go(pf_down_kernel<kIQ4_NL>);
+        DownArgs a;
+        a.wd = (const uint8_t*)w_down;
+        a.stride = down_expert_stride;
+        a.expert_bytes = (uint32_t)d_bytes;
+        a.nexperts = nexperts;
+        a.hidden = (int)hidden;
+        a.inter = (int)inter;
+        a.h16 = h16;
+        a.hbytes = (uint32_t)(nentries * inter * 2);
+        a.tiles = tiles;
+        a.y = y;
+        const int64_t ny = (hidden + kPfDownCols - 1) / kPfDownCols;
+        const dim3 g((unsigned)(8 * per_xcd * ny));
+        if (wtype_down == QMM_Q8_0) hipLaunchKernelGGL(pf_down_kernel<kQ8_0>, g, dim3(kPfThreads), 0, st, a);
+        else hipLaunchKernelGGL(pf_down_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
         return launch_status();
     }
 }

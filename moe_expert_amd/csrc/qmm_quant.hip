@@ -4,9 +4,10 @@
 // d = amax/127 (binary32), q = x/d (binary32 IEEE division) rounded half away from zero,
 // stored d = fp16(d), s = fp16(d * sum q); an all-zero block is all zeros.
 // FP16 dequant [DQ, Change: one thread per 8 outputs and one 16-byte store; every value the
-// exact product rounded once to nearest even]: the integer factor times the fp16 scale is
-// exact in binary32 (at most 11 x 11 significant bits), so one v_cvt_f16_f32 gives the
-// nearest-even binary16 of the exact value.
+// exact product rounded once to nearest even].  Q8_0 / IQ4_NL: the factor, formed exactly as
+// a binary16 integer, times the binary16 scale in one packed binary16 multiply (a single
+// rounding of the exact product); the prefill GEMM converts its weights with the same code.
+// CB3 (factor up to 8 x 31 x 15): the binary32 product is exact, one v_cvt_f16_f32 rounds it.
 #include "qmm_device.h"
 #include "qmm_host.h"
 
@@ -87,10 +88,27 @@ __global__ __launch_bounds__(256) void dequant_f16_kernel(const uint8_t* __restr
         int f[8];
         uint32_t dbits;
         factors8<WT>(w + r * rb, grid, j0, f, &dbits);
-        const float d = h2f(dbits);
         uint32_t h[8];
+        if constexpr (WT == kCB3) {
+            // integer factor times multiplier exceeds a byte: binary32 product (exact), one RNE
+            const float d = h2f(dbits);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = f2h(opaque(d * (float)f[i]));
+            for (int i = 0; i < 8; ++i) h[i] = f2h(opaque(d * (float)f[i]));
+        } else {
+            // the packed binary16 conversion the prefill GEMM uses for its weights
+            const half2_t dd = splat_h2(dbits);
+#pragma unroll
+            for (int i = 0; i < 8; i += 4) {
+                const uint32_t u = (uint32_t)(f[i] + 128) | ((uint32_t)(f[i + 1] + 128) << 8) |
+                                   ((uint32_t)(f[i + 2] + 128) << 16) | ((uint32_t)(f[i + 3] + 128) << 24);
+                uint32_t lo, hi;
+                u8x4_to_f16(u, dd, lo, hi);
+                h[i] = lo & 0xFFFFu;
+                h[i + 1] = lo >> 16;
+                h[i + 2] = hi & 0xFFFFu;
+                h[i + 3] = hi >> 16;
+            }
+        }
         uint16_t* dst = out + r * ld + j0;
         if constexpr (VEC) {
             u32x4 v;

@@ -72,3 +72,57 @@ def test_quantize_and_dequant_reject():
     assert L.qmm_dequant_f16(M.QMM_IQ4_NL, FAKE, None, 4, 64, FAKE, 32, None) == -1
     assert L.qmm_dequant_f16(M.QMM_CB3, FAKE, None, 4, 256, FAKE, 256, None) == -1
     assert L.qmm_dequant_f16(M.QMM_Q8_0, C.c_void_p(0x100001), None, 4, 64, FAKE, 64, None) == -3
+
+
+def _gu_args(**kw):
+    """qgemv_grouped_experts arguments for 4 experts 2560 -> 1024 (IQ4_NL / Q8_0), valid apart
+    from what `kw` changes."""
+    a = dict(wtype_gu=M.QMM_IQ4_NL, w_gate=FAKE, w_up=FAKE, gu_stride=1024 * 1440, wtype_down=M.QMM_Q8_0,
+             w_down=FAKE, d_stride=2560 * 1088, nexperts=4, grid=None, hidden=2560, inter=1024, xq=FAKE,
+             xq_cols=2, ge=FAKE, go=FAKE, ngroups=2, ec=FAKE, nentries=4, y=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, flags=0, stream=None)
+    a.update(kw)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(w_up=None), -1),
+    (dict(wtype_gu=M.QMM_CB3), -1),                            # CB3 without a grid
+    (dict(gu_stride=1024 * 1440 - 4), -1),                     # stride below one matrix
+    (dict(gu_stride=1024 * 1440 + 2), -3),                     # stride not a multiple of 4
+    (dict(hidden=2560 + 16), -1),                              # not a block multiple
+    (dict(inter=65536), -2),                                   # beyond the K limit
+    (dict(ngroups=70000), -2),
+    (dict(ws=ODD), -3),
+    (dict(ws_bytes=16), -5),
+    (dict(ngroups=0), 0),                                      # nothing to do: no launch
+])
+def test_grouped_rejects(kw, expect):
+    assert M.lib().qgemv_grouped_experts(*_gu_args(**kw)) == expect
+
+
+def _pf_args(**kw):
+    """qgemm_prefill_experts arguments for 4 experts 2560 -> 1024 (IQ4_NL / Q8_0), valid apart
+    from what `kw` changes."""
+    a = dict(wtype_gu=M.QMM_IQ4_NL, w_gate=FAKE, w_up=FAKE, gu_stride=1024 * 1440, wtype_down=M.QMM_Q8_0,
+             w_down=FAKE, d_stride=2560 * 1088, nexperts=4, hidden=2560, inter=1024, x=FAKE, ntok=64,
+             st=FAKE, off=FAKE, nentries=128, y=FAKE, ws=FAKE, ws_bytes=1 << 30, flags=0, stream=None)
+    a.update(kw)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(wtype_down=9), -1),
+    (dict(x=None), -1),
+    (dict(wtype_gu=M.QMM_CB3, gu_stride=1024 * 1100), -2),    # no codebook argument
+    (dict(hidden=2560 + 32), -2),                              # K steps of 64
+    (dict(inter=1024 + 32, d_stride=2560 * 1122), -2),
+    (dict(d_stride=2560 * 1088 - 4), -1),
+    (dict(x=C.c_void_p(0x100008)), -3),                        # x_f16 must be 16-byte aligned
+    (dict(ws_bytes=64), -5),
+    (dict(nentries=0, ws_bytes=4096), 0),                      # nothing to do: no launch
+    (dict(ntok=1 << 20), -2),                                  # x_f16 of 4 GiB or more
+])
+def test_prefill_rejects(kw, expect):
+    assert M.lib().qgemm_prefill_experts(*_pf_args(**kw)) == expect
+    assert M.lib().qgemm_prefill_experts_workspace(4, 1024, 128, 0) >= 128 * 1024 * 2
