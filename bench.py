@@ -325,15 +325,21 @@ def bench_prefill(args, torch, M):
                              "kernel": "schedule + pf_gateup_kernel + pf_down_kernel (one call)"}})
     if not args.no_cpu:
         import oracle
-        samples = np.arange(off[0], off[0] + 32, dtype=np.int64)   # 32 rows of expert 0
+        # rows of the first experts, sized from a 32-row trial to about 10 s of CPU work
+        t0 = time.perf_counter()
+        oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off,
+                            np.arange(32, dtype=np.int64))
+        trial = time.perf_counter() - t0
+        nrow = int(min(nent, max(32, 32 * 10.0 / max(trial, 1e-3))))
+        samples = np.arange(nrow, dtype=np.int64)
         t0 = time.perf_counter()
         oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off, samples)
         dt = time.perf_counter() - t0
         per_row = dt / samples.size
         out["cpu_baseline"] = {"value": round(flops / nent / per_row / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.num_threads(), "kind": "oracle",
-                               "sample": f"32 rows of expert 0 (incl. dequantizing its weights), {dt:.2f} s, "
-                                         f"scaled to {nent} rows"}
+                               "sample": f"the first {nrow} sorted rows (experts 0..{int(np.searchsorted(off, nrow, 'right')) - 1}, "
+                                         f"incl. dequantizing their weights), {dt:.1f} s, scaled to {nent} rows"}
     return out
 
 

@@ -20,8 +20,9 @@
 //     straight into LDS (buffer_load ... lds) three steps ahead, in a row-major layout whose
 //     16-byte chunks are XOR-swizzled by the row (no bank conflicts for the fragment reads);
 //     fragment reads run one k16 slice ahead, across step boundaries; one barrier per step;
-//   - weights: each lane's raw bytes for step s + 3 are loaded during the last slice of step s
-//     into the registers step s has finished with (three sets).
+//   - weights: each lane pair reads its row's two blocks of a step once (one block per lane)
+//     and trades halves through v_permlane32_swap; the raw bytes for step s + 3 are loaded
+//     in the last slice of step s, into the registers of step s + 1 (prepared just before).
 // Lane l of a 32x32x16 fragment holds row (or column) l % 32 and k = 8 (l / 32) + 0..7; the
 // accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
 // Weight values: the integer factor as an exact binary16 integer times the binary16 scale in
@@ -117,59 +118,107 @@ __device__ __forceinline__ bool pf_tile(const int32_t* tiles, int ny, Tile& t, i
 //
 // A lane's weight row contributes, per step, the values 8 h .. 8 h + 7 (fragment j = 2 bi) and
 // 16 + 8 h .. + 7 (fragment j = 2 bi + 1) of its two quantized blocks bi = 0, 1, h = lane / 32.
-// load(bi) fetches the raw bytes of one block; convert(j, i) produces the 4 values 4 i .. 4 i + 3
-// of fragment j as two binary16 pairs (dwords 2 i, 2 i + 1 of the fragment).
+// Loading: lane l < 32 reads block 0 of its row whole, lane l + 32 block 1 (adjacent bytes), so
+// a load instruction touches each row's step bytes once; prepare() realigns the block and
+// trades halves with the partner lane through v_permlane32_swap (the low half-wave keeps bytes
+// 0..7 of each 16-byte run, the high half-wave bytes 8..15), giving every lane its bytes of
+// both blocks.  convert(j, i) then produces the 4 values 4 i .. 4 i + 3 of fragment j as two
+// binary16 pairs (dwords 2 i, 2 i + 1 of the fragment).
 
+// permlane32_swap(x, y): lanes 0..31 get {x, x of lane + 32}, lanes 32..63 {y of lane - 32, y}.
+__device__ __forceinline__ void swap32(uint32_t x, uint32_t y, uint32_t& r0, uint32_t& r1) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    r0 = r[0];
+    r1 = r[1];
+}
+
+template <int WT>
+struct BPrep;
 template <int WT>
 struct BRow;
 
-// Q8_0: 34-byte blocks (fp16 d, 32 int8).  The lane reads the two 12-byte windows around its
-// 8-byte runs and the scale.
+// Q8_0: 34-byte blocks (fp16 d, 32 int8); the 9 dwords around a block.
+template <>
+struct BPrep<kQ8_0> {
+    uint32_t x[2][2][2];  // [run][block][dword]: bytes 16 run + 8 h .. + 7 of block bi
+    uint32_t d[2];
+    __device__ __forceinline__ void convert(int j, int i, const IQ4Consts&, u32x4& f) const {
+        const int bi = j >> 1;
+        uint32_t lo, hi;
+        u8x4_to_f16(x[j & 1][bi][i] ^ 0x80808080u, splat_h2(d[bi]), lo, hi);
+        if (i) { f.z = lo; f.w = hi; } else { f.x = lo; f.y = hi; }
+    }
+};
 template <>
 struct BRow<kQ8_0> {
     static constexpr uint32_t kBytes = 34;
-    u32x3 a[2], b[2];
-    uint32_t d[2];
-    __device__ __forceinline__ void load(int bi, rsrc_t r, uint32_t row, int blk0, uint32_t h8) {
-        const uint32_t off = row + (uint32_t)(blk0 + bi) * kBytes;
-        const uint32_t w = ((off + 2u) & ~3u) + h8;
-        a[bi] = ld96(r, w);
-        b[bi] = ld96(r, w + 16u);
-        d[bi] = ld16(r, off);
+    static constexpr int kLoads = 3;
+    u32x4 a, b;
+    uint32_t c;
+    __device__ __forceinline__ static uint32_t off(uint32_t row, int blk0, uint32_t hh) {
+        return row + ((uint32_t)blk0 + hh) * kBytes;
     }
-    __device__ __forceinline__ void convert(int j, int i, uint32_t row, int blk0, const IQ4Consts&, u32x4& f) const {
-        const int bi = j >> 1;
-        const uint32_t sh = (row + (uint32_t)(blk0 + bi) * kBytes + 2u) & 3u;
-        const u32x3 x = (j & 1) ? b[bi] : a[bi];
-        const uint32_t q = i ? align8(x.z, x.y, sh) : align8(x.y, x.x, sh);
-        uint32_t lo, hi;
-        u8x4_to_f16(q ^ 0x80808080u, splat_h2(d[bi]), lo, hi);
-        if (i) { f.z = lo; f.w = hi; } else { f.x = lo; f.y = hi; }
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t row, int blk0, uint32_t hh) {
+        const uint32_t w0 = off(row, blk0, hh) & ~3u;
+        a = ld128(r, w0);
+        b = ld128(r, w0 + 16u);
+        c = ld32(r, w0 + 32u);
+    }
+    __device__ __forceinline__ void prepare(uint32_t row, int blk0, uint32_t hh, BPrep<kQ8_0>& P) const {
+        const uint32_t o = off(row, blk0, hh);
+        const uint32_t sel = realign_sel(o);
+        const uint32_t raw[9] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c};
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = perm(raw[i + 1], raw[i], sel);
+#pragma unroll
+        for (int run = 0; run < 2; ++run)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) swap32(q[4 * run + i], q[4 * run + 2 + i], P.x[run][0][i], P.x[run][1][i]);
+        const uint32_t ds = realign_scale(a.x, o);
+        swap32(ds, ds, P.d[0], P.d[1]);
     }
 };
 
 // IQ4_NL: 18-byte blocks (fp16 d, 16 bytes of indices; value i < 16 in the low nibble of byte
-// i, value 16 + i in its high nibble).  The lane reads the 12-byte window around index bytes
-// 8 h .. 8 h + 7 (its low nibbles feed fragment 2 bi, its high nibbles fragment 2 bi + 1).
+// i, value 16 + i in its high nibble); the 5 dwords around a block.  Index bytes 8 h .. 8 h + 7
+// feed fragment 2 bi (low nibbles) and 2 bi + 1 (high nibbles).
 template <>
-struct BRow<kIQ4_NL> {
-    static constexpr uint32_t kBytes = 18;
-    u32x3 a[2];
+struct BPrep<kIQ4_NL> {
+    uint32_t x[2][2];  // [block][dword]: index bytes 8 h .. + 7 of block bi
     uint32_t d[2];
-    __device__ __forceinline__ void load(int bi, rsrc_t r, uint32_t row, int blk0, uint32_t h8) {
-        const uint32_t off = row + (uint32_t)(blk0 + bi) * kBytes;
-        a[bi] = ld96(r, ((off + 2u) & ~3u) + h8);
-        d[bi] = ld16(r, off);
-    }
-    __device__ __forceinline__ void convert(int j, int i, uint32_t row, int blk0, const IQ4Consts& k, u32x4& f) const {
+    __device__ __forceinline__ void convert(int j, int i, const IQ4Consts& k, u32x4& f) const {
         const int bi = j >> 1;
-        const uint32_t sh = (row + (uint32_t)(blk0 + bi) * kBytes + 2u) & 3u;
-        const u32x3 x = a[bi];
-        uint32_t q = i ? align8(x.z, x.y, sh) : align8(x.y, x.x, sh);
+        uint32_t q = x[bi][i];
         if (j & 1) q >>= 4;  // high nibbles
         uint32_t lo, hi;
         u8x4_to_f16(iq4nl_lookup_u(q & k.m7, ((q >> 1) & k.m4) | k.c0123), splat_h2(d[bi]), lo, hi);
         if (i) { f.z = lo; f.w = hi; } else { f.x = lo; f.y = hi; }
+    }
+};
+template <>
+struct BRow<kIQ4_NL> {
+    static constexpr uint32_t kBytes = 18;
+    static constexpr int kLoads = 2;
+    u32x4 a;
+    uint32_t b;
+    __device__ __forceinline__ static uint32_t off(uint32_t row, int blk0, uint32_t hh) {
+        return row + ((uint32_t)blk0 + hh) * kBytes;
+    }
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t row, int blk0, uint32_t hh) {
+        const uint32_t w0 = off(row, blk0, hh) & ~3u;
+        a = ld128(r, w0);
+        b = ld32(r, w0 + 16u);
+    }
+    __device__ __forceinline__ void prepare(uint32_t row, int blk0, uint32_t hh, BPrep<kIQ4_NL>& P) const {
+        const uint32_t o = off(row, blk0, hh);
+        const uint32_t sel = realign_sel(o);
+        const uint32_t q0 = perm(a.y, a.x, sel), q1 = perm(a.z, a.y, sel), q2 = perm(a.w, a.z, sel),
+                       q3 = perm(b, a.w, sel);
+        swap32(q0, q2, P.x[0][0], P.x[1][0]);
+        swap32(q1, q3, P.x[0][1], P.x[1][1]);
+        const uint32_t ds = realign_scale(a.x, o);
+        swap32(ds, ds, P.d[0], P.d[1]);
     }
 };
 
@@ -194,25 +243,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Step ks reads LDS stage ks % 4: its four k16 slices, then slice 0 of step ks + 1 from the next
 // stage.  In its first slice it starts the loads of step ks + 3's activations into the stage
 // step ks - 1 read; before the barrier that ends it, it waits for step ks + 2's activations
-// (started a step earlier), which slice 3 of step ks + 1 reads first.  During slice j it converts the weight fragment of the next slice;
-// in its last slice it loads step ks + 3's raw weights into the registers step ks has finished
-// with (three register sets, each load two steps ahead of its first use).  One barrier per step
-// orders every wave's stage fills before the reads of the next step and every read of a stage
-// before its refill.  Instruction order is fixed by hand: each M block of a slice is one
-// scheduling region with its MFMA, the next fragment read for that block and a share of the
-// other work.
+// (started a step earlier), which slice 3 of step ks + 1 reads first.  During slice j it
+// converts the weight fragment of the next slice; in its last slice it prepares step ks + 1's
+// raw weights and loads step ks + 3's into the same registers (two register sets, each load
+// two steps ahead of its use).  One barrier per step orders every wave's stage fills before
+// the reads of the next step and every read of a stage before its refill.  Instruction order is
+// fixed by hand: each M block of a slice is one scheduling region with its MFMA, the next
+// fragment read for that block and a share of the other work.
 template <int WT, int MB>
 struct PfLoop {
     rsrc_t ar, wr;
     uint32_t voff[4];  // per load i: activation row offset + swizzled chunk offset
     uint32_t b_row;
     uint32_t raddr[4];
-    uint32_t h8, wrow;  // wrow: byte offset of this wave's 32 rows in a stage
+    uint32_t hh, wrow;  // hh: lane / 32; wrow: byte offset of this wave's 32 rows in a stage
     int last;
     uint8_t* lds;
     IQ4Consts kc;
 
-    static constexpr int kBLoads = WT == kQ8_0 ? 6 : 4;  // buffer loads of one BRow step
+    static constexpr int kBLoads = BRow<WT>::kLoads;
     // vmcnt that leaves outstanding only what was issued after step ks + 2's activation loads:
     // the raw weights of steps ks + 2 and ks + 3 and step ks + 3's activation loads
     static constexpr int kWait = 2 * kBLoads + 4;
@@ -224,10 +273,11 @@ struct PfLoop {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(lds + st + wrow + 1024 * i), 16, voff[i], kbyte, 0, 0);
     }
 
-    // one step; Bc: raw weights of this step, Bn: of the next step.  Stage of step ks: ks % 4.
-    __device__ __forceinline__ void step(int ks, BRow<WT>& Bc, const BRow<WT>& Bn, u32x4& Fa, u32x4& Fb,
-                                         half8 (&a0)[MB], half8 (&a1)[MB], f32x16 (&acc)[MB]) const {
-        const int cblk = 2 * min(ks, last);
+    // One step.  Bl: raw weights of step ks + 1 (prepared in the last slice, then reloaded with
+    // step ks + 3's); P: prepared weights of this step (replaced by step ks + 1's in the last
+    // slice).  Stage of step ks: ks % 4.
+    __device__ __forceinline__ void step(int ks, BRow<WT>& Bl, BPrep<WT>& P, u32x4& Fa, u32x4& Fb, half8 (&a0)[MB],
+                                         half8 (&a1)[MB], f32x16 (&acc)[MB]) const {
         const int nblk = 2 * min(ks + 1, last);
         const int lblk = 2 * min(ks + 3, last);
         const uint32_t kbyte = (uint32_t)min(ks + 3, last) * 128u;
@@ -250,17 +300,11 @@ struct PfLoop {
                     for (int i = 0; i < 4; ++i)
                         if ((i * MB) / 4 == m) fill(i, s_fill, kbyte);
                 }
+                if (j == 3 && m == 0) Bl.prepare(b_row, nblk, hh, P);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    if ((i * MB) / 2 + (MB >= 4 ? 1 : 0) == m) {
-                        if (j < 3) Bc.convert(j + 1, i, b_row, cblk, kc, Fn);
-                        else Bn.convert(0, i, b_row, nblk, kc, Fn);
-                    }
-                if (j == 3) {
-#pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
-                        if ((bi * MB) / 2 == m) Bc.load(bi, wr, b_row, lblk, h8);
-                }
+                    if (min((i * MB) / 2 + 1, MB - 1) == m) P.convert(j < 3 ? j + 1 : 0, i, kc, Fn);
+                if (j == 3 && m == MB - 1) Bl.load(wr, b_row, lblk, hh);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -279,8 +323,8 @@ struct PfLoop {
 // acc[m]: rows 32 m .. 32 m + 31 of the tile, this wave's 32 weight rows.  a_off[i]: byte offset
 // of row pf_arow(i) in the activation buffer (past its end for rows beyond the tile, which then
 // read zeros); b_row: byte offset of this lane's weight row in the matrix of resource wr.
-// Steps run in threes so the raw-weight register roles are constants; the last one or two
-// steps run after the loop.
+// Steps run in pairs so the raw-weight register roles are constants; an odd last step runs
+// after the loop.
 template <int WT, int MB>
 __device__ __forceinline__ void pf_gemm(rsrc_t ar, const uint32_t (&a_off)[4], rsrc_t wr, uint32_t b_row, int nk,
                                         uint8_t* lds, f32x16 (&acc)[MB]) {
@@ -294,7 +338,7 @@ __device__ __forceinline__ void pf_gemm(rsrc_t ar, const uint32_t (&a_off)[4], r
         L.voff[i] = a_off[i] + (((lane & 7u) ^ pf_swz(r)) * 16u);
     }
     L.b_row = b_row;
-    L.h8 = (lane >> 5) * 8u;
+    L.hh = lane >> 5;
     L.wrow = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 32u * 128u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) L.raddr[j] = (lane & 31u) * 128u + ((((uint32_t)(2 * j) + (lane >> 5)) ^ pf_swz(lane & 31u)) * 16u);
@@ -303,35 +347,32 @@ __device__ __forceinline__ void pf_gemm(rsrc_t ar, const uint32_t (&a_off)[4], r
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
 
-    BRow<WT> R0, R1, R2;
+    BRow<WT> R0, R1;
+    BPrep<WT> P;
     u32x4 Fa, Fb;
     half8 a0[MB], a1[MB];
-    // prologue: stages 0, 1, 2 filled, raw weights of steps 0, 1, 2 loaded, fragment 0 of step 0
-    // converted
+    // prologue: stages 0, 1, 2 filled; step 0's weights prepared and fragment 0 converted; raw
+    // weights of steps 1 and 2 loaded
 #pragma unroll
     for (int s = 0; s < 3; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) L.fill(i, s * kPfStage, (uint32_t)min(s, L.last) * 128u);
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) R0.load(bi, wr, b_row, 0, L.h8);
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) R1.load(bi, wr, b_row, 2 * min(1, L.last), L.h8);
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) R2.load(bi, wr, b_row, 2 * min(2, L.last), L.h8);
+    R0.load(wr, b_row, 0, L.hh);
+    R1.load(wr, b_row, 2 * min(1, L.last), L.hh);
+    R0.prepare(b_row, 0, L.hh, P);
+    R0.load(wr, b_row, 2 * min(2, L.last), L.hh);
+    P.convert(0, 0, L.kc, Fa);
+    P.convert(0, 1, L.kc, Fa);
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the stage fills are not tracked
-    R0.convert(0, 0, b_row, 0, L.kc, Fa);
-    R0.convert(0, 1, b_row, 0, L.kc, Fa);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < MB; ++m) a0[m] = L.read_a(0, 0, m);
     int ks = 0;
-    for (; ks + 2 < nk; ks += 3) {
-        L.step(ks, R0, R1, Fa, Fb, a0, a1, acc);
-        L.step(ks + 1, R1, R2, Fa, Fb, a0, a1, acc);
-        L.step(ks + 2, R2, R0, Fa, Fb, a0, a1, acc);
+    for (; ks + 1 < nk; ks += 2) {
+        L.step(ks, R1, P, Fa, Fb, a0, a1, acc);
+        L.step(ks + 1, R0, P, Fa, Fb, a0, a1, acc);
     }
-    if (ks < nk) L.step(ks, R0, R1, Fa, Fb, a0, a1, acc);
-    if (ks + 1 < nk) L.step(ks + 1, R1, R2, Fa, Fb, a0, a1, acc);
+    if (ks < nk) L.step(ks, R1, P, Fa, Fb, a0, a1, acc);
     // the last steps started (clamped) stage fills: let every wave's land before LDS is reused
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     __syncthreads();
