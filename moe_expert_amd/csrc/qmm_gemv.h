@@ -7,8 +7,8 @@
 
 namespace qmm {
 
-constexpr int kGemvLanesPerRow = 16;  // one DPP row
-constexpr int kGemvThreads = 512;     // 8 waves, two per SIMD
+constexpr int kGemvLanesPerRow = 16;  // one DPP row (the default row width)
+constexpr int kGemvThreads = 512;     // 8 waves, two per SIMD (the default workgroup)
 constexpr int kGemvRowsPerWG = 32;    // 8 waves x 4 rows
 constexpr int kGemvChunk = 6;         // blocks per lane whose loads are issued together
 constexpr size_t kLdsCap = 65536;     // LDS a workgroup may use
@@ -45,14 +45,20 @@ __device__ __forceinline__ void stage_grid(const uint8_t* grid, uint32_t* lds_gr
     for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_grid[i] = ld32(gr, 4u * i);
 }
 
-// The 512-word codebook staged by a 512-thread workgroup, one word per thread, split into an
-// early load and a late LDS write like the activations.
+// The 512-word codebook staged by a workgroup of TH threads (512 / TH words per thread), split
+// into an early load and a late LDS write like the activations.
+template <int TH = kGemvThreads>
 struct GridStage {
-    uint32_t v;
+    static_assert(512 % TH == 0, "the codebook must split evenly over the workgroup");
+    uint32_t v[512 / TH];
     __device__ __forceinline__ void load(const uint8_t* grid) {
-        v = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x & 511u));
+#pragma unroll
+        for (int i = 0; i < 512 / TH; ++i) v[i] = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x + i * TH));
     }
-    __device__ __forceinline__ void store(uint32_t* lds_grid) const { lds_grid[threadIdx.x & 511u] = v; }
+    __device__ __forceinline__ void store(uint32_t* lds_grid) const {
+#pragma unroll
+        for (int i = 0; i < 512 / TH; ++i) lds_grid[threadIdx.x + i * TH] = v[i];
+    }
 };
 
 // Activation staging in two halves so that its global loads can be issued before the weight
@@ -126,12 +132,12 @@ struct ActStage {
     }
 };
 
-// One lane's share of one row: blocks s = l16 + 16 i, i = 0, 1, ...  U blocks are loaded per
-// chunk; MULTI = the row has more than U blocks per lane (double-buffered chunks), otherwise U
-// is exactly the lane's block count.  Loads are unconditional (a block past the row is read at
-// the row's last block and not used), so the code between the loads and their uses stays
-// straight-line and each use waits only for its own load.
-template <int WT, int NC, bool SUMS, int U, bool MULTI>
+// One lane's share of one row of LPR lanes: blocks s = l + LPR i, i = 0, 1, ...  U blocks are
+// loaded per chunk; MULTI = the row has more than U blocks per lane (double-buffered chunks),
+// otherwise U is at least the lane's block count.  Loads are unconditional (a block past the
+// row is read at the row's last block and not used), so the code between the loads and their
+// uses stays straight-line and each use waits only for its own load.
+template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow>
 struct RowEngine {
     static constexpr int RAW = Unit<WT>::RAW;
     rsrc_t wr;
@@ -140,8 +146,8 @@ struct RowEngine {
     uint32_t A[U][RAW], B[MULTI ? U : 1][RAW];
     IQ4Consts kc;
 
-    __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l16_)
-        : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + 15) / 16), l16(l16_) {}
+    __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l_)
+        : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + LPR - 1) / LPR), l16(l_) {}
 
     __device__ __forceinline__ uint32_t unit_off(int s) const {
         // 32-bit multiply-add (a 64-bit one would tie a dead high half to a pending load)
@@ -153,7 +159,7 @@ struct RowEngine {
     __device__ __forceinline__ void load(uint32_t (&buf)[N][RAW], int i0) {
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            int s = l16 + 16 * (i0 + u);
+            int s = l16 + LPR * (i0 + u);
             s = s < nunits ? s : nunits - 1;
             if constexpr (WT == kCB3) Unit<WT>::load(wr, unit_off(s), s & 7, buf[u]);
             else Unit<WT>::load(wr, unit_off(s), buf[u]);
@@ -168,7 +174,7 @@ struct RowEngine {
                                             bool row_ok) {
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            const int s = l16 + 16 * (i0 + u);
+            const int s = l16 + LPR * (i0 + u);
             if (s < nunits) {
                 uint32_t W[8];
                 uint32_t dw;
@@ -222,30 +228,44 @@ struct RowEngine {
     }
 };
 
-// One workgroup's 32 rows [row0, row0 + 32) of a decode GEMV pass: columns [col0, col0 + ncp)
-// of the q8_1 activations behind `xr` (column c is q8_1 blocks c*K/32 ...), results to
-// y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  Order of work: activation
-// loads, then this lane's weight loads, then the activation LDS writes (they wait only for
-// the activation loads), barrier, decode + apply as the weights arrive, DPP row sums.
-template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS>
+// Sum over the LPR lanes of a row (16: one DPP row; 64: the wave); every lane of the row gets
+// the same value, added in the same order for every column.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+    v = row16_sum(v);
+    if constexpr (LPR == 64) {
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+    }
+    return v;
+}
+
+// One workgroup's TH / 64 * (64 / LPR) rows starting at row0 of a decode GEMV pass: columns
+// [col0, col0 + ncp) of the q8_1 activations behind `xr` (column c is q8_1 blocks c*K/32 ...),
+// results to y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  LPR lanes per
+// row (16 or 64).  Order of work: activation loads, then this lane's weight loads, then the
+// activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
+// the weights arrive, cross-lane row sums.
+template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, int col0, int ncp,
                                           float* y, int64_t ldy, int32_t* sums, int row0, uint32_t* lds) {
+    static_assert(LPR == 16 || LPR == 64, "a row is one DPP row or one wave");
     ActLds act = act_lds_layout(lds, K, ncp);
     uint32_t* lds_grid = act_lds_end(act, ncp);
 
     const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15;
-    const int row = row0 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+    const int l16 = lane & (LPR - 1);
+    const int row = row0 + (threadIdx.x >> 6) * (64 / LPR) + lane / LPR;
     const bool row_ok = row < nrows;
     const int rowc = row_ok ? row : nrows - 1;
     const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
 
     ActStage<NS> stage;
     stage.load(xr, act, col0, ncp);
-    GridStage gstage;
+    GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
-    RowEngine<WT, NC, SUMS, U, MULTI> eng(wr, row_off, K, l16);
+    RowEngine<WT, NC, SUMS, U, MULTI, LPR> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
     stage.store(act, ncp);
@@ -266,15 +286,15 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
         float out = 0.0f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const float s = row16_sum(acc[c]);
+            const float s = row_sum<LPR>(acc[c]);
             if (l16 == c) out = s;
         }
         if (row_ok && l16 < ncp) y[(int64_t)(col0 + l16) * ldy + row] = out;
     }
 }
 
-// Blocks per lane of a row of k values (16 lanes per row).
-inline int lane_blocks(int64_t k) { return (int)((k / 32 + 15) / 16); }
+// Blocks per lane of a row of k values (lpr lanes per row).
+inline int lane_blocks(int64_t k, int lpr = kGemvLanesPerRow) { return (int)((k / 32 + lpr - 1) / lpr); }
 
 // Staging slots per thread for a pass of ncp columns of k values.
 inline int stage_slots(int64_t k, int ncp, int threads) {

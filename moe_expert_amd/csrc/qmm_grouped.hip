@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kGemvThreads) void gu_kernel(
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
         ActStage<NS> stage;
         stage.load_cols(xr, act, ncp, cols);
-        GridStage gstage;
+        GridStage<> gstage;
         if constexpr (WT == kCB3) gstage.load(grid);
         __builtin_amdgcn_sched_barrier(0);
         if (c0 == gi.k0 || MULTI) {
