@@ -136,8 +136,10 @@ struct ActStage {
 // loaded per chunk; MULTI = the row has more than U blocks per lane (double-buffered chunks),
 // otherwise U is at least the lane's block count.  Loads are unconditional (a block past the
 // row is read at the row's last block and not used), so the code between the loads and their
-// uses stays straight-line and each use waits only for its own load.
-template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow>
+// uses stays straight-line and each use waits only for its own load.  NCMIN: columns every pass
+// of this instance has (NC / 2 + 1 for the dense GEMV, whose NC is the smallest of 1, 2, 4, 8
+// that holds the pass; 1 where passes may be narrower).
+template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow, int NCMIN = 1>
 struct RowEngine {
     static constexpr int RAW = Unit<WT>::RAW;
     rsrc_t wr;
@@ -182,27 +184,29 @@ struct RowEngine {
                 if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(s), s & 7, grid, W, dw, mult);
                 else Unit<WT>::decode(buf[u], unit_off(s), W, dw, mult, kc);
                 const float dwf = h2f(dw);
+                // Columns below NCMIN always exist in the pass and run straight-line (their LDS
+                // reads can be issued ahead); the others only when the pass has them.
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    if (c < ncp) {
-                        const uint32_t* a = act.q + __umul24((uint32_t)c, (uint32_t)act.kw) + s * 8;
-                        const u32x4 a0 = *(const u32x4*)a;
-                        const u32x4 a1 = *(const u32x4*)(a + 4);
-                        int v = dot4(W[0], a0.x, 0);
-                        v = dot4(W[1], a0.y, v);
-                        v = dot4(W[2], a0.z, v);
-                        v = dot4(W[3], a0.w, v);
-                        v = dot4(W[4], a1.x, v);
-                        v = dot4(W[5], a1.y, v);
-                        v = dot4(W[6], a1.z, v);
-                        v = dot4(W[7], a1.w, v);
-                        const int isum = v * mult;
-                        if constexpr (SUMS) {
-                            if (row_ok) srow[c * scol + s] = isum;
-                        } else {
-                            const float dd = dwf * act.d[__umul24((uint32_t)c, (uint32_t)act.nb) + s];
-                            acc[c] = __builtin_fmaf(dd, (float)isum, acc[c]);
-                        }
+                    if (c >= NCMIN && c >= ncp) continue;
+                    const uint32_t cc = (uint32_t)c;
+                    const uint32_t* a = act.q + __umul24(cc, (uint32_t)act.kw) + s * 8;
+                    const u32x4 a0 = *(const u32x4*)a;
+                    const u32x4 a1 = *(const u32x4*)(a + 4);
+                    int v = dot4(W[0], a0.x, 0);
+                    v = dot4(W[1], a0.y, v);
+                    v = dot4(W[2], a0.z, v);
+                    v = dot4(W[3], a0.w, v);
+                    v = dot4(W[4], a1.x, v);
+                    v = dot4(W[5], a1.y, v);
+                    v = dot4(W[6], a1.z, v);
+                    v = dot4(W[7], a1.w, v);
+                    const int isum = v * mult;
+                    if constexpr (SUMS) {
+                        if (row_ok) srow[c * scol + s] = isum;
+                    } else {
+                        const float dd = dwf * act.d[__umul24(cc, (uint32_t)act.nb) + s];
+                        acc[c] = __builtin_fmaf(dd, (float)isum, acc[c]);
                     }
                 }
             }
@@ -246,7 +250,8 @@ __device__ __forceinline__ float row_sum(float v) {
 // row (16 or 64).  Order of work: activation loads, then this lane's weight loads, then the
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
 // the weights arrive, cross-lane row sums.
-template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads>
+template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
+          int NCMIN = 1>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, int col0, int ncp,
                                           float* y, int64_t ldy, int32_t* sums, int row0, uint32_t* lds) {
     static_assert(LPR == 16 || LPR == 64, "a row is one DPP row or one wave");
@@ -265,7 +270,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
-    RowEngine<WT, NC, SUMS, U, MULTI, LPR> eng(wr, row_off, K, l16);
+    RowEngine<WT, NC, SUMS, U, MULTI, LPR, NCMIN> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
     stage.store(act, ncp);

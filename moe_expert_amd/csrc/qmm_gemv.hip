@@ -26,8 +26,9 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                   uint32_t xqbytes, int col0, int ncp, float* __restrict__ y,
                                                   int64_t ldy, int32_t* __restrict__ sums) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    gemv_tile<WT, SUMS, NC, U, MULTI, NS, LPR, TH>(make_rsrc_dw(w, wbytes), nrows, K, grid, make_rsrc(xq, xqbytes),
-                                                   col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
+    gemv_tile<WT, SUMS, NC, U, MULTI, NS, LPR, TH, NC / 2 + 1>(make_rsrc_dw(w, wbytes), nrows, K, grid,
+                                                               make_rsrc(xq, xqbytes), col0, ncp, y, ldy, sums,
+                                                               blockIdx.x * (TH / LPR), lds);
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
