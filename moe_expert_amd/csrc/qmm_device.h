@@ -234,7 +234,9 @@ __device__ __forceinline__ uint32_t sign_bits_to_bytes(uint32_t nib) {
 // never carries into its neighbour.
 __device__ __forceinline__ uint32_t cb3_signed(uint32_t g, uint32_t nib) {
     const uint32_t x = sign_bits_to_bytes(nib);
-    const uint32_t mask = (x << 8) - x;
+    // (x << 8) - x = x * 255; kept as a shift and a subtract (the compiler would otherwise emit
+    // a quarter-rate v_mul_lo_u32)
+    const uint32_t mask = IQ4Consts::opaque_u(x << 8) - x;
     return (g ^ mask) + x;
 }
 

@@ -49,15 +49,18 @@ __device__ __forceinline__ void stage_grid(const uint8_t* grid, uint32_t* lds_gr
 // into an early load and a late LDS write like the activations.
 template <int TH = kGemvThreads>
 struct GridStage {
-    static_assert(512 % TH == 0, "the codebook must split evenly over the workgroup");
-    uint32_t v[512 / TH];
+    static_assert(512 % TH == 0 || TH % 512 == 0, "the codebook must split evenly over the workgroup");
+    static constexpr int N = TH >= 512 ? 1 : 512 / TH;
+    uint32_t v[N];
+    // threads past the first 512 of a larger workgroup re-read word tid % 512 and store nothing
     __device__ __forceinline__ void load(const uint8_t* grid) {
 #pragma unroll
-        for (int i = 0; i < 512 / TH; ++i) v[i] = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x + i * TH));
+        for (int i = 0; i < N; ++i) v[i] = ld32(make_rsrc(grid, 2048), 4u * ((threadIdx.x + i * TH) & 511u));
     }
     __device__ __forceinline__ void store(uint32_t* lds_grid) const {
 #pragma unroll
-        for (int i = 0; i < 512 / TH; ++i) lds_grid[threadIdx.x + i * TH] = v[i];
+        for (int i = 0; i < N; ++i)
+            if (TH <= 512 || threadIdx.x < 512) lds_grid[threadIdx.x + i * TH] = v[i];
     }
 };
 
@@ -101,17 +104,16 @@ struct ActStage {
             load_slot(xr, act, j, col0 + (i >> lsh), i);
         }
     }
-    // Pass column c taken from activation column cols[c] (a uniform table).
-    template <int NCOL>
-    __device__ __forceinline__ void load_cols(rsrc_t xr, const ActLds& act, int ncp, const int (&cols)[NCOL]) {
+    // Pass column c taken from activation column entry_col[c0 + c]; a column outside
+    // [0, ncols) reads the zeros past the end of the activations.
+    __device__ __forceinline__ void load_entries(rsrc_t xr, const ActLds& act, int ncp, const int32_t* entry_col, int c0,
+                                                 int ncols) {
         setup(act, ncp);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             const int i = slot(j, act, ncp);
-            const int c = i >> lsh;
-            int col = cols[0];
-#pragma unroll
-            for (int cc = 1; cc < NCOL; ++cc) col = c == cc ? cols[cc] : col;
+            int col = entry_col[c0 + (i >> lsh)];
+            col = (col >= 0 && col < ncols) ? col : ncols;
             load_slot(xr, act, j, col, i);
         }
     }
@@ -201,7 +203,8 @@ struct RowEngine {
                     v = dot4(W[5], a1.y, v);
                     v = dot4(W[6], a1.z, v);
                     v = dot4(W[7], a1.w, v);
-                    const int isum = v * mult;
+                    // |v| < 2^23 and mult <= 31: the 24-bit multiply is exact
+                    const int isum = WT == kCB3 ? __mul24(v, mult) : v;
                     if constexpr (SUMS) {
                         if (row_ok) srow[c * scol + s] = isum;
                     } else {

@@ -12,16 +12,17 @@
 //                    forms h = silu(g) * u and quantizes the 32 values to one q8_1 block of H.
 //   down kernel    : the decode GEMV tile over W_down[e] with the group's H blocks (the entries
 //                    of a group are consecutive, so their H blocks are too).
-// silu(z) = z / (1 + e^-z): the exponential is taken in binary64 and rounded to binary32, the
-// rest is binary32 (IEEE division), so h depends only on the binary32 g and u.
+// silu(z) = z / (1 + e^-z) in binary32 (expf within 1 ulp, IEEE division).
 #include "qmm_gemv.h"
 
 namespace qmm {
 
 constexpr int kGroupPass = 8;  // entries per pass
 
+// silu(z) * u in binary32 with the library expf (documented maximum error 1 ulp), an IEEE
+// division and a product: within a few ulp of the same expression evaluated exactly.
 __device__ __forceinline__ float silu_mul(float z, float u) {
-    const float e = (float)exp(-(double)z);
+    const float e = expf(-z);
     const float den = opaque(1.0f + e);
     const float sl = opaque(z / den);
     return sl * u;
@@ -41,8 +42,13 @@ struct GroupInfo {
     }
 };
 
+// gate/up workgroup: 1024 threads, 16 waves (4 per SIMD).  Waves 0..7 run the gate rows and
+// waves 8..15 the up rows of the 32 intermediate indices of one q8_1 block of H (4 indices per
+// wave, a DPP row of 16 lanes each), so each lane holds one row engine.
+constexpr int kGuThreads = 1024;
+
 template <int WT, int U, bool MULTI, int NS>
-__global__ __launch_bounds__(kGemvThreads) void gu_kernel(
+__global__ __launch_bounds__(kGuThreads) void gu_kernel(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
     int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
     uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
@@ -59,63 +65,49 @@ __global__ __launch_bounds__(kGemvThreads) void gu_kernel(
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15;
-    const int rg = (threadIdx.x >> 6) * 4 + (lane >> 4);  // 0..31
-    const int i = blockIdx.x * 32 + rg;                    // intermediate index
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool up = wave >= 8;
+    const int rg = (wave & 7) * 4 + (lane >> 4);  // 0..31
+    const int i = blockIdx.x * 32 + rg;           // intermediate index
     const uint32_t rb = (uint32_t)row_bytes_dev<WT>(hidden);
     const rsrc_t xr = make_rsrc(xq, xqbytes);
-    const rsrc_t rg_w = make_rsrc_dw(wg + gi.e * gu_stride, expert_bytes);
-    const rsrc_t ru_w = make_rsrc_dw(wu + gi.e * gu_stride, expert_bytes);
+    const rsrc_t wr = make_rsrc_dw((up ? wu : wg) + gi.e * gu_stride, expert_bytes);
     const int nbh = inter / 32;
-
-    RowEngine<WT, kGroupPass, false, U, MULTI> eg(rg_w, (uint32_t)i * rb, hidden, l16);
-    RowEngine<WT, kGroupPass, false, U, MULTI> eu(ru_w, (uint32_t)i * rb, hidden, l16);
+    float* sums = up ? ul : gl;
+    float* dbg = up ? dbg_u : dbg_g;
 
     for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
-        // the pass's activation columns (uniform); out-of-range columns read as zeros
-        int cols[kGroupPass];
-#pragma unroll
-        for (int c = 0; c < kGroupPass; ++c) {
-            int col = __builtin_amdgcn_readfirstlane(entry_col[c0 + (c < ncp ? c : ncp - 1)]);
-            cols[c] = (col >= 0 && col < xq_cols) ? col : xq_cols;
-        }
+        // The row engine is rebuilt each pass from values the compiler cannot see through, so
+        // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
+        // in registers, or spill it, across the whole loop).
+        RowEngine<WT, kGroupPass, false, U, MULTI> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
+                                                       (int)IQ4Consts::opaque_u((uint32_t)l16));
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
         ActStage<NS> stage;
-        stage.load_cols(xr, act, ncp, cols);
-        GridStage<> gstage;
+        stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols);
+        GridStage<kGuThreads> gstage;
         if constexpr (WT == kCB3) gstage.load(grid);
         __builtin_amdgcn_sched_barrier(0);
-        if (c0 == gi.k0 || MULTI) {
-            eg.load_first();
-            eu.load_first();
-        }
+        eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
         __builtin_amdgcn_sched_barrier(0);
         stage.store(act, ncp);
         if constexpr (WT == kCB3) gstage.store(lds_grid);
         __syncthreads();
 
-        float ag[kGroupPass], au[kGroupPass];
+        float acc[kGroupPass];
 #pragma unroll
-        for (int c = 0; c < kGroupPass; ++c) ag[c] = au[c] = 0.0f;
-        eg.run(act, ncp, lds_grid, ag, nullptr, 0, true);
-        eu.run(act, ncp, lds_grid, au, nullptr, 0, true);
-        float gsum = 0.0f, usum = 0.0f;
+        for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
+        eng.run(act, ncp, lds_grid, acc, nullptr, 0, true);
+        float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) {
-            const float sg = row16_sum(ag[c]);
-            const float su = row16_sum(au[c]);
-            if (l16 == c) {
-                gsum = sg;
-                usum = su;
-            }
+            const float sc = row16_sum(acc[c]);
+            if (l16 == c) sum = sc;
         }
         if (l16 < ncp) {
-            gl[l16 * 32 + rg] = gsum;
-            ul[l16 * 32 + rg] = usum;
-            if (dbg_g) {
-                dbg_g[(int64_t)(c0 + l16) * inter + i] = gsum;
-                dbg_u[(int64_t)(c0 + l16) * inter + i] = usum;
-            }
+            sums[l16 * 32 + rg] = sum;
+            if (dbg) dbg[(int64_t)(c0 + l16) * inter + i] = sum;
         }
         __syncthreads();
         // SwiGLU -> q8_1: one half wave per entry (waves 0..3), value j = intermediate 32t + j
@@ -156,14 +148,16 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
     }
 }
 
-template <int WT, typename F>
+// UM: chunk of the double-buffered (MULTI) instance, for rows of more than 6 blocks per lane
+// (3 in the 1024-thread gate/up kernel, whose lanes have 128 registers).
+template <int WT, int UM = 6, typename F>
 static void dispatch_u_ns(int lb, int ns, F&& go) {
     auto by_u = [&](auto ns_c) {
         constexpr int NS = decltype(ns_c)::value;
         if (lb <= 2) go.template operator()<WT, 2, false, NS>();
         else if (lb <= 5) go.template operator()<WT, 5, false, NS>();
         else if (lb == 6) go.template operator()<WT, 6, false, NS>();
-        else go.template operator()<WT, 6, true, NS>();
+        else go.template operator()<WT, UM, true, NS>();
     };
     if (ns == 1) by_u(std::integral_constant<int, 1>{});
     else if (ns == 2) by_u(std::integral_constant<int, 2>{});
@@ -199,14 +193,14 @@ static int launch_grouped(const GroupedArgs& a) {
         const size_t lds = gemv_lds_bytes(a.wtype_gu, a.hidden, kGroupPass) + 2 * kGroupPass * 32 * sizeof(float);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
-            hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGemvThreads), lds, a.st, a.w_gate, a.w_up,
+            hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up,
                                a.gu_stride, gu_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes,
                                a.xq_cols, a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
-        const int lb = lane_blocks(a.hidden), ns = stage_slots(a.hidden, kGroupPass, kGemvThreads);
-        if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0>(lb, ns, go);
-        else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(lb, ns, go);
-        else dispatch_u_ns<kCB3>(lb, ns, go);
+        const int lb = lane_blocks(a.hidden), ns = stage_slots(a.hidden, kGroupPass, kGuThreads);
+        if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0, 3>(lb, ns, go);
+        else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL, 3>(lb, ns, go);
+        else dispatch_u_ns<kCB3, 3>(lb, ns, go);
         const int rc = launch_status();
         if (rc) return rc;
     }

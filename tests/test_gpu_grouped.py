@@ -95,6 +95,17 @@ def test_grouped_other_formats(wt_gu, wt_down):
     run_case(ex, ge, go, ec, 2, 822)
 
 
+def test_grouped_long_rows():
+    """hidden 4096 (8 blocks per lane: the double-buffered gate/up chunks) with 11 entries in a
+    group (two passes)."""
+    print("grouped long rows: 3 experts 4096 -> 64, groups of 11 and 2 entries", flush=True)
+    ex = Experts(850, 3, 4096, 64, wt_gu=M.QMM_CB3, wt_down=M.QMM_Q8_0)
+    ge = np.array([2, 0], np.int32)
+    go = np.array([0, 11, 13], np.int32)
+    ec = synth.rng_for(851).integers(0, 6, size=13).astype(np.int32)
+    run_case(ex, ge, go, ec, 6, 852)
+
+
 @pytest.fixture(scope="module")
 def full_experts():
     """The grouped decode workload: 128 experts, hidden 2560, CB3 gate/up 2560->1024, IQ4_NL
