@@ -120,8 +120,8 @@ size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned fla
  * e = group_expert[g]) and every entry j in [group_entry_off[g], group_entry_off[g+1]):
  *   x  = q8_1 column entry_col[j] of xq (width hidden)
  *   gv = W_gate[e] x,  uv = W_up[e] x          (qgemv_dense arithmetic, inter rows)
- *   h  = silu(gv) * uv,  silu(z) = z / (1 + exp(-z)): exp in binary64 rounded to binary32,
- *        the rest binary32
+ *   h  = silu(gv) * uv,  silu(z) = z / (1 + exp(-z)) in binary32 (device expf, <= 1 ulp;
+ *        IEEE division)
  *   H  = q8_1(h) per 32 consecutive intermediate values          (workspace)
  *   y[j*hidden + r] = (W_down[e] H)[r]                            (binary32; unweighted)
  *   w_gate, w_up : expert e's matrix at byte offset e*gu_expert_stride, inter rows of width
