@@ -34,6 +34,34 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2516.6
 MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CALIB_BYTES = 64 << 20   # the plain copy that scales the counters
+
+
+def source_digest():
+    """sha256 of the library sources: recorded counter figures are only reported for the sources
+    they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in ("moe_expert_amd/csrc", "include"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            h.update(f.encode())
+            with open(os.path.join(ROOT, d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch recorded for `key` by --pmc-summary, or None when there is no record
+    or the sources have changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest():
+        return None
+    return rec
 
 
 def timed_graph(torch, fn, reps, use_graph=True):
@@ -155,6 +183,10 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                 M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
         literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
+    rec = recorded_traffic(f"gemv:{wtype}:{nrows}x{k}")
+    traffic = None
+    if rec and all(str(n) in rec["bytes_per_launch"] for n in cols):
+        traffic = round(sum(rec["bytes_per_launch"][str(n)] for n in cols) / len(cols))
     out = base_line(metric, step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
                     {"workload": f"{name}, cold rotation of {ncopies} weight copies "
                                  f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
@@ -162,7 +194,8 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
     out.update({"us_per_call": us, "gbps_per_call": gbps, "warm_us_per_call": warm,
                 f"rotation_{ndistinct}_copies_us_per_call": literal,
                 "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                             "algorithmic_bytes_per_launch": round(tot_b / len(cols)),
                              "kernel": f"gemv_kernel ({name.split(',')[0]}), columns {list(cols)}"}})
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_gemv(wtype, host_copies[0], nrows, k, cols, seed, step_bytes)
@@ -198,12 +231,13 @@ def grouped_bytes(hidden, inter, ngroups, m, expert_bytes):
     return ngroups * expert_bytes + m * (hidden // 32) * 36 + nent * (inter // 32) * 36 * 2 + nent * hidden * 4
 
 
-def bench_grouped(args, torch, M):
+def grouped_setup(torch, M):
+    """Weights (expert sets in rotation), routing and buffers of the grouped decode workload;
+    returns (sets, calls, call(m, set), host weights, grid, sizes)."""
     import numpy as np
 
     import synth
     nexp, hidden, inter, ngroups = 128, 2560, 1024, 16
-    ms_list = (1, 4, 8)
     seed = synth.SEEDS["grouped_decode"]
     rng = synth.rng_for(seed)
     grid = synth.cb3_grid(synth.rng_for(synth.SEEDS["cb3_grid"]))
@@ -216,7 +250,7 @@ def bench_grouped(args, torch, M):
     sets = [{k: torch.from_numpy(v).to(dev) for k, v in host.items()} for _ in range(nsets)]
     gd = torch.from_numpy(grid).to(dev)
     calls = {}
-    for m in ms_list:
+    for m in GROUPED_M:
         ge, go, ec = synth.decode_routing(synth.rng_for(seed + m), nexp, ngroups, m)
         x = synth.activations(synth.rng_for(seed + 100 + m), m, hidden)
         xd = torch.from_numpy(x).to(dev)
@@ -225,12 +259,23 @@ def bench_grouped(args, torch, M):
         ws = torch.empty(max(16, M.qgemv_grouped_experts_workspace(inter, ngroups * m)), dtype=torch.uint8, device=dev)
         calls[m] = dict(ge=torch.from_numpy(ge).to(dev), go=torch.from_numpy(go).to(dev),
                         ec=torch.from_numpy(ec).to(dev), x=xd, xq=xq, y=y, ws=ws, host=(ge, go, ec, x))
-    use_graph = not args.no_graph
 
     def call(m, s):
         c = calls[m]
         M.qgemv_grouped_experts(synth.CB3, s["wg"], s["wu"], synth.IQ4_NL, s["wd"], hidden, inter, c["xq"], c["ge"],
                                 c["go"], c["ec"], grid=gd, y=c["y"], ws=c["ws"])
+
+    sizes = dict(nexp=nexp, hidden=hidden, inter=inter, ngroups=ngroups, expert_bytes=expert_bytes, nsets=nsets)
+    return sets, calls, call, host, grid, sizes
+
+
+def bench_grouped(args, torch, M):
+    import synth
+    ms_list = GROUPED_M
+    sets, calls, call, host, grid, z = grouped_setup(torch, M)
+    hidden, inter, ngroups, expert_bytes, nsets, nexp = (z["hidden"], z["inter"], z["ngroups"], z["expert_bytes"],
+                                                         z["nsets"], z["nexp"])
+    use_graph = not args.no_graph
 
     def step(slot):
         s = sets[slot % nsets]
@@ -254,6 +299,8 @@ def bench_grouped(args, torch, M):
         tot_b += b
         tot_us += t
     ach = tot_b / (tot_us * 1e-6) / 1e9
+    rec = recorded_traffic("grouped")
+    traffic = round(sum(rec["bytes_per_launch"][str(m)] for m in ms_list) / len(ms_list)) if rec else None
     out = base_line("µs/call and achieved HBM GB/s, grouped MoE decode (16 groups x m entries, 128 experts)",
                     step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
                     {"workload": "grouped MoE decode: hidden 2560, 128 experts, CB3 gate/up 2560->1024, IQ4_NL down "
@@ -262,7 +309,8 @@ def bench_grouped(args, torch, M):
                      "hip_graph": use_graph})
     out.update({"us_per_call": us, "gbps_per_call": gbps,
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                             "algorithmic_bytes_per_launch": round(tot_b / len(ms_list)),
                              "kernel": "gu_kernel + down_kernel (one call, m = 1/4/8)"}})
     if not args.no_cpu:
         import oracle
@@ -285,7 +333,8 @@ def bench_grouped(args, torch, M):
 
 # ------------------------------------------------------------------ prefill grouped expert GEMM
 
-def bench_prefill(args, torch, M):
+def prefill_setup(torch, M):
+    """Weights, tokens, routing and buffers of the prefill workload; returns (call, host data, sizes)."""
     import numpy as np
 
     import synth
@@ -309,6 +358,17 @@ def bench_prefill(args, torch, M):
         M.qgemm_prefill_experts(synth.IQ4_NL, d["wg"], d["wu"], synth.Q8_0, d["wd"], nexp, hidden, inter, d["x"],
                                 d["st"], d["off"], y=y, ws=ws)
 
+    host = dict(wg=wg, wu=wu, wd=wd, x16=x16, st=st, off=off)
+    return call, host, dict(nexp=nexp, ntok=ntok, topk=topk, hidden=hidden, inter=inter, nent=nent)
+
+
+def bench_prefill(args, torch, M):
+    import numpy as np
+
+    import synth
+    call, h, z = prefill_setup(torch, M)
+    wg, wu, wd, x16, st, off = h["wg"], h["wu"], h["wd"], h["x16"], h["st"], h["off"]
+    nexp, ntok, hidden, inter, nent = z["nexp"], z["ntok"], z["hidden"], z["inter"], z["nent"]
     use_graph = not args.no_graph
     run_step = capture_slots(torch, call, 1) if use_graph else call
     ms = contract_steps(torch, run_step, args.steps, args.warmup)
@@ -319,9 +379,11 @@ def bench_prefill(args, torch, M):
                     {"workload": "prefill grouped expert GEMM: 8192 tokens x hidden 2560, top-8 of 128 experts, "
                                  "IQ4_NL gate/up 2560->1024, Q8_0 down 1024->2560, FP16 dequant in LDS + fp16 MFMA",
                      "tokens": ntok, "entries": int(nent), "hip_graph": use_graph})
+    rec = recorded_traffic("prefill")
     out.update({"us_per_call": round(ms * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": rec["bytes_per_launch"]["call"] if rec else None,
                              "kernel": "schedule + pf_gateup_kernel + pf_down_kernel (one call)"}})
     if not args.no_cpu:
         import oracle
@@ -343,6 +405,138 @@ def bench_prefill(args, torch, M):
     return out
 
 
+# ------------------------------------------------------------------ HBM traffic counters
+#
+# The traffic figure comes from two rocprofv3 counter runs of `--pmc-probe` (FETCH_SIZE, then
+# WRITE_SIZE, kilobytes per dispatch), each scaled by what the same counter reads for a plain
+# 64 MiB device copy, and is recorded by `--pmc-summary` with a digest of the sources:
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o run -- python bench.py --pmc-probe
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o run -- python bench.py --pmc-probe
+#   python bench.py --pmc-summary <F>/run_counter_collection.csv <W>/run_counter_collection.csv
+
+PROBE_COLS = (1, 4, 8)
+GROUPED_M = (1, 4, 8)
+
+
+def pmc_probe(torch, M, workload):
+    """Three plain device copies of CALIB_BYTES, then one cold pass of `workload` with no graphs,
+    so that every launch is a dispatch of its own: the headline GEMV once per weight copy at 1, 4
+    and 8 columns; the grouped decode once per expert set at m = 1, 4, 8; the prefill call twice."""
+    import synth
+    dev = torch.device("cuda", 0)
+    if workload == "gemv":
+        nrows, k, wt = 8192, 2560, synth.IQ4_NL
+        wbytes = nrows * synth.row_bytes(wt, k)
+        ncopies = -(-2 * MALL_BYTES // wbytes) + 1
+        host = [synth.weights(wt, synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + i), nrows, k) for i in range(6)]
+        copies = [torch.from_numpy(host[i % 6]).to(dev) for i in range(ncopies)]
+        rng = synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + 100)
+        xq = {n: M.qmm_quantize_q8_1(torch.from_numpy(synth.activations(rng, n, k)).to(dev)) for n in PROBE_COLS}
+        y = {n: torch.empty((n, nrows), dtype=torch.float32, device=dev) for n in PROBE_COLS}
+
+        def run():
+            for n in PROBE_COLS:
+                for w in copies:
+                    M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
+    elif workload == "grouped":
+        sets, _, call, _, _, _ = grouped_setup(torch, M)
+
+        def run():
+            for m in GROUPED_M:
+                for st in sets:
+                    call(m, st)
+    elif workload == "prefill":
+        call, _, _ = prefill_setup(torch, M)
+
+        def run():
+            call()
+            call()
+    else:
+        raise SystemExit(f"no counter probe for workload {workload}")
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    run()
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": workload}), flush=True)
+
+
+def pmc_summary(workload, fetch_csv, write_csv):
+    """Per-launch HBM bytes of the probe's launches, from the two counter runs: each counter's
+    kilobytes per dispatch times CALIB_BYTES over what that counter reads for the plain copies."""
+    import csv
+    import re
+
+    import synth
+    pattern = {"gemv": r"gemv_kernel<\d+, false, (\d+),", "grouped": r"(gu_kernel|down_kernel)",
+               "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)"}[workload]
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        ours = [r for r in rows if re.search(pattern, r["Kernel_Name"])]
+        first = int(ours[0]["Dispatch_Id"])
+        # the calibration copies: the large device copies just before the first launch measured
+        cp = [float(r["Counter_Value"]) for r in rows
+              if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first]
+        calib = [v for v in cp if v >= 0.5 * max(cp)][-3:]
+        return sum(calib) / len(calib), [(re.search(pattern, r["Kernel_Name"]).group(1), float(r["Counter_Value"]))
+                                         for r in ours]
+
+    fcal, fk = per_kernel(fetch_csv, "FETCH_SIZE")
+    wcal, wk = per_kernel(write_csv, "WRITE_SIZE")
+    ff = CALIB_BYTES / 1024 / fcal
+    wf = CALIB_BYTES / 1024 / wcal
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    rec = {"fetch_scale": round(ff, 4), "write_scale": round(wf, 4), "calibration_bytes": CALIB_BYTES}
+    if workload == "gemv":
+        fetch = {n: mean([v for g, v in fk if int(g) == n]) for n in PROBE_COLS}
+        write = {n: mean([v for g, v in wk if int(g) == n]) for n in PROBE_COLS}
+        rec["algorithmic_bytes"] = {str(n): gemv_bytes(synth.IQ4_NL, 8192, 2560, n) for n in PROBE_COLS}
+        key = f"gemv:{synth.IQ4_NL}:8192x2560"
+    elif workload == "grouped":
+        # dispatch order: for each m, one gu_kernel and one down_kernel per expert set
+        def by_m(lst):
+            per_call = [lst[i][1] + lst[i + 1][1] for i in range(0, len(lst), 2)]
+            c = len(per_call) // len(GROUPED_M)
+            return {m: mean(per_call[i * c:(i + 1) * c]) for i, m in enumerate(GROUPED_M)}
+        fetch, write = by_m(fk), by_m(wk)
+        key = "grouped"
+    else:
+        def per_call(lst):
+            calls, cur = [], 0.0
+            for g, v in lst:
+                cur += v
+                if g == "pf_down_kernel":
+                    calls.append(cur)
+                    cur = 0.0
+            return {"call": mean(calls[1:] or calls)}
+        fetch, write = per_call(fk), per_call(wk)
+        for name in ("pf_gateup_kernel", "pf_down_kernel"):
+            rec[f"{name}_bytes"] = round((mean([v for g, v in fk if g == name]) * ff
+                                          + mean([v for g, v in wk if g == name]) * wf) * 1024)
+        key = "prefill"
+    rec["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
+    rec["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
+    rec["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in fetch}
+    rec["source_sha256"] = source_digest()
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[key] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1)
+    print(json.dumps({key: rec}, indent=1))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,7 +546,13 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--batch-reps", type=int, default=5)
+    ap.add_argument("--pmc-probe", action="store_true", help="launch sequence for the counter runs")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record per-launch HBM bytes from the two counter runs (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): each workload is measured on one "
               "GPU's share; the design notes say how it would shard.", file=sys.stderr)
@@ -364,6 +564,9 @@ def main() -> int:
     import synth
 
     torch.cuda.set_device(0)
+    if args.pmc_probe:
+        pmc_probe(torch, M, args.workload)
+        return 0
     if args.workload == "gemv":
         out = bench_gemv(args, torch, M, synth.IQ4_NL, 8192, 2560, (1, 4, 8), synth.SEEDS["iq4nl_8192x2560"],
                          "µs/call and achieved HBM GB/s, IQ4_NL 8192x2560 GEMV at 1/4/8 columns",
