@@ -87,6 +87,14 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
+// The first product of a chain, dot4(a, b) with a zero accumulator, in the VOP3P form whose third
+// operand is the inline constant 0 (written through the builtin, the zero would be moved into
+// the destination register first for the accumulate-in-place form).
+__device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // ------------------------------------------------------------------ IQ4_NL
 
@@ -109,21 +117,22 @@ struct IQ4Consts {
         return v;
     }
 };
-
-// Four 4-bit indices, one per byte, given as their low 3 bits `i7` and the selector `i8` of the
-// byte-wise choice between the two table halves (byte k = k, or k + 4 when bit 3 is set) ->
-// four int8 levels: two v_perm pick from each half of the table, a third picks per byte.
-__device__ __forceinline__ uint32_t iq4nl_lookup(uint32_t i7, uint32_t i8) {
-    const uint32_t lo = perm(kv_word(1), kv_word(0), i7);
-    const uint32_t hi = perm(kv_word(3), kv_word(2), i7);
-    return perm(hi, lo, i8);
-}
+// ... plus the four signed level words, so they are not re-materialized for every block.
+struct IQ4Levels : IQ4Consts {
+    uint32_t t0, t1, t2, t3;
+    __device__ __forceinline__ IQ4Levels()
+        : t0(opaque_u(kv_word(0))), t1(opaque_u(kv_word(1))), t2(opaque_u(kv_word(2))), t3(opaque_u(kv_word(3))) {}
+};
+struct NoConsts {};
 
 // One dword of IQ4_NL index bytes (elements j..j+3 in the low nibbles, j+16..j+19 in the
-// high nibbles) -> the int8 levels of both element groups (13 VALU).
-__device__ __forceinline__ void iq4nl_decode_word(uint32_t q, uint32_t& lo, uint32_t& hi, const IQ4Consts& k) {
-    lo = iq4nl_lookup(q & k.m7, ((q >> 1) & k.m4) | k.c0123);
-    hi = iq4nl_lookup((q >> 4) & k.m7, ((q >> 5) & k.m4) | k.c0123);
+// high nibbles) -> the int8 levels of both element groups (13 VALU).  Per group of four
+// indices: two v_perm look the low 3 bits up in each half of the level table, a third picks
+// per byte (byte k of the selector = k, or k + 4 when the index's bit 3 is set).
+__device__ __forceinline__ void iq4nl_decode_word(uint32_t q, uint32_t& lo, uint32_t& hi, const IQ4Levels& k) {
+    const uint32_t l7 = q & k.m7, h7 = (q >> 4) & k.m7;
+    lo = perm(perm(k.t3, k.t2, l7), perm(k.t1, k.t0, l7), ((q >> 1) & k.m4) | k.c0123);
+    hi = perm(perm(k.t3, k.t2, h7), perm(k.t1, k.t0, h7), ((q >> 5) & k.m4) | k.c0123);
 }
 
 // ------------------------------------------------------------------ FP16 dequantization
@@ -181,7 +190,7 @@ __device__ __forceinline__ uint32_t realign_scale(uint32_t w0, uint32_t off) { r
 
 template <>
 struct Unit<kQ8_0> {
-    using Consts = IQ4Consts;  // unused
+    using Consts = NoConsts;
     static constexpr int RAW = 9;
     static constexpr int BYTES = 34;
     __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
@@ -192,7 +201,7 @@ struct Unit<kQ8_0> {
         raw[8] = ld32(r, a + 32);
     }
     __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
-                                                  const IQ4Consts&) {
+                                                  const NoConsts&) {
         const uint32_t sel = realign_sel(off);
         dw = realign_scale(raw[0], off);
 #pragma unroll
@@ -203,6 +212,7 @@ struct Unit<kQ8_0> {
 
 template <>
 struct Unit<kIQ4_NL> {
+    using Consts = IQ4Levels;
     static constexpr int RAW = 5;
     static constexpr int BYTES = 18;
     __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
@@ -212,7 +222,7 @@ struct Unit<kIQ4_NL> {
         raw[4] = ld32(r, a + 16);
     }
     __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
-                                                  const IQ4Consts& k) {
+                                                  const IQ4Levels& k) {
         const uint32_t sel = realign_sel(off);
         dw = realign_scale(raw[0], off);
 #pragma unroll
@@ -242,6 +252,7 @@ __device__ __forceinline__ uint32_t cb3_signed(uint32_t g, uint32_t nib) {
 
 template <>
 struct Unit<kCB3> {
+    using Consts = NoConsts;
     static constexpr int RAW = 8;
     // raw: [0..2] qs window, [3..4] signs window, [5] qh byte, [6] scales byte, [7] d
     // `off` = byte offset of the super-block, `ss` = sub-block 0..7.
@@ -276,30 +287,6 @@ struct Unit<kCB3> {
         mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
     }
 };
-
-// ------------------------------------------------------------------ activations in LDS
-//
-// The q8_1 columns of a pass are staged once per workgroup as an int8 plane (32 bytes per
-// block, 16-byte aligned) plus a float plane of the block scales [GP, What changed].
-
-struct ActLds {
-    uint32_t* q;  // [ncols][k/4] dwords
-    float* d;     // [ncols][k/32]
-    int kw;       // k/4
-    int nb;       // k/32
-};
-
-// Copy q8_1 block b of column `src_col` of xq into LDS column c.
-__device__ __forceinline__ void stage_block(rsrc_t xr, uint32_t src_block, ActLds a, int c, int b) {
-    const uint32_t off = src_block * 36u;
-    const uint32_t h = ld32(xr, off);
-    const u32x4 q0 = ld128(xr, off + 4);
-    const u32x4 q1 = ld128(xr, off + 20);
-    uint32_t* dst = a.q + c * a.kw + b * 8;
-    *(u32x4*)dst = q0;
-    *(u32x4*)(dst + 4) = q1;
-    a.d[c * a.nb + b] = h2f(h);
-}
 
 // ------------------------------------------------------------------ q8_1 quantization
 

@@ -10,39 +10,81 @@ namespace qmm {
 constexpr int kGemvLanesPerRow = 16;  // one DPP row (the default row width)
 constexpr int kGemvThreads = 512;     // 8 waves, two per SIMD (the default workgroup)
 constexpr int kGemvRowsPerWG = 32;    // 8 waves x 4 rows
-constexpr int kGemvChunk = 6;         // blocks per lane whose loads are issued together
 constexpr size_t kLdsCap = 65536;     // LDS a workgroup may use
+constexpr int kStageSlots = 4;        // most q8_1 blocks one thread stages
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int WT>
 __host__ __device__ constexpr int row_bytes_dev(int K) {
     return WT == kQ8_0 ? (K / 32) * 34 : WT == kIQ4_NL ? (K / 32) * 18 : (K / 256) * kCB3Bytes;
 }
 
-// LDS of a pass of ncp columns: int8 plane + float scales, plus the CB3 codebook.
-__host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int ncp) {
-    return (size_t)ncp * ((size_t)k + (size_t)(k / 32) * 4) + (wt == kCB3 ? 2048 : 0);
+// ------------------------------------------------------------------ activations in LDS
+//
+// The q8_1 columns of a pass are staged once per workgroup as int8 values plus float block
+// scales [GP, What changed], in the order the readers take them.  Lane l of a row of L lanes
+// takes the blocks s = l + L i of its row, i = 0, 1, ... ("slots"); a kernel instance of pass
+// width NC lays slot i of column c out as
+//   int8   half h (16 bytes) of block l + L i  at  ((i NC + c) 2 + h) 16 L + 16 l
+//   scale  of block l + L i                     at  S + ((i NC/G + c/G) L + l) 4 G + 4 (c mod G)
+// with G = min(NC, 4) and S the size of the int8 area.  A lane then reads every column of a
+// slot at compile-time offsets from one address, and the L lanes of a row read 16 L
+// consecutive bytes per instruction (no bank conflicts; the rows of a wave read the same
+// bytes).  The slot count is the lane's block count rounded up to the chunk U the kernel loads
+// at a time, and blocks past k/32 hold zeros, so every slot a lane computes is defined.
+
+// Slots (blocks per lane) of a row of k values over lpr lanes.
+__host__ __device__ inline int lane_blocks(int64_t k, int lpr) { return (int)((k / 32 + lpr - 1) / lpr); }
+// Slots held in LDS: the lane's blocks rounded up to whole chunks of u.
+__host__ __device__ inline int lds_slots(int64_t k, int lpr, int u) {
+    const int n = lane_blocks(k, lpr);
+    return (n + u - 1) / u * u;
 }
-inline int gemv_max_pass(int wt, int64_t k) {
-    const size_t per = (size_t)k + (size_t)(k / 32) * 4;
-    const size_t fixed = wt == kCB3 ? 2048 : 0;
-    if (kLdsCap < fixed + per) return 0;
-    const int m = (int)((kLdsCap - fixed) / per);
-    return m > 8 ? 8 : m;
+__host__ __device__ inline size_t act_lds_bytes(int64_t k, int nc, int lpr, int u) {
+    return (size_t)lds_slots(k, lpr, u) * (size_t)lpr * (size_t)nc * 36u;
+}
+// LDS of a pass: activations, plus the CB3 codebook.
+__host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int nc, int lpr, int u) {
+    return act_lds_bytes(k, nc, lpr, u) + (wt == kCB3 ? 2048 : 0);
+}
+// Staging slots per thread for ncp columns (1, 2 or 4; 0 when more would be needed): a
+// column's blocks are numbered up to the slot area rounded up to a power of two.
+inline int stage_slots(int64_t k, int ncp, int threads, int lpr, int u) {
+    const int64_t n = (int64_t)ncp * pow2_ceil((int64_t)lds_slots(k, lpr, u) * lpr);
+    return n <= threads ? 1 : n <= 2 * threads ? 2 : n <= 4 * threads ? 4 : 0;
 }
 
-__device__ __forceinline__ ActLds act_lds_layout(uint32_t* lds, int K, int ncp) {
+struct ActLds {
+    uint8_t* base;   // start of the area
+    int nb;          // q8_1 blocks per column (k/32)
+    int nbp;         // blocks per column the area holds (slots x L)
+    uint32_t dbyte;  // byte offset of the scales
+};
+template <int NC, int LPR, int U>
+__device__ __forceinline__ ActLds act_lds_layout(uint32_t* lds, int K) {
     ActLds a;
-    a.kw = K / 4;
+    a.base = (uint8_t*)lds;
     a.nb = K / 32;
-    a.q = lds;
-    a.d = (float*)(lds + ncp * a.kw);
+    a.nbp = lds_slots(K, LPR, U) * LPR;
+    a.dbyte = (uint32_t)a.nbp * (uint32_t)(NC * 32);
     return a;
 }
-__device__ __forceinline__ uint32_t* act_lds_end(ActLds a, int ncp) { return (uint32_t*)(a.d + ncp * a.nb); }
+template <int NC>
+__device__ __forceinline__ uint32_t* act_lds_end(const ActLds& a) {
+    return (uint32_t*)(a.base + a.dbyte + (uint32_t)a.nbp * (uint32_t)(NC * 4));
+}
 
-__device__ __forceinline__ void stage_grid(const uint8_t* grid, uint32_t* lds_grid) {
-    const rsrc_t gr = make_rsrc(grid, 2048);
-    for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_grid[i] = ld32(gr, 4u * i);
+// A lane's view of the area: its int8 and scale addresses of slot 0, column 0.
+struct ActView {
+    const uint8_t* q;
+    const uint8_t* d;
+};
+template <int NC>
+__device__ __forceinline__ ActView act_view(const ActLds& a, int l) {
+    constexpr int G = NC >= 4 ? 4 : NC;
+    return ActView{a.base + 16 * l, a.base + a.dbyte + 4 * G * l};
 }
 
 // The 512-word codebook staged by a workgroup of TH threads (512 / TH words per thread), split
@@ -65,32 +107,35 @@ struct GridStage {
 };
 
 // Activation staging in two halves so that its global loads can be issued before the weight
-// loads and its LDS writes after them: a thread stages up to kStageSlots q8_1 blocks, the pass's
-// (column, block) pairs being numbered column * 2^ceil(log2(blocks)) + block.
-constexpr int kStageSlots = 4;
-
-template <int NS>
+// loads and its LDS writes after them.  A thread stages up to NS q8_1 blocks, the pass's
+// (column, block) pairs being numbered column * 2^lsh + block, 2^lsh >= the area's blocks per
+// column.
+template <int NS, int NC, int LPR>
 struct ActStage {
+    static constexpr int G = NC >= 4 ? 4 : NC;
     uint32_t h[NS];
     u32x4 q0[NS], q1[NS];
-    int lsh;   // log2 of the block count rounded up to a power of two
-    int last;  // last valid (column, block) slot index
+    int lsh;   // log2 of the per-column numbering span
+    int last;  // last (column, block) pair of the pass
 
-    // Slot index i -> column i >> lsh, block i & (2^lsh - 1); indices past the pass or past a
-    // column's blocks are clamped to the pass's last block.  Loads are unconditional so the
-    // code stays straight-line.
+    // Pair index i -> column i >> lsh, block i & (2^lsh - 1); pairs past the pass or past the
+    // area are clamped to the pass's last pair.  Loads are unconditional so the code stays
+    // straight-line.
     __device__ __forceinline__ int slot(int j, const ActLds& act, int ncp) const {
         const int i = (int)threadIdx.x + j * (int)blockDim.x;
         const int c = i >> lsh, b = i & ((1 << lsh) - 1);
-        return (c < ncp && b < act.nb) ? i : last;
+        return (c < ncp && b < act.nbp) ? i : last;
     }
     __device__ __forceinline__ void setup(const ActLds& act, int ncp) {
-        lsh = 32 - __builtin_clz((unsigned)act.nb - 1u);
-        if (act.nb == 1) lsh = 0;
-        last = ((ncp - 1) << lsh) | (act.nb - 1);
+        lsh = 32 - __builtin_clz((unsigned)act.nbp - 1u);  // nbp >= 16
+        last = ((ncp - 1) << lsh) | (act.nbp - 1);
     }
+    // Block b of source column src_col (blocks past the column are read at its last block and
+    // stored as zeros).
     __device__ __forceinline__ void load_slot(rsrc_t xr, const ActLds& act, int j, int src_col, int i) {
-        const uint32_t off = __umul24((uint32_t)(src_col * act.nb + (i & ((1 << lsh) - 1))), 36u);
+        int b = i & ((1 << lsh) - 1);
+        b = b < act.nb ? b : act.nb - 1;
+        const uint32_t off = __umul24((uint32_t)(src_col * act.nb + b), 36u);
         h[j] = ld32(xr, off);
         q0[j] = ld128(xr, off + 4);
         q1[j] = ld128(xr, off + 20);
@@ -117,38 +162,72 @@ struct ActStage {
             load_slot(xr, act, j, col, i);
         }
     }
-    // Unconditional too: a slot past the pass rewrites the pass's last block with the same
-    // bytes (identical values, so the overlapping writes are benign).  Keeping the stores
+    // Unconditional too: a clamped pair rewrites the pass's last pair with the same bytes
+    // (identical values, so the overlapping writes are benign).  Keeping the stores
     // unconditional keeps the loads where they are written (otherwise the compiler sinks them
     // into the store's branch, behind the weight loads).
     __device__ __forceinline__ void store(const ActLds& act, int ncp) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             const int i = slot(j, act, ncp);
-            const int c = i >> lsh, b = i & ((1 << lsh) - 1);
-            uint32_t* dst = act.q + __umul24((uint32_t)c, (uint32_t)act.kw) + b * 8;
-            *(u32x4*)dst = q0[j];
-            *(u32x4*)(dst + 4) = q1[j];
-            act.d[__umul24((uint32_t)c, (uint32_t)act.nb) + b] = h2f(h[j]);
+            const uint32_t c = (uint32_t)(i >> lsh), b = (uint32_t)(i & ((1 << lsh) - 1));
+            const uint32_t si = b / LPR, l = b % LPR;
+            const bool zero = (int)b >= act.nb;
+            uint8_t* dq = act.base + (si * NC + c) * (32u * LPR) + 16u * l;
+            *(u32x4*)dq = zero ? u32x4{0, 0, 0, 0} : q0[j];
+            *(u32x4*)(dq + 16 * LPR) = zero ? u32x4{0, 0, 0, 0} : q1[j];
+            float* dd = (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
+            *dd = zero ? 0.0f : h2f(h[j]);
         }
     }
 };
 
-// One lane's share of one row of LPR lanes: blocks s = l + LPR i, i = 0, 1, ...  U blocks are
-// loaded per chunk; MULTI = the row has more than U blocks per lane (double-buffered chunks),
-// otherwise U is at least the lane's block count.  Loads are unconditional (a block past the
-// row is read at the row's last block and not used), so the code between the loads and their
-// uses stays straight-line and each use waits only for its own load.  NCMIN: columns every pass
-// of this instance has (NC / 2 + 1 for the dense GEMV, whose NC is the smallest of 1, 2, 4, 8
-// that holds the pass; 1 where passes may be narrower).
-template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow, int NCMIN = 1>
+// ------------------------------------------------------------------ the row engine
+//
+// One lane's share of one row of LPR lanes: slots i = 0, 1, ... (blocks s = l + LPR i).  U
+// blocks are loaded per chunk; MULTI = the row has more than U blocks per lane (double-buffered
+// chunks), otherwise U is at least the lane's block count.  Loads are unconditional (a block
+// past the row is read at the row's last block; its activations are zeros and its scale is
+// taken as 0, so it adds nothing), so the code between the loads and their uses stays
+// straight-line and each use waits only for its own load.
+//
+// A pass computes NCP columns, NCP the pass's column count rounded up to a power of two (VAR:
+// one straight-line copy of the code per NCP <= NC, picked once per pass; otherwise NCP = NC).
+// Columns past the pass run on whatever LDS holds there and are never stored.  The columns of a
+// slot are applied in groups of CG; the LDS reads of the next group are issued before the
+// current group's integer dots (a slot's decode sits between the reads of its first group and
+// their use), so LDS latency hides behind VALU work.
+//
+// CG is the widest power of two whose double-buffered activation registers (9 per column), with
+// the raw weight chunks, the decoded block and the accumulators, stay within a budget of VGPRs
+// (about 100 by default, so that two 512-thread workgroups fit a CU).  A budget of 0 reads one
+// column at a time just before its use (for kernels held to 128 registers per lane).
+template <int WT, int NC, int U, bool MULTI, int BUDGET>
+constexpr int pick_cg() {
+    constexpr int fixed = Unit<WT>::RAW * U * (MULTI ? 2 : 1) + 8 + NC;
+    int cg = NC;
+    while (cg > 1 && 18 * cg + fixed > BUDGET) cg /= 2;
+    return cg;
+}
+
+template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow, bool VAR = false,
+          int BUDGET = 100>
 struct RowEngine {
     static constexpr int RAW = Unit<WT>::RAW;
+    static constexpr int CGMAX = pick_cg<WT, NC, U, MULTI, BUDGET>();
+    static constexpr int G = NC >= 4 ? 4 : NC;  // scales per slot group in LDS
+    static constexpr uint32_t kSlotQ = 32u * LPR * NC, kColQ = 32u * LPR, kSlotD = 4u * LPR * NC;
     rsrc_t wr;
     uint32_t row_off;
     int nunits, niter, l16;
     uint32_t A[U][RAW], B[MULTI ? U : 1][RAW];
-    IQ4Consts kc;
+    typename Unit<WT>::Consts kc;
+
+    template <int CG>
+    struct Cols {
+        u32x4 x0[CG], x1[CG];
+        float d[CG];
+    };
 
     __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l_)
         : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + LPR - 1) / LPR), l16(l_) {}
@@ -158,13 +237,13 @@ struct RowEngine {
         if constexpr (WT == kCB3) return row_off + __umul24((uint32_t)(s >> 3), (uint32_t)kCB3Bytes);
         else return row_off + __umul24((uint32_t)s, (uint32_t)Unit<WT>::BYTES);
     }
+    __device__ __forceinline__ int clamp_unit(int s) const { return s < nunits ? s : nunits - 1; }
 
     template <int N>
     __device__ __forceinline__ void load(uint32_t (&buf)[N][RAW], int i0) {
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            int s = l16 + LPR * (i0 + u);
-            s = s < nunits ? s : nunits - 1;
+            const int s = clamp_unit(l16 + LPR * (i0 + u));
             if constexpr (WT == kCB3) Unit<WT>::load(wr, unit_off(s), s & 7, buf[u]);
             else Unit<WT>::load(wr, unit_off(s), buf[u]);
         }
@@ -172,64 +251,127 @@ struct RowEngine {
 
     __device__ __forceinline__ void load_first() { load(A, 0); }
 
-    template <int N>
-    __device__ __forceinline__ void compute(const uint32_t (&buf)[N][RAW], int i0, const ActLds& act, int ncp,
+    // LDS reads of columns g CG .. g CG + CG - 1 of slot i (addresses relative to the chunk's
+    // slot 0)
+    template <int CG>
+    __device__ __forceinline__ static void read_cols(Cols<CG>& a, const uint8_t* q, const uint8_t* d, int i, int g) {
+        constexpr int SG = CG < G ? CG : G;  // scales per read
+#pragma unroll
+        for (int k = 0; k < CG; ++k) {
+            const uint8_t* p = q + i * kSlotQ + (g * CG + k) * kColQ;
+            a.x0[k] = *(const u32x4*)p;
+            a.x1[k] = *(const u32x4*)(p + 16 * LPR);
+        }
+#pragma unroll
+        for (int k = 0; k < CG; k += SG) {
+            const int c = g * CG + k;
+            const uint8_t* p = d + i * kSlotD + (c / G) * (4u * G * LPR) + 4 * (c % G);
+            if constexpr (SG == 4) {
+                const f32x4 v = *(const f32x4*)p;
+                a.d[k] = v.x;
+                a.d[k + 1] = v.y;
+                a.d[k + 2] = v.z;
+                a.d[k + 3] = v.w;
+            } else if constexpr (SG == 2) {
+                const f32x2 v = *(const f32x2*)p;
+                a.d[k] = v.x;
+                a.d[k + 1] = v.y;
+            } else {
+                a.d[k] = *(const float*)p;
+            }
+        }
+    }
+
+    template <int NCP, int N>
+    __device__ __forceinline__ void compute(const uint32_t (&buf)[N][RAW], int i0, const ActView& av, int ncp,
                                             const uint32_t* grid, float (&acc)[NC], int32_t* srow, int64_t scol,
                                             bool row_ok) {
+        constexpr int CG = CGMAX < NCP ? CGMAX : NCP;
+        constexpr int NG = NCP / CG;
+        const uint8_t* q = av.q + (uint32_t)i0 * kSlotQ;
+        const uint8_t* d = av.d + (uint32_t)i0 * kSlotD;
+        constexpr bool kAhead = BUDGET > 0;  // otherwise each group is read just before its use
+        Cols<CG> cols[kAhead ? 2 : 1];
+        if constexpr (kAhead) read_cols<CG>(cols[0], q, d, 0, 0);
+        uint32_t W[8];
+        uint32_t dw = 0;
+        int mult = 1;
 #pragma unroll
-        for (int u = 0; u < N; ++u) {
+        for (int n = 0; n < N * NG; ++n) {
+            const int u = n / NG, g = n % NG;
+            if constexpr (kAhead) {
+                if (n + 1 < N * NG) read_cols<CG>(cols[(n + 1) & 1], q, d, (n + 1) / NG, (n + 1) % NG);
+            } else {
+                read_cols<CG>(cols[0], q, d, u, g);
+            }
             const int s = l16 + LPR * (i0 + u);
-            if (s < nunits) {
-                uint32_t W[8];
-                uint32_t dw;
-                int mult;
-                if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(s), s & 7, grid, W, dw, mult);
-                else Unit<WT>::decode(buf[u], unit_off(s), W, dw, mult, kc);
-                const float dwf = h2f(dw);
-                // Columns below NCMIN always exist in the pass and run straight-line (their LDS
-                // reads can be issued ahead); the others only when the pass has them.
+            if (g == 0) {
+                const int sc = clamp_unit(s);
+                if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
+                else Unit<WT>::decode(buf[u], unit_off(sc), W, dw, mult, kc);
+            }
+            const Cols<CG>& a = cols[kAhead ? (n & 1) : 0];
+            const bool ok = s < nunits;
+            const float dwf = ok ? h2f(dw) : 0.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    if (c >= NCMIN && c >= ncp) continue;
-                    const uint32_t cc = (uint32_t)c;
-                    const uint32_t* a = act.q + __umul24(cc, (uint32_t)act.kw) + s * 8;
-                    const u32x4 a0 = *(const u32x4*)a;
-                    const u32x4 a1 = *(const u32x4*)(a + 4);
-                    int v = dot4(W[0], a0.x, 0);
-                    v = dot4(W[1], a0.y, v);
-                    v = dot4(W[2], a0.z, v);
-                    v = dot4(W[3], a0.w, v);
-                    v = dot4(W[4], a1.x, v);
-                    v = dot4(W[5], a1.y, v);
-                    v = dot4(W[6], a1.z, v);
-                    v = dot4(W[7], a1.w, v);
-                    // |v| < 2^23 and mult <= 31: the 24-bit multiply is exact
-                    const int isum = WT == kCB3 ? __mul24(v, mult) : v;
-                    if constexpr (SUMS) {
-                        if (row_ok) srow[c * scol + s] = isum;
-                    } else {
-                        const float dd = dwf * act.d[__umul24(cc, (uint32_t)act.nb) + s];
-                        acc[c] = __builtin_fmaf(dd, (float)isum, acc[c]);
-                    }
+            for (int k = 0; k < CG; ++k) {
+                const int c = g * CG + k;
+                int v = dot4_first(W[0], a.x0[k].x);
+                v = dot4(W[1], a.x0[k].y, v);
+                v = dot4(W[2], a.x0[k].z, v);
+                v = dot4(W[3], a.x0[k].w, v);
+                v = dot4(W[4], a.x1[k].x, v);
+                v = dot4(W[5], a.x1[k].y, v);
+                v = dot4(W[6], a.x1[k].z, v);
+                v = dot4(W[7], a.x1[k].w, v);
+                // |v| < 2^23 and mult <= 31: the 24-bit multiply is exact
+                const int isum = WT == kCB3 ? __mul24(v, mult) : v;
+                if constexpr (SUMS) {
+                    if (row_ok && ok && c < ncp) srow[c * scol + s] = isum;
+                } else {
+                    acc[c] = __builtin_fmaf(dwf * a.d[k], (float)isum, acc[c]);
+                }
+            }
+            // keeps the reads of later groups from being hoisted here (two buffers at most)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    template <int NCP>
+    __device__ __forceinline__ void run_pass(const ActView& av, int ncp, const uint32_t* grid, float (&acc)[NC],
+                                             int32_t* srow, int64_t scol, bool row_ok) {
+        if constexpr (!MULTI) {
+            compute<NCP>(A, 0, av, ncp, grid, acc, srow, scol, row_ok);
+        } else {
+            for (int i0 = 0; i0 < niter; i0 += 2 * U) {
+                const bool more = i0 + U < niter;
+                if (more) load(B, i0 + U);
+                compute<NCP>(A, i0, av, ncp, grid, acc, srow, scol, row_ok);
+                if (more) {
+                    if (i0 + 2 * U < niter) load(A, i0 + 2 * U);
+                    compute<NCP>(B, i0 + U, av, ncp, grid, acc, srow, scol, row_ok);
                 }
             }
         }
     }
 
     // All of the lane's blocks; the first chunk must already be loaded (load_first).
-    __device__ __forceinline__ void run(const ActLds& act, int ncp, const uint32_t* grid, float (&acc)[NC],
+    __device__ __forceinline__ void run(const ActView& av, int ncp, const uint32_t* grid, float (&acc)[NC],
                                         int32_t* srow, int64_t scol, bool row_ok) {
-        if constexpr (!MULTI) {
-            compute(A, 0, act, ncp, grid, acc, srow, scol, row_ok);
+        if constexpr (!VAR || NC == 1) {
+            run_pass<NC>(av, ncp, grid, acc, srow, scol, row_ok);
         } else {
-            for (int i0 = 0; i0 < niter; i0 += 2 * U) {
-                const bool more = i0 + U < niter;
-                if (more) load(B, i0 + U);
-                compute(A, i0, act, ncp, grid, acc, srow, scol, row_ok);
-                if (more) {
-                    if (i0 + 2 * U < niter) load(A, i0 + 2 * U);
-                    compute(B, i0 + U, act, ncp, grid, acc, srow, scol, row_ok);
+            if (ncp > NC / 2) run_pass<NC>(av, ncp, grid, acc, srow, scol, row_ok);
+            else if constexpr (NC >= 4) {
+                if (ncp > NC / 4) run_pass<NC / 2>(av, ncp, grid, acc, srow, scol, row_ok);
+                else if constexpr (NC >= 8) {
+                    if (ncp > 1) run_pass<2>(av, ncp, grid, acc, srow, scol, row_ok);
+                    else run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
+                } else {
+                    run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
                 }
+            } else {
+                run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
             }
         }
     }
@@ -254,12 +396,12 @@ __device__ __forceinline__ float row_sum(float v) {
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
 // the weights arrive, cross-lane row sums.
 template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
-          int NCMIN = 1>
+          bool VAR = false>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, int col0, int ncp,
                                           float* y, int64_t ldy, int32_t* sums, int row0, uint32_t* lds) {
     static_assert(LPR == 16 || LPR == 64, "a row is one DPP row or one wave");
-    ActLds act = act_lds_layout(lds, K, ncp);
-    uint32_t* lds_grid = act_lds_end(act, ncp);
+    const ActLds act = act_lds_layout<NC, LPR, U>(lds, K);
+    uint32_t* lds_grid = act_lds_end<NC>(act);
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & (LPR - 1);
@@ -268,12 +410,12 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const int rowc = row_ok ? row : nrows - 1;
     const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
 
-    ActStage<NS> stage;
+    ActStage<NS, NC, LPR> stage;
     stage.load(xr, act, col0, ncp);
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
-    RowEngine<WT, NC, SUMS, U, MULTI, LPR, NCMIN> eng(wr, row_off, K, l16);
+    RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
     stage.store(act, ncp);
@@ -289,7 +431,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
         srow = sums + ((int64_t)col0 * nrows + rowc) * act.nb;
         scol = (int64_t)nrows * act.nb;
     }
-    eng.run(act, ncp, lds_grid, acc, srow, scol, row_ok);
+    eng.run(act_view<NC>(act, l16), ncp, lds_grid, acc, srow, scol, row_ok);
     if constexpr (!SUMS) {
         float out = 0.0f;
 #pragma unroll
@@ -301,13 +443,20 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     }
 }
 
-// Blocks per lane of a row of k values (lpr lanes per row).
-inline int lane_blocks(int64_t k, int lpr = kGemvLanesPerRow) { return (int)((k / 32 + lpr - 1) / lpr); }
-
-// Staging slots per thread for a pass of ncp columns of k values.
-inline int stage_slots(int64_t k, int ncp, int threads) {
-    const int64_t n = (int64_t)ncp * pow2_ceil(k / 32);
-    return n <= threads ? 1 : n <= 2 * threads ? 2 : 4;
+// The chunk a kernel instance loads per lane for rows of `lb` blocks per lane: chunks of 2, 3,
+// 5 or 6 (a chunk longer than the lane's count re-reads its last block), double-buffered
+// chunks of `um` beyond 6 (or always, for the block-sum hook).
+struct Chunk {
+    int u;
+    bool multi;
+};
+inline Chunk gemv_chunk(int lb, int lpr, bool sums, int um = 6) {
+    if (sums) return {6, true};
+    if (lb <= 2) return {2, false};
+    if (lpr == 64 && lb <= 3) return {3, false};
+    if (lb <= 5 && lpr != 64) return {5, false};
+    if (lb <= 6) return {6, false};
+    return {um, true};
 }
 
 }  // namespace qmm

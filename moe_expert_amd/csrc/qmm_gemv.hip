@@ -4,9 +4,10 @@
 // Method [IQ, What it does]: every weight block of the call is loaded and decoded once and
 // applied to each column of the pass (1, 2, 4 or 8 columns; passes of 8 beyond 8), with the
 // same integer chain and the same float expression for every column, so each column equals a
-// one-column call bit for bit.  Activations are staged once per workgroup in LDS as an int8
-// plane plus block scales [GP, What changed]; the per-block integer dot is v_dot4_i32_i8;
-// a row's partial sums are combined across its 16 lanes with DPP, no barrier.
+// one-column call bit for bit.  Activations are staged once per workgroup in LDS as int8
+// values plus block scales [GP, What changed], in the order the lanes read them; the
+// per-block integer dot is v_dot4_i32_i8; a row's partial sums are combined across its lanes
+// with DPP, no barrier.
 //
 // Mapping (wave64): 16 lanes per row (one DPP row), 4 rows per wave, 8 waves (32 rows) per
 // workgroup, two waves per SIMD; passes of 1-2 columns use 16-row workgroups (twice as many),
@@ -26,9 +27,8 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                   uint32_t xqbytes, int col0, int ncp, float* __restrict__ y,
                                                   int64_t ldy, int32_t* __restrict__ sums) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    gemv_tile<WT, SUMS, NC, U, MULTI, NS, LPR, TH, NC / 2 + 1>(make_rsrc_dw(w, wbytes), nrows, K, grid,
-                                                               make_rsrc(xq, xqbytes), col0, ncp, y, ldy, sums,
-                                                               blockIdx.x * (TH / LPR), lds);
+    gemv_tile<WT, SUMS, NC, U, MULTI, NS, LPR, TH>(make_rsrc_dw(w, wbytes), nrows, K, grid, make_rsrc(xq, xqbytes),
+                                                   col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
@@ -37,38 +37,40 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
 //   kLong   64 x 512:  8 rows, one row per wave, for rows of more than 96 blocks
 enum GemvShape { kWide, kNarrow, kLong };
 
-// Pick the kernel instance for a pass of ncp columns, `lb` blocks per lane and `ns` staging
-// slots per thread.  Blocks per lane are covered by chunks of 2, 3, 5 or 6 (a chunk longer than
-// the lane's count re-reads its last block), double-buffered chunks of 6 beyond 6.
+// Pick the kernel instance for a pass of NC columns, the chunk `ch` and `ns` staging slots per
+// thread (the same chunk choice as gemv_chunk).
 template <int WT, bool SUMS, int NC, int NS, int LPR, int TH, typename F>
-static void dispatch_u(int lb, F&& go) {
+static void dispatch_u(Chunk ch, F&& go) {
     if constexpr (SUMS) {
         go(gemv_kernel<WT, SUMS, NC, 6, true, NS, LPR, TH>);
-    } else if constexpr (LPR == 64) {
-        if (lb <= 2) go(gemv_kernel<WT, SUMS, NC, 2, false, NS, LPR, TH>);
-        else if (lb <= 3) go(gemv_kernel<WT, SUMS, NC, 3, false, NS, LPR, TH>);
-        else if (lb <= 6) go(gemv_kernel<WT, SUMS, NC, 6, false, NS, LPR, TH>);
-        else go(gemv_kernel<WT, SUMS, NC, 6, true, NS, LPR, TH>);
     } else {
-        if (lb <= 2) go(gemv_kernel<WT, SUMS, NC, 2, false, NS, LPR, TH>);
-        else if (lb <= 5) go(gemv_kernel<WT, SUMS, NC, 5, false, NS, LPR, TH>);
-        else if (lb == 6) go(gemv_kernel<WT, SUMS, NC, 6, false, NS, LPR, TH>);
-        else go(gemv_kernel<WT, SUMS, NC, 6, true, NS, LPR, TH>);
+        if (ch.multi) go(gemv_kernel<WT, SUMS, NC, 6, true, NS, LPR, TH>);
+        else if (ch.u == 2) go(gemv_kernel<WT, SUMS, NC, 2, false, NS, LPR, TH>);
+        else if (LPR == 64 && ch.u == 3) go(gemv_kernel<WT, SUMS, NC, 3, false, NS, LPR, TH>);
+        else if (LPR != 64 && ch.u == 5) go(gemv_kernel<WT, SUMS, NC, 5, false, NS, LPR, TH>);
+        else go(gemv_kernel<WT, SUMS, NC, 6, false, NS, LPR, TH>);
     }
 }
 template <int WT, bool SUMS, int NC, int LPR, int TH, typename F>
-static void dispatch_ns(int ns, int lb, F&& go) {
-    if (ns == 1) dispatch_u<WT, SUMS, NC, 1, LPR, TH>(lb, go);
-    else if (ns == 2) dispatch_u<WT, SUMS, NC, 2, LPR, TH>(lb, go);
-    else dispatch_u<WT, SUMS, NC, 4, LPR, TH>(lb, go);
+static void dispatch_ns(int ns, Chunk ch, F&& go) {
+    if (ns == 1) dispatch_u<WT, SUMS, NC, 1, LPR, TH>(ch, go);
+    else if (ns == 2) dispatch_u<WT, SUMS, NC, 2, LPR, TH>(ch, go);
+    else dispatch_u<WT, SUMS, NC, 4, LPR, TH>(ch, go);
 }
 template <int WT, bool SUMS, int LPR, int TH, typename F>
-static void dispatch_nc(int ncp, int ns, int lb, F&& go) {
-    if (ncp == 1) dispatch_ns<WT, SUMS, 1, LPR, TH>(ns, lb, go);
-    else if (ncp == 2) dispatch_ns<WT, SUMS, 2, LPR, TH>(ns, lb, go);
+static void dispatch_nc(int nc, int ns, Chunk ch, F&& go) {
+    if (nc == 1) dispatch_ns<WT, SUMS, 1, LPR, TH>(ns, ch, go);
+    else if (nc == 2) dispatch_ns<WT, SUMS, 2, LPR, TH>(ns, ch, go);
     else if constexpr (TH == 256) return;  // the narrow shape serves passes of 1-2 columns only
-    else if (ncp <= 4) dispatch_ns<WT, SUMS, 4, LPR, TH>(ns, lb, go);
-    else dispatch_ns<WT, SUMS, 8, LPR, TH>(ns, lb, go);
+    else if (nc == 4) dispatch_ns<WT, SUMS, 4, LPR, TH>(ns, ch, go);
+    else dispatch_ns<WT, SUMS, 8, LPR, TH>(ns, ch, go);
+}
+
+// Lanes per row: one wave per row for rows of more than 96 blocks (not for the block-sum hook).
+static int pass_lpr(bool sums, int64_t k) { return !sums && k / 32 > 96 ? 64 : 16; }
+static Chunk pass_chunk(bool sums, int64_t k) {
+    const int lpr = pass_lpr(sums, k);
+    return gemv_chunk(lane_blocks(k, lpr), lpr, sums);
 }
 
 // The shape of a pass: one wave per row for long rows (enough workgroups and at most a few
@@ -76,35 +78,43 @@ static void dispatch_nc(int ncp, int ns, int lb, F&& go) {
 // staging per workgroup), 32-row workgroups otherwise.  The block-sum hook keeps the default.
 static GemvShape gemv_shape(bool sums, int64_t k, int ncp) {
     if (sums) return kWide;
-    if (k / 32 > 96) return kLong;
-    return ncp <= 2 && (int64_t)ncp * pow2_ceil(k / 32) <= (int64_t)kStageSlots * 256 ? kNarrow : kWide;
+    if (pass_lpr(sums, k) == 64) return kLong;
+    const Chunk ch = pass_chunk(sums, k);
+    return ncp <= 2 && stage_slots(k, ncp, 256, 16, ch.u) != 0 ? kNarrow : kWide;
 }
 static int shape_threads(GemvShape s) { return s == kNarrow ? 256 : 512; }
-static int shape_lpr(GemvShape s) { return s == kLong ? 64 : 16; }
+
+// Widest pass (1, 2, 4 or 8 columns) whose LDS and staging fit a 512-thread workgroup.
+static int gemv_max_pass(int wt, bool sums, int64_t k) {
+    const int lpr = pass_lpr(sums, k);
+    const Chunk ch = pass_chunk(sums, k);
+    for (int nc = 8; nc >= 1; nc /= 2)
+        if (gemv_lds_bytes(wt, k, nc, lpr, ch.u) <= kLdsCap && stage_slots(k, nc, 512, lpr, ch.u) != 0) return nc;
+    return 0;
+}
 
 template <int WT, bool SUMS>
 static int launch_gemv(const void* w, uint64_t wbytes, const uint8_t* grid, int64_t nrows, int64_t k, const void* xq,
                        uint64_t xqbytes, int ncols, float* y, int64_t ldy, int32_t* sums, hipStream_t st) {
-    // widest pass the LDS allows, and at most kStageSlots q8_1 blocks staged per thread
-    // (numbered with the block count rounded up to a power of two) in a 512-thread shape
-    int max_pass = gemv_max_pass(WT, k);
-    const int64_t slot_cap = (int64_t)kStageSlots * 512 / pow2_ceil(k / 32);
-    if (max_pass > slot_cap) max_pass = (int)slot_cap;
+    const int max_pass = gemv_max_pass(WT, SUMS, k);
     if (max_pass < 1) return QMM_EUNSUPPORTED;
+    const int lpr = pass_lpr(SUMS, k);
+    const Chunk ch = pass_chunk(SUMS, k);
     for (int c0 = 0; c0 < ncols; c0 += max_pass) {
         const int ncp = ncols - c0 < max_pass ? ncols - c0 : max_pass;
+        const int nc = (int)pow2_ceil(ncp);
         const GemvShape shape = gemv_shape(SUMS, k, ncp);
-        const int th = shape_threads(shape), lpr = shape_lpr(shape);
+        const int th = shape_threads(shape);
         const dim3 grid_dim((unsigned)((nrows + th / lpr - 1) / (th / lpr)));
-        const size_t lds = gemv_lds_bytes(WT, k, ncp);
+        const size_t lds = gemv_lds_bytes(WT, k, nc, lpr, ch.u);
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid_dim, dim3(th), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows,
                                (int)k, grid, (const uint8_t*)xq, (uint32_t)xqbytes, c0, ncp, y, ldy, sums);
         };
-        const int ns = stage_slots(k, ncp, th), lb = lane_blocks(k, lpr);
-        if (shape == kLong) dispatch_nc<WT, SUMS, 64, 512>(ncp, ns, lb, go);
-        else if (shape == kNarrow) dispatch_nc<WT, SUMS, 16, 256>(ncp, ns, lb, go);
-        else dispatch_nc<WT, SUMS, 16, 512>(ncp, ns, lb, go);
+        const int ns = stage_slots(k, ncp, th, lpr, ch.u);
+        if (shape == kLong) dispatch_nc<WT, SUMS, 64, 512>(nc, ns, ch, go);
+        else if (shape == kNarrow) dispatch_nc<WT, SUMS, 16, 256>(nc, ns, ch, go);
+        else dispatch_nc<WT, SUMS, 16, 512>(nc, ns, ch, go);
         const int rc = launch_status();
         if (rc) return rc;
     }

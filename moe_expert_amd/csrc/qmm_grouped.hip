@@ -42,7 +42,8 @@ struct GroupInfo {
     }
 };
 
-// gate/up workgroup: 1024 threads, 16 waves (4 per SIMD).  Waves 0..7 run the gate rows and
+// gate/up workgroup: 1024 threads, 16 waves (4 per SIMD; 128 registers per lane, so the row
+// engine reads each column's activations just before use).  Waves 0..7 run the gate rows and
 // waves 8..15 the up rows of the 32 intermediate indices of one q8_1 block of H (4 indices per
 // wave, a DPP row of 16 lanes each), so each lane holds one row engine.
 constexpr int kGuThreads = 1024;
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     GroupInfo gi;
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
 
-    ActLds act = act_lds_layout(lds, hidden, kGroupPass);
-    uint32_t* lds_grid = act_lds_end(act, kGroupPass);
+    const ActLds act = act_lds_layout<kGroupPass, kGemvLanesPerRow, U>(lds, hidden);
+    uint32_t* lds_grid = act_lds_end<kGroupPass>(act);
     float* gl = (float*)(lds_grid + (WT == kCB3 ? 512 : 0));  // [8][32] gate sums
     float* ul = gl + kGroupPass * 32;                            // [8][32] up sums
 
@@ -81,10 +82,10 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         // The row engine is rebuilt each pass from values the compiler cannot see through, so
         // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
         // in registers, or spill it, across the whole loop).
-        RowEngine<WT, kGroupPass, false, U, MULTI> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
+        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
                                                        (int)IQ4Consts::opaque_u((uint32_t)l16));
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
-        ActStage<NS> stage;
+        ActStage<NS, kGroupPass, kGemvLanesPerRow> stage;
         stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols);
         GridStage<kGuThreads> gstage;
         if constexpr (WT == kCB3) gstage.load(grid);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         float acc[kGroupPass];
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
-        eng.run(act, ncp, lds_grid, acc, nullptr, 0, true);
+        eng.run(act_view<kGroupPass>(act, l16), ncp, lds_grid, acc, nullptr, 0, true);
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) {
@@ -143,21 +144,21 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
     for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
         if (c0 != gi.k0) __syncthreads();
-        gemv_tile<WT, false, kGroupPass, U, MULTI, NS>(wr, hidden, inter, grid, hr, c0, ncp, y, hidden, nullptr,
-                                                      blockIdx.x * kGemvRowsPerWG, lds);
+        gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kGemvThreads, true>(
+            wr, hidden, inter, grid, hr, c0, ncp, y, hidden, nullptr, blockIdx.x * kGemvRowsPerWG, lds);
     }
 }
 
 // UM: chunk of the double-buffered (MULTI) instance, for rows of more than 6 blocks per lane
-// (3 in the 1024-thread gate/up kernel, whose lanes have 128 registers).
+// (2 in the 1024-thread gate/up kernel, whose lanes have 128 registers).
 template <int WT, int UM = 6, typename F>
-static void dispatch_u_ns(int lb, int ns, F&& go) {
+static void dispatch_u_ns(Chunk ch, int ns, F&& go) {
     auto by_u = [&](auto ns_c) {
         constexpr int NS = decltype(ns_c)::value;
-        if (lb <= 2) go.template operator()<WT, 2, false, NS>();
-        else if (lb <= 5) go.template operator()<WT, 5, false, NS>();
-        else if (lb == 6) go.template operator()<WT, 6, false, NS>();
-        else go.template operator()<WT, UM, true, NS>();
+        if (ch.multi) go.template operator()<WT, UM, true, NS>();
+        else if (ch.u == 2) go.template operator()<WT, 2, false, NS>();
+        else if (ch.u == 5) go.template operator()<WT, 5, false, NS>();
+        else go.template operator()<WT, 6, false, NS>();
     };
     if (ns == 1) by_u(std::integral_constant<int, 1>{});
     else if (ns == 2) by_u(std::integral_constant<int, 2>{});
@@ -176,6 +177,23 @@ struct GroupedArgs {
 };
 
 static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nentries * (size_t)(inter / 32) * 36; }
+
+// Chunks, LDS and staging slots of the two kernels (gate/up: 1024 threads, double-buffered
+// chunks of 2 for long rows; down: 512 threads).
+static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
+static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
+static size_t gu_lds_bytes(int wt, int64_t hidden) {
+    return gemv_lds_bytes(wt, hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u) + 2 * kGroupPass * 32 * sizeof(float);
+}
+static size_t down_lds_bytes(int wt, int64_t inter) {
+    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u);
+}
+static int gu_slots(int64_t hidden) {
+    return stage_slots(hidden, kGroupPass, kGuThreads, kGemvLanesPerRow, gu_chunk(hidden).u);
+}
+static int down_slots(int64_t inter) {
+    return stage_slots(inter, kGroupPass, kGemvThreads, kGemvLanesPerRow, down_chunk(inter).u);
+}
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 static int launch_grouped(const GroupedArgs& a) {
@@ -190,32 +208,34 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     const uint32_t xqbytes = (uint32_t)((uint64_t)a.xq_cols * (a.hidden / 32) * 36);
     {
-        const size_t lds = gemv_lds_bytes(a.wtype_gu, a.hidden, kGroupPass) + 2 * kGroupPass * 32 * sizeof(float);
+        const size_t lds = gu_lds_bytes(a.wtype_gu, a.hidden);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
             hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up,
                                a.gu_stride, gu_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes,
                                a.xq_cols, a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
-        const int lb = lane_blocks(a.hidden), ns = stage_slots(a.hidden, kGroupPass, kGuThreads);
-        if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0, 3>(lb, ns, go);
-        else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL, 3>(lb, ns, go);
-        else dispatch_u_ns<kCB3, 3>(lb, ns, go);
+        const Chunk ch = gu_chunk(a.hidden);
+        const int ns = gu_slots(a.hidden);
+        if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0, 2>(ch, ns, go);
+        else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL, 2>(ch, ns, go);
+        else dispatch_u_ns<kCB3, 2>(ch, ns, go);
         const int rc = launch_status();
         if (rc) return rc;
     }
     {
-        const size_t lds = gemv_lds_bytes(a.wtype_down, a.inter, kGroupPass);
+        const size_t lds = down_lds_bytes(a.wtype_down, a.inter);
         const dim3 grid_dim((unsigned)((a.hidden + kGemvRowsPerWG - 1) / kGemvRowsPerWG), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
             hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGemvThreads), lds, a.st, a.w_down,
                                a.d_stride, d_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.ws,
                                (uint32_t)hbytes, a.group_expert, a.group_off, a.nentries, a.y);
         };
-        const int lb = lane_blocks(a.inter), ns = stage_slots(a.inter, kGroupPass, kGemvThreads);
-        if (a.wtype_down == QMM_Q8_0) dispatch_u_ns<kQ8_0>(lb, ns, go);
-        else if (a.wtype_down == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(lb, ns, go);
-        else dispatch_u_ns<kCB3>(lb, ns, go);
+        const Chunk ch = down_chunk(a.inter);
+        const int ns = down_slots(a.inter);
+        if (a.wtype_down == QMM_Q8_0) dispatch_u_ns<kQ8_0>(ch, ns, go);
+        else if (a.wtype_down == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(ch, ns, go);
+        else dispatch_u_ns<kCB3>(ch, ns, go);
         return launch_status();
     }
 }
@@ -252,10 +272,8 @@ extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const voi
         !aligned(ws, 16))
         return QMM_EALIGN;
     // a pass of 8 entries must fit the workgroup's LDS and staging slots
-    if (gemv_lds_bytes(wtype_gu, hidden, kGroupPass) + 2 * kGroupPass * 32 * 4 > kLdsCap ||
-        gemv_lds_bytes(wtype_down, inter, kGroupPass) > kLdsCap ||
-        (int64_t)kGroupPass * pow2_ceil(hidden / 32) > (int64_t)kStageSlots * kGemvThreads ||
-        (int64_t)kGroupPass * pow2_ceil(inter / 32) > (int64_t)kStageSlots * kGemvThreads)
+    if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
+        gu_slots(hidden) == 0 || down_slots(inter) == 0)
         return QMM_EUNSUPPORTED;
     if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxBufferBytes ||
         grouped_h_bytes(inter, nentries) > kMaxBufferBytes)
