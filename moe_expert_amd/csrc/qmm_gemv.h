@@ -421,6 +421,9 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     stage.store(act, ncp);
     if constexpr (WT == kCB3) gstage.store(lds_grid);
     __syncthreads();
+    // the weight decode stays after the barrier (hoisted above it, each wave would wait for its
+    // first weight block before the workgroup could pass)
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[NC];
 #pragma unroll

@@ -9,10 +9,10 @@
 // per-block integer dot is v_dot4_i32_i8; a row's partial sums are combined across its lanes
 // with DPP, no barrier.
 //
-// Mapping (wave64): 16 lanes per row (one DPP row), 4 rows per wave, 8 waves (32 rows) per
-// workgroup, two waves per SIMD; passes of 1-2 columns use 16-row workgroups (twice as many),
-// rows of more than 96 blocks one row per wave (64 lanes, a DPP row sum and two cross-row
-// shuffles).  Lane l of a row takes the 32-value blocks l, l+L, l+2L, ... of its row (L lanes),
+// Mapping (wave64): 16 lanes per row (one DPP row), 4 rows per wave, 4 waves (16 rows) per
+// workgroup, two workgroups per CU (32-row workgroups of 8 waves where a smaller one cannot
+// stage the pass); rows of more than 96 blocks one row per wave (64 lanes, a DPP row sum and
+// two cross-row shuffles).  Lane l of a row takes the 32-value blocks l, l+L, l+2L, ... of its row (L lanes),
 // so the lanes of a row read consecutive blocks and every weight byte of the matrix is read
 // once per call.  A lane issues the loads of its first chunk of blocks before
 // the activation staging and the barrier, so weight latency and staging overlap; longer rows
@@ -32,8 +32,8 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
-//   kWide   16 x 512: 32 rows, the default
-//   kNarrow 16 x 256: 16 rows, twice the workgroups, for 1-2 column passes
+//   kWide   16 x 512: 32 rows, where 256 threads cannot stage the pass (and the block-sum hook)
+//   kNarrow 16 x 256: 16 rows, the default
 //   kLong   64 x 512:  8 rows, one row per wave, for rows of more than 96 blocks
 enum GemvShape { kWide, kNarrow, kLong };
 
@@ -61,7 +61,6 @@ template <int WT, bool SUMS, int LPR, int TH, typename F>
 static void dispatch_nc(int nc, int ns, Chunk ch, F&& go) {
     if (nc == 1) dispatch_ns<WT, SUMS, 1, LPR, TH>(ns, ch, go);
     else if (nc == 2) dispatch_ns<WT, SUMS, 2, LPR, TH>(ns, ch, go);
-    else if constexpr (TH == 256) return;  // the narrow shape serves passes of 1-2 columns only
     else if (nc == 4) dispatch_ns<WT, SUMS, 4, LPR, TH>(ns, ch, go);
     else dispatch_ns<WT, SUMS, 8, LPR, TH>(ns, ch, go);
 }
@@ -74,13 +73,14 @@ static Chunk pass_chunk(bool sums, int64_t k) {
 }
 
 // The shape of a pass: one wave per row for long rows (enough workgroups and at most a few
-// blocks per lane), 16-row workgroups for passes of 1-2 columns (twice the workgroups, half the
-// staging per workgroup), 32-row workgroups otherwise.  The block-sum hook keeps the default.
+// blocks per lane), otherwise 16-row workgroups where a 256-thread workgroup can stage the pass
+// (twice the workgroups of the 32-row shape: two per CU progress independently and each
+// barrier spans 4 waves), 32-row workgroups beyond.  The block-sum hook keeps the default.
 static GemvShape gemv_shape(bool sums, int64_t k, int ncp) {
     if (sums) return kWide;
     if (pass_lpr(sums, k) == 64) return kLong;
     const Chunk ch = pass_chunk(sums, k);
-    return ncp <= 2 && stage_slots(k, ncp, 256, 16, ch.u) != 0 ? kNarrow : kWide;
+    return stage_slots(k, ncp, 256, 16, ch.u) != 0 ? kNarrow : kWide;
 }
 static int shape_threads(GemvShape s) { return s == kNarrow ? 256 : 512; }
 

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         stage.store(act, ncp);
         if constexpr (WT == kCB3) gstage.store(lds_grid);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
 
         float acc[kGroupPass];
 #pragma unroll
