@@ -49,11 +49,11 @@ __host__ __device__ inline size_t act_lds_bytes(int64_t k, int nc, int lpr, int 
 __host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int nc, int lpr, int u) {
     return act_lds_bytes(k, nc, lpr, u) + (wt == kCB3 ? 2048 : 0);
 }
-// Staging slots per thread for ncp columns (1, 2 or 4; 0 when more would be needed): a
-// column's blocks are numbered up to the slot area rounded up to a power of two.
-inline int stage_slots(int64_t k, int ncp, int threads, int lpr, int u) {
-    const int64_t n = (int64_t)ncp * pow2_ceil((int64_t)lds_slots(k, lpr, u) * lpr);
-    return n <= threads ? 1 : n <= 2 * threads ? 2 : n <= 4 * threads ? 4 : 0;
+// Staging slots per thread for a pass of nc columns (the kernel's pass width): one per q8_1
+// block of the area, 0 when more than kStageSlots would be needed.
+inline int stage_slots(int64_t k, int nc, int threads, int lpr, int u) {
+    const int64_t n = ((int64_t)lds_slots(k, lpr, u) * lpr * nc + threads - 1) / threads;
+    return n <= kStageSlots ? (int)n : 0;
 }
 
 struct ActLds {
@@ -107,77 +107,67 @@ struct GridStage {
 };
 
 // Activation staging in two halves so that its global loads can be issued before the weight
-// loads and its LDS writes after them.  A thread stages up to NS q8_1 blocks, the pass's
-// (column, block) pairs being numbered column * 2^lsh + block, 2^lsh >= the area's blocks per
-// column.
+// loads and its LDS writes after them.  The area's q8_1 blocks ("pairs": a column and a block)
+// are numbered in LDS order, p = (slot NC + column) L + lane, and thread t stages pairs
+// t, t + TH, ... (NS of them).  A pair of a column past the pass or of a block past the row
+// reads from `zero_off`, at or past the end of the buffer, where the hardware returns zeros; a
+// pair index past the area is clamped to its last pair (a second write of the same bytes).
 template <int NS, int NC, int LPR>
 struct ActStage {
     static constexpr int G = NC >= 4 ? 4 : NC;
+    static constexpr int kLogL = LPR == 64 ? 6 : 4;
+    static constexpr int kLogN = NC == 8 ? 3 : NC == 4 ? 2 : NC == 2 ? 1 : 0;
+    static_assert((1 << kLogL) == LPR && (1 << kLogN) == NC, "power-of-two row and pass widths");
     uint32_t h[NS];
     u32x4 q0[NS], q1[NS];
-    int lsh;   // log2 of the per-column numbering span
-    int last;  // last (column, block) pair of the pass
 
-    // Pair index i -> column i >> lsh, block i & (2^lsh - 1); pairs past the pass or past the
-    // area are clamped to the pass's last pair.  Loads are unconditional so the code stays
-    // straight-line.
-    __device__ __forceinline__ int slot(int j, const ActLds& act, int ncp) const {
-        const int i = (int)threadIdx.x + j * (int)blockDim.x;
-        const int c = i >> lsh, b = i & ((1 << lsh) - 1);
-        return (c < ncp && b < act.nbp) ? i : last;
+    __device__ __forceinline__ static int pair(int j, const ActLds& act) {
+        const int p = (int)threadIdx.x + j * (int)blockDim.x;
+        const int last = act.nbp * NC - 1;
+        return p < last ? p : last;
     }
-    __device__ __forceinline__ void setup(const ActLds& act, int ncp) {
-        lsh = 32 - __builtin_clz((unsigned)act.nbp - 1u);  // nbp >= 16
-        last = ((ncp - 1) << lsh) | (act.nbp - 1);
-    }
-    // Block b of source column src_col (blocks past the column are read at its last block and
-    // stored as zeros).
-    __device__ __forceinline__ void load_slot(rsrc_t xr, const ActLds& act, int j, int src_col, int i) {
-        int b = i & ((1 << lsh) - 1);
-        b = b < act.nb ? b : act.nb - 1;
-        const uint32_t off = __umul24((uint32_t)(src_col * act.nb + b), 36u);
+    __device__ __forceinline__ static int pair_col(int p) { return (p >> kLogL) & (NC - 1); }
+    __device__ __forceinline__ static int pair_block(int p) { return ((p >> (kLogL + kLogN)) << kLogL) | (p & (LPR - 1)); }
+
+    __device__ __forceinline__ void load_block(rsrc_t xr, const ActLds& act, int j, int src_col, bool ok, int b,
+                                               uint32_t zero_off) {
+        const uint32_t off = ok ? __umul24((uint32_t)(src_col * act.nb + b), 36u) : zero_off;
         h[j] = ld32(xr, off);
         q0[j] = ld128(xr, off + 4);
         q1[j] = ld128(xr, off + 20);
     }
-    // Columns col0 .. col0 + ncp - 1 of the activations.
-    __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp) {
-        setup(act, ncp);
+    // Columns col0 .. col0 + ncp - 1 of the activations (zero_off: the buffer's size).
+    __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp, uint32_t zero_off) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const int i = slot(j, act, ncp);
-            load_slot(xr, act, j, col0 + (i >> lsh), i);
+            const int p = pair(j, act), c = pair_col(p), b = pair_block(p);
+            load_block(xr, act, j, col0 + c, c < ncp && b < act.nb, b, zero_off);
         }
     }
     // Pass column c taken from activation column entry_col[c0 + c]; a column outside
-    // [0, ncols) reads the zeros past the end of the activations.
+    // [0, ncols) reads zeros as well (zero_off: the buffer's size).
     __device__ __forceinline__ void load_entries(rsrc_t xr, const ActLds& act, int ncp, const int32_t* entry_col, int c0,
-                                                 int ncols) {
-        setup(act, ncp);
+                                                 int ncols, uint32_t zero_off) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const int i = slot(j, act, ncp);
-            int col = entry_col[c0 + (i >> lsh)];
-            col = (col >= 0 && col < ncols) ? col : ncols;
-            load_slot(xr, act, j, col, i);
+            const int p = pair(j, act), c = pair_col(p), b = pair_block(p);
+            const int col = entry_col[c0 + (c < ncp ? c : 0)];
+            load_block(xr, act, j, col, c < ncp && b < act.nb && col >= 0 && col < ncols, b, zero_off);
         }
     }
-    // Unconditional too: a clamped pair rewrites the pass's last pair with the same bytes
-    // (identical values, so the overlapping writes are benign).  Keeping the stores
-    // unconditional keeps the loads where they are written (otherwise the compiler sinks them
-    // into the store's branch, behind the weight loads).
-    __device__ __forceinline__ void store(const ActLds& act, int ncp) {
+    // Unconditional too: keeping the stores unconditional keeps the loads where they are
+    // written (otherwise the compiler sinks them into the store's branch, behind the weight
+    // loads).
+    __device__ __forceinline__ void store(const ActLds& act) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const int i = slot(j, act, ncp);
-            const uint32_t c = (uint32_t)(i >> lsh), b = (uint32_t)(i & ((1 << lsh) - 1));
-            const uint32_t si = b / LPR, l = b % LPR;
-            const bool zero = (int)b >= act.nb;
-            uint8_t* dq = act.base + (si * NC + c) * (32u * LPR) + 16u * l;
-            *(u32x4*)dq = zero ? u32x4{0, 0, 0, 0} : q0[j];
-            *(u32x4*)(dq + 16 * LPR) = zero ? u32x4{0, 0, 0, 0} : q1[j];
+            const uint32_t p = (uint32_t)pair(j, act);
+            const uint32_t c = (uint32_t)pair_col((int)p), l = p & (LPR - 1), si = p >> (kLogL + kLogN);
+            uint8_t* dq = act.base + 16u * (p + (p & ~(uint32_t)(LPR - 1)));  // (si NC + c) 32 L + 16 l
+            *(u32x4*)dq = q0[j];
+            *(u32x4*)(dq + 16 * LPR) = q1[j];
             float* dd = (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
-            *dd = zero ? 0.0f : h2f(h[j]);
+            *dd = h2f(h[j]);
         }
     }
 };
@@ -390,15 +380,17 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 
 // One workgroup's TH / 64 * (64 / LPR) rows starting at row0 of a decode GEMV pass: columns
-// [col0, col0 + ncp) of the q8_1 activations behind `xr` (column c is q8_1 blocks c*K/32 ...),
+// [col0, col0 + ncp) of the q8_1 activations behind `xr` (xbytes long; column c is q8_1 blocks
+// c*K/32 ...),
 // results to y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  LPR lanes per
 // row (16 or 64).  Order of work: activation loads, then this lane's weight loads, then the
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
 // the weights arrive, cross-lane row sums.
 template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
           bool VAR = false>
-__device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, int col0, int ncp,
-                                          float* y, int64_t ldy, int32_t* sums, int row0, uint32_t* lds) {
+__device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, uint32_t xbytes,
+                                          int col0, int ncp, float* y, int64_t ldy, int32_t* sums, int row0,
+                                          uint32_t* lds) {
     static_assert(LPR == 16 || LPR == 64, "a row is one DPP row or one wave");
     const ActLds act = act_lds_layout<NC, LPR, U>(lds, K);
     uint32_t* lds_grid = act_lds_end<NC>(act);
@@ -411,14 +403,14 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
 
     ActStage<NS, NC, LPR> stage;
-    stage.load(xr, act, col0, ncp);
+    stage.load(xr, act, col0, ncp, xbytes);
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
     RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
-    stage.store(act, ncp);
+    stage.store(act);
     if constexpr (WT == kCB3) gstage.store(lds_grid);
     __syncthreads();
     // the weight decode stays after the barrier (hoisted above it, each wave would wait for its

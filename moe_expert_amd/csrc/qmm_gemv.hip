@@ -28,7 +28,7 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                   int64_t ldy, int32_t* __restrict__ sums) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     gemv_tile<WT, SUMS, NC, U, MULTI, NS, LPR, TH>(make_rsrc_dw(w, wbytes), nrows, K, grid, make_rsrc(xq, xqbytes),
-                                                   col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
+                                                   xqbytes, col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
@@ -55,6 +55,7 @@ template <int WT, bool SUMS, int NC, int LPR, int TH, typename F>
 static void dispatch_ns(int ns, Chunk ch, F&& go) {
     if (ns == 1) dispatch_u<WT, SUMS, NC, 1, LPR, TH>(ch, go);
     else if (ns == 2) dispatch_u<WT, SUMS, NC, 2, LPR, TH>(ch, go);
+    else if (ns == 3) dispatch_u<WT, SUMS, NC, 3, LPR, TH>(ch, go);
     else dispatch_u<WT, SUMS, NC, 4, LPR, TH>(ch, go);
 }
 template <int WT, bool SUMS, int LPR, int TH, typename F>
@@ -80,7 +81,7 @@ static GemvShape gemv_shape(bool sums, int64_t k, int ncp) {
     if (sums) return kWide;
     if (pass_lpr(sums, k) == 64) return kLong;
     const Chunk ch = pass_chunk(sums, k);
-    return stage_slots(k, ncp, 256, 16, ch.u) != 0 ? kNarrow : kWide;
+    return stage_slots(k, (int)pow2_ceil(ncp), 256, 16, ch.u) != 0 ? kNarrow : kWide;
 }
 static int shape_threads(GemvShape s) { return s == kNarrow ? 256 : 512; }
 
@@ -111,7 +112,7 @@ static int launch_gemv(const void* w, uint64_t wbytes, const uint8_t* grid, int6
             hipLaunchKernelGGL(kern, grid_dim, dim3(th), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows,
                                (int)k, grid, (const uint8_t*)xq, (uint32_t)xqbytes, c0, ncp, y, ldy, sums);
         };
-        const int ns = stage_slots(k, ncp, th, lpr, ch.u);
+        const int ns = stage_slots(k, nc, th, lpr, ch.u);
         if (shape == kLong) dispatch_nc<WT, SUMS, 64, 512>(nc, ns, ch, go);
         else if (shape == kNarrow) dispatch_nc<WT, SUMS, 16, 256>(nc, ns, ch, go);
         else dispatch_nc<WT, SUMS, 16, 512>(nc, ns, ch, go);
@@ -131,7 +132,7 @@ static int check_gemv_args(int wtype, const void* w, const uint8_t* grid, int64_
     if (!aligned(w, 4) || !aligned(xq, 4) || !aligned(out, 4)) return QMM_EALIGN;
     *wbytes = (uint64_t)nrows * (uint64_t)qmm_row_bytes(wtype, k);
     *xqbytes = (uint64_t)ncols * (uint64_t)(k / 32) * 36u;
-    if (*wbytes > kMaxBufferBytes || *xqbytes > kMaxBufferBytes) return QMM_EUNSUPPORTED;
+    if (*wbytes > kMaxBufferBytes || *xqbytes > kMaxActBytes) return QMM_EUNSUPPORTED;
     return QMM_OK;
 }
 

@@ -86,13 +86,13 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
                                                        (int)IQ4Consts::opaque_u((uint32_t)l16));
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
         ActStage<NS, kGroupPass, kGemvLanesPerRow> stage;
-        stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols);
+        stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
         GridStage<kGuThreads> gstage;
         if constexpr (WT == kCB3) gstage.load(grid);
         __builtin_amdgcn_sched_barrier(0);
         eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
         __builtin_amdgcn_sched_barrier(0);
-        stage.store(act, ncp);
+        stage.store(act);
         if constexpr (WT == kCB3) gstage.store(lds_grid);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
         if (c0 != gi.k0) __syncthreads();
         gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kGemvThreads, true>(
-            wr, hidden, inter, grid, hr, c0, ncp, y, hidden, nullptr, blockIdx.x * kGemvRowsPerWG, lds);
+            wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kGemvRowsPerWG, lds);
     }
 }
 
@@ -163,6 +163,7 @@ static void dispatch_u_ns(Chunk ch, int ns, F&& go) {
     };
     if (ns == 1) by_u(std::integral_constant<int, 1>{});
     else if (ns == 2) by_u(std::integral_constant<int, 2>{});
+    else if (ns == 3) by_u(std::integral_constant<int, 3>{});
     else by_u(std::integral_constant<int, 4>{});
 }
 
@@ -276,8 +277,7 @@ extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const voi
     if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
         gu_slots(hidden) == 0 || down_slots(inter) == 0)
         return QMM_EUNSUPPORTED;
-    if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxBufferBytes ||
-        grouped_h_bytes(inter, nentries) > kMaxBufferBytes)
+    if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxActBytes || grouped_h_bytes(inter, nentries) > kMaxActBytes)
         return QMM_EUNSUPPORTED;
     if (ws_bytes < qgemv_grouped_experts_workspace(inter, nentries, flags)) return QMM_ESPACE;
     if (ngroups == 0 || nentries == 0) return QMM_OK;

@@ -31,5 +31,8 @@ inline int64_t pow2_ceil(int64_t v) {
     return p;
 }
 constexpr uint64_t kMaxBufferBytes = 0xFFFFFFFFull;  // raw-buffer record range (32-bit offsets)
+// Activation buffers: the kernels read zeros at their end (offset = size, plus up to 36 bytes),
+// which must not wrap the 32-bit offset.
+constexpr uint64_t kMaxActBytes = 0xFFFFFF00ull;
 
 }  // namespace qmm
