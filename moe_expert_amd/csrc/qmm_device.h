@@ -334,14 +334,43 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15); every lane of the row gets the same
-// value (each step adds a lane's value to its partner's, so partners compute identical sums).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x140>(v);  // row_mirror
-    return v;
+// Lane l (of a 16-lane DPP row) pairs with lane l ^ m in the four steps m = 15, 7, 2, 1
+// (row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]).  One step adds the
+// value a lane keeps to the value its partner sends.  With NC per-lane partials (NC = 1, 2, 4,
+// 8), the first log2 NC steps also halve the values a lane holds: the lanes whose bit 3 (then
+// 2, then 1) is set keep the upper half of the columns, the partner the lower half.  Each
+// column's sum is then the same addition tree whatever NC (partners add the same two values,
+// in either order), and lane l ends with the sum over the row of column row_col<NC>(l).
+template <int NC>
+__device__ __forceinline__ int row_col(int l) {
+    return NC == 8 ? (l >> 1) & 7 : NC == 4 ? (l >> 2) & 3 : NC == 2 ? (l >> 3) & 1 : 0;
+}
+template <int CTRL, int N>
+__device__ __forceinline__ void row_step(float (&a)[8], bool upper) {
+    if constexpr (N == 1) {
+        a[0] += dpp<CTRL>(a[0]);
+    } else {
+        float keep[N / 2], send[N / 2];
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            keep[k] = upper ? a[k + N / 2] : a[k];
+            send[k] = upper ? a[k] : a[k + N / 2];
+        }
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) a[k] = keep[k] + dpp<CTRL>(send[k]);
+    }
+}
+template <int NC>
+__device__ __forceinline__ float row16_sums(const float (&acc)[NC], int l) {
+    static_assert(NC == 1 || NC == 2 || NC == 4 || NC == 8, "1, 2, 4 or 8 columns");
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) a[c] = acc[c];
+    row_step<0x140, NC>(a, (l & 8) != 0);
+    row_step<0x141, (NC >= 2 ? NC / 2 : 1)>(a, (l & 4) != 0);
+    row_step<0x4E, (NC >= 4 ? NC / 4 : 1)>(a, (l & 2) != 0);
+    row_step<0xB1, 1>(a, false);
+    return a[0];
 }
 
 }  // namespace qmm

@@ -367,11 +367,11 @@ struct RowEngine {
     }
 };
 
-// Sum over the LPR lanes of a row (16: one DPP row; 64: the wave); every lane of the row gets
-// the same value, added in the same order for every column.
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-    v = row16_sum(v);
+// Sums over the LPR lanes of a row (16: one DPP row; 64: the wave, whose four DPP rows are then
+// added across) of the NC per-lane partials: lane l ends with column row_col<NC>(l mod 16).
+template <int NC, int LPR>
+__device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
+    float v = row16_sums<NC>(acc, l & 15);
     if constexpr (LPR == 64) {
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
@@ -428,13 +428,11 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     }
     eng.run(act_view<NC>(act, l16), ncp, lds_grid, acc, srow, scol, row_ok);
     if constexpr (!SUMS) {
-        float out = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const float s = row_sum<LPR>(acc[c]);
-            if (l16 == c) out = s;
-        }
-        if (row_ok && l16 < ncp) y[(int64_t)(col0 + l16) * ldy + row] = out;
+        const float s = row_sums<NC, LPR>(acc, l16);
+        const int c = row_col<NC>(l16 & 15);
+        // one lane per column: the lowest of the lanes holding it, in the row's first 16 lanes
+        const bool writer = (l16 & (16 / NC - 1)) == 0 && l16 < 16;
+        if (row_ok && writer && c < ncp) y[(int64_t)(col0 + c) * ldy + row] = s;
     }
 }
 

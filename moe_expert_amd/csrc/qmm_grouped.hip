@@ -101,15 +101,11 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
         eng.run(act_view<kGroupPass>(act, l16), ncp, lds_grid, acc, nullptr, 0, true);
-        float sum = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kGroupPass; ++c) {
-            const float sc = row16_sum(acc[c]);
-            if (l16 == c) sum = sc;
-        }
-        if (l16 < ncp) {
-            sums[l16 * 32 + rg] = sum;
-            if (dbg) dbg[(int64_t)(c0 + l16) * inter + i] = sum;
+        const float sum = row16_sums<kGroupPass>(acc, l16);
+        const int c = row_col<kGroupPass>(l16);
+        if ((l16 & 1) == 0 && c < ncp) {
+            sums[c * 32 + rg] = sum;
+            if (dbg) dbg[(int64_t)(c0 + c) * inter + i] = sum;
         }
         __syncthreads();
         // SwiGLU -> q8_1: one half wave per entry (waves 0..3), value j = intermediate 32t + j
