@@ -42,38 +42,39 @@ __host__ __device__ inline int lds_slots(int64_t k, int lpr, int u) {
     const int n = lane_blocks(k, lpr);
     return (n + u - 1) / u * u;
 }
-__host__ __device__ inline size_t act_lds_bytes(int64_t k, int nc, int lpr, int u) {
-    return (size_t)lds_slots(k, lpr, u) * (size_t)lpr * (size_t)nc * 36u;
-}
-// LDS of a pass: activations, plus the CB3 codebook.
-__host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int nc, int lpr, int u) {
-    return act_lds_bytes(k, nc, lpr, u) + (wt == kCB3 ? 2048 : 0);
-}
-// Staging slots per thread for a pass of nc columns (the kernel's pass width): one per q8_1
-// block of the area, 0 when more than kStageSlots would be needed.
-inline int stage_slots(int64_t k, int nc, int threads, int lpr, int u) {
+// Staging slots per thread for a pass of nc columns (the kernel's pass width) in a workgroup of
+// `threads`: the lanes' slots, for every column, spread over the threads; 0 when more than
+// kStageSlots would be needed (or the workgroup is narrower than a slot of the pass).
+__host__ __device__ inline int stage_slots(int64_t k, int nc, int threads, int lpr, int u) {
+    if (threads % (nc * lpr) != 0) return 0;
     const int64_t n = ((int64_t)lds_slots(k, lpr, u) * lpr * nc + threads - 1) / threads;
     return n <= kStageSlots ? (int)n : 0;
+}
+// The area holds every q8_1 block the threads stage: slots x threads blocks of 36 bytes.
+__host__ __device__ inline size_t act_lds_bytes(int64_t k, int nc, int lpr, int u, int threads) {
+    return (size_t)stage_slots(k, nc, threads, lpr, u) * (size_t)threads * 36u;
+}
+// LDS of a pass: activations, plus the CB3 codebook.
+__host__ __device__ inline size_t gemv_lds_bytes(int wt, int64_t k, int nc, int lpr, int u, int threads) {
+    return act_lds_bytes(k, nc, lpr, u, threads) + (wt == kCB3 ? 2048 : 0);
 }
 
 struct ActLds {
     uint8_t* base;   // start of the area
     int nb;          // q8_1 blocks per column (k/32)
-    int nbp;         // blocks per column the area holds (slots x L)
     uint32_t dbyte;  // byte offset of the scales
 };
-template <int NC, int LPR, int U>
+template <int NC, int NS, int TH>
 __device__ __forceinline__ ActLds act_lds_layout(uint32_t* lds, int K) {
     ActLds a;
     a.base = (uint8_t*)lds;
     a.nb = K / 32;
-    a.nbp = lds_slots(K, LPR, U) * LPR;
-    a.dbyte = (uint32_t)a.nbp * (uint32_t)(NC * 32);
+    a.dbyte = (uint32_t)(NS * TH * 32);
     return a;
 }
-template <int NC>
+template <int NS, int TH>
 __device__ __forceinline__ uint32_t* act_lds_end(const ActLds& a) {
-    return (uint32_t*)(a.base + a.dbyte + (uint32_t)a.nbp * (uint32_t)(NC * 4));
+    return (uint32_t*)(a.base + NS * TH * 36);
 }
 
 // A lane's view of the area: its int8 and scale addresses of slot 0, column 0.
@@ -109,65 +110,63 @@ struct GridStage {
 // Activation staging in two halves so that its global loads can be issued before the weight
 // loads and its LDS writes after them.  The area's q8_1 blocks ("pairs": a column and a block)
 // are numbered in LDS order, p = (slot NC + column) L + lane, and thread t stages pairs
-// t, t + TH, ... (NS of them).  A pair of a column past the pass or of a block past the row
-// reads from `zero_off`, at or past the end of the buffer, where the hardware returns zeros; a
-// pair index past the area is clamped to its last pair (a second write of the same bytes).
-template <int NS, int NC, int LPR>
+// t, t + TH, ... (NS of them).  TH is a multiple of NC L, so a thread keeps its column and lane
+// in every slot it stages and its pairs lie a constant number of slots apart: their sources and
+// destinations differ by constants.  A pair of a column past the pass or of a block past the row
+// reads from `zero_off`, at or past the end of the buffer, where the hardware returns zeros.
+template <int NS, int NC, int LPR, int TH>
 struct ActStage {
     static constexpr int G = NC >= 4 ? 4 : NC;
     static constexpr int kLogL = LPR == 64 ? 6 : 4;
     static constexpr int kLogN = NC == 8 ? 3 : NC == 4 ? 2 : NC == 2 ? 1 : 0;
     static_assert((1 << kLogL) == LPR && (1 << kLogN) == NC, "power-of-two row and pass widths");
+    static_assert(TH % (NC * LPR) == 0, "the workgroup covers whole slots");
+    static constexpr int kStep = TH / (NC * LPR) * LPR;  // blocks between a thread's pairs
     uint32_t h[NS];
     u32x4 q0[NS], q1[NS];
 
-    __device__ __forceinline__ static int pair(int j, const ActLds& act) {
-        const int p = (int)threadIdx.x + j * (int)blockDim.x;
-        const int last = act.nbp * NC - 1;
-        return p < last ? p : last;
+    __device__ __forceinline__ static int col() { return ((int)threadIdx.x >> kLogL) & (NC - 1); }
+    __device__ __forceinline__ static int block0() {
+        return (((int)threadIdx.x >> (kLogL + kLogN)) << kLogL) | ((int)threadIdx.x & (LPR - 1));
     }
-    __device__ __forceinline__ static int pair_col(int p) { return (p >> kLogL) & (NC - 1); }
-    __device__ __forceinline__ static int pair_block(int p) { return ((p >> (kLogL + kLogN)) << kLogL) | (p & (LPR - 1)); }
-
-    __device__ __forceinline__ void load_block(rsrc_t xr, const ActLds& act, int j, int src_col, bool ok, int b,
-                                               uint32_t zero_off) {
-        const uint32_t off = ok ? __umul24((uint32_t)(src_col * act.nb + b), 36u) : zero_off;
-        h[j] = ld32(xr, off);
-        q0[j] = ld128(xr, off + 4);
-        q1[j] = ld128(xr, off + 20);
+    // q8_1 block `base` of the buffer and the blocks kStep, 2 kStep, ... after it (pair j is
+    // block b0 + j kStep of its column, read when ok and b0 + j kStep < nb)
+    __device__ __forceinline__ void load_blocks(rsrc_t xr, const ActLds& act, uint32_t base, int b0, bool ok,
+                                                uint32_t zero_off) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const uint32_t off = (ok && b0 + j * kStep < act.nb) ? __umul24(base, 36u) + 36u * kStep * j : zero_off;
+            h[j] = ld32(xr, off);
+            q0[j] = ld128(xr, off + 4);
+            q1[j] = ld128(xr, off + 20);
+        }
     }
     // Columns col0 .. col0 + ncp - 1 of the activations (zero_off: the buffer's size).
     __device__ __forceinline__ void load(rsrc_t xr, const ActLds& act, int col0, int ncp, uint32_t zero_off) {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int p = pair(j, act), c = pair_col(p), b = pair_block(p);
-            load_block(xr, act, j, col0 + c, c < ncp && b < act.nb, b, zero_off);
-        }
+        const int c = col(), b0 = block0();
+        load_blocks(xr, act, (uint32_t)((col0 + c) * act.nb + b0), b0, c < ncp, zero_off);
     }
     // Pass column c taken from activation column entry_col[c0 + c]; a column outside
     // [0, ncols) reads zeros as well (zero_off: the buffer's size).
     __device__ __forceinline__ void load_entries(rsrc_t xr, const ActLds& act, int ncp, const int32_t* entry_col, int c0,
                                                  int ncols, uint32_t zero_off) {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int p = pair(j, act), c = pair_col(p), b = pair_block(p);
-            const int col = entry_col[c0 + (c < ncp ? c : 0)];
-            load_block(xr, act, j, col, c < ncp && b < act.nb && col >= 0 && col < ncols, b, zero_off);
-        }
+        const int c = col(), b0 = block0();
+        const int src = entry_col[c0 + (c < ncp ? c : 0)];
+        const bool ok = c < ncp && src >= 0 && src < ncols;
+        load_blocks(xr, act, (uint32_t)((ok ? src : 0) * act.nb + b0), b0, ok, zero_off);
     }
     // Unconditional too: keeping the stores unconditional keeps the loads where they are
     // written (otherwise the compiler sinks them into the store's branch, behind the weight
     // loads).
     __device__ __forceinline__ void store(const ActLds& act) {
+        const uint32_t t = threadIdx.x, c = (uint32_t)col(), l = t & (LPR - 1), si = t >> (kLogL + kLogN);
+        uint8_t* dq = act.base + 16u * (t + (t & ~(uint32_t)(LPR - 1)));  // (si NC + c) 32 L + 16 l
+        float* dd = (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const uint32_t p = (uint32_t)pair(j, act);
-            const uint32_t c = (uint32_t)pair_col((int)p), l = p & (LPR - 1), si = p >> (kLogL + kLogN);
-            uint8_t* dq = act.base + 16u * (p + (p & ~(uint32_t)(LPR - 1)));  // (si NC + c) 32 L + 16 l
-            *(u32x4*)dq = q0[j];
-            *(u32x4*)(dq + 16 * LPR) = q1[j];
-            float* dd = (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
-            *dd = h2f(h[j]);
+            *(u32x4*)(dq + 32 * TH * j) = q0[j];
+            *(u32x4*)(dq + 32 * TH * j + 16 * LPR) = q1[j];
+            dd[TH * j] = h2f(h[j]);
         }
     }
 };
@@ -392,8 +391,8 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
                                           int col0, int ncp, float* y, int64_t ldy, int32_t* sums, int row0,
                                           uint32_t* lds) {
     static_assert(LPR == 16 || LPR == 64, "a row is one DPP row or one wave");
-    const ActLds act = act_lds_layout<NC, LPR, U>(lds, K);
-    uint32_t* lds_grid = act_lds_end<NC>(act);
+    const ActLds act = act_lds_layout<NC, NS, TH>(lds, K);
+    uint32_t* lds_grid = act_lds_end<NS, TH>(act);
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & (LPR - 1);
@@ -402,7 +401,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const int rowc = row_ok ? row : nrows - 1;
     const uint32_t row_off = (uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K);
 
-    ActStage<NS, NC, LPR> stage;
+    ActStage<NS, NC, LPR, TH> stage;
     stage.load(xr, act, col0, ncp, xbytes);
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);

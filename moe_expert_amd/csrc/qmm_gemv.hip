@@ -73,24 +73,28 @@ static Chunk pass_chunk(bool sums, int64_t k) {
     return gemv_chunk(lane_blocks(k, lpr), lpr, sums);
 }
 
+// Whether a workgroup of `th` threads can stage a pass of nc columns within the LDS budget.
+static bool shape_fits(int wt, int64_t k, int nc, int th, int lpr, Chunk ch) {
+    return stage_slots(k, nc, th, lpr, ch.u) != 0 && gemv_lds_bytes(wt, k, nc, lpr, ch.u, th) <= kLdsCap;
+}
+
 // The shape of a pass: one wave per row for long rows (enough workgroups and at most a few
 // blocks per lane), otherwise 16-row workgroups where a 256-thread workgroup can stage the pass
 // (twice the workgroups of the 32-row shape: two per CU progress independently and each
 // barrier spans 4 waves), 32-row workgroups beyond.  The block-sum hook keeps the default.
-static GemvShape gemv_shape(bool sums, int64_t k, int ncp) {
+static GemvShape gemv_shape(int wt, bool sums, int64_t k, int ncp) {
     if (sums) return kWide;
     if (pass_lpr(sums, k) == 64) return kLong;
-    const Chunk ch = pass_chunk(sums, k);
-    return stage_slots(k, (int)pow2_ceil(ncp), 256, 16, ch.u) != 0 ? kNarrow : kWide;
+    return shape_fits(wt, k, (int)pow2_ceil(ncp), 256, 16, pass_chunk(sums, k)) ? kNarrow : kWide;
 }
 static int shape_threads(GemvShape s) { return s == kNarrow ? 256 : 512; }
 
-// Widest pass (1, 2, 4 or 8 columns) whose LDS and staging fit a 512-thread workgroup.
+// Widest pass (1, 2, 4 or 8 columns) that one of the shapes can stage.
 static int gemv_max_pass(int wt, bool sums, int64_t k) {
     const int lpr = pass_lpr(sums, k);
     const Chunk ch = pass_chunk(sums, k);
     for (int nc = 8; nc >= 1; nc /= 2)
-        if (gemv_lds_bytes(wt, k, nc, lpr, ch.u) <= kLdsCap && stage_slots(k, nc, 512, lpr, ch.u) != 0) return nc;
+        if (shape_fits(wt, k, nc, 512, lpr, ch) || (!sums && lpr == 16 && shape_fits(wt, k, nc, 256, lpr, ch))) return nc;
     return 0;
 }
 
@@ -104,10 +108,10 @@ static int launch_gemv(const void* w, uint64_t wbytes, const uint8_t* grid, int6
     for (int c0 = 0; c0 < ncols; c0 += max_pass) {
         const int ncp = ncols - c0 < max_pass ? ncols - c0 : max_pass;
         const int nc = (int)pow2_ceil(ncp);
-        const GemvShape shape = gemv_shape(SUMS, k, ncp);
+        const GemvShape shape = gemv_shape(WT, SUMS, k, ncp);
         const int th = shape_threads(shape);
         const dim3 grid_dim((unsigned)((nrows + th / lpr - 1) / (th / lpr)));
-        const size_t lds = gemv_lds_bytes(WT, k, nc, lpr, ch.u);
+        const size_t lds = gemv_lds_bytes(WT, k, nc, lpr, ch.u, th);
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid_dim, dim3(th), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows,
                                (int)k, grid, (const uint8_t*)xq, (uint32_t)xqbytes, c0, ncp, y, ldy, sums);

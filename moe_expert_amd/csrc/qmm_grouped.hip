@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     GroupInfo gi;
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
 
-    const ActLds act = act_lds_layout<kGroupPass, kGemvLanesPerRow, U>(lds, hidden);
-    uint32_t* lds_grid = act_lds_end<kGroupPass>(act);
+    const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
+    uint32_t* lds_grid = act_lds_end<NS, kGuThreads>(act);
     float* gl = (float*)(lds_grid + (WT == kCB3 ? 512 : 0));  // [8][32] gate sums
     float* ul = gl + kGroupPass * 32;                            // [8][32] up sums
 
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
                                                        (int)IQ4Consts::opaque_u((uint32_t)l16));
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
-        ActStage<NS, kGroupPass, kGemvLanesPerRow> stage;
+        ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads> stage;
         stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
         GridStage<kGuThreads> gstage;
         if constexpr (WT == kCB3) gstage.load(grid);
@@ -181,10 +181,11 @@ static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nent
 static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
 static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
 static size_t gu_lds_bytes(int wt, int64_t hidden) {
-    return gemv_lds_bytes(wt, hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u) + 2 * kGroupPass * 32 * sizeof(float);
+    return gemv_lds_bytes(wt, hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, kGuThreads) +
+           2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
-    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u);
+    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u, kGemvThreads);
 }
 static int gu_slots(int64_t hidden) {
     return stage_slots(hidden, kGroupPass, kGuThreads, kGemvLanesPerRow, gu_chunk(hidden).u);
