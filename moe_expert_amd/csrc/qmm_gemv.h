@@ -296,8 +296,12 @@ struct RowEngine {
             const int s = l16 + LPR * (i0 + u);
             if (g == 0) {
                 const int sc = clamp_unit(s);
+                // Q8_0 / IQ4_NL blocks (34 / 18 bytes) of one lane all start at the same offset
+                // mod 4 (the lane's blocks are an even number apart), so the realignment uses the
+                // lane's first block; a block past the row (loaded at the row's last block) may
+                // decode to garbage, which its zero scale discards.
                 if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
-                else Unit<WT>::decode(buf[u], unit_off(sc), W, dw, mult, kc);
+                else Unit<WT>::decode(buf[u], unit_off(l16), W, dw, mult, kc);
             }
             const Cols<CG>& a = cols[kAhead ? (n & 1) : 0];
             const bool ok = s < nunits;
