@@ -231,6 +231,18 @@ struct Unit<kIQ4_NL> {
     }
 };
 
+// Byte k of q, shifted left by 6 (one SDWA instruction).
+__device__ __forceinline__ uint32_t byte_shl6(uint32_t q, int k) {
+    uint32_t r;
+    switch (k) {
+        case 0: asm("v_lshlrev_b32_sdwa %0, 6, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(q)); break;
+        case 1: asm("v_lshlrev_b32_sdwa %0, 6, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(q)); break;
+        case 2: asm("v_lshlrev_b32_sdwa %0, 6, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(q)); break;
+        default: asm("v_lshlrev_b32_sdwa %0, 6, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(q)); break;
+    }
+    return r;
+}
+
 // CB3 super-block field offsets
 constexpr int kCB3Bytes = 110, kCB3Qs = 2, kCB3Qh = 66, kCB3Signs = 74, kCB3Scales = 106;
 
@@ -286,7 +298,32 @@ struct Unit<kCB3> {
         dw = raw[7];
         mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
     }
+    // The same with the signs already applied: sgrid is the signed codebook in LDS.
+    __device__ static __forceinline__ void decode_signed(const uint32_t* raw, uint32_t off, int ss, const uint32_t* sgrid,
+                                                         uint32_t* W, uint32_t& dw, int& mult) {
+        const uint32_t shq = (off + kCB3Qs) & 3u;
+        const uint32_t shs = (off + kCB3Signs) & 3u;
+        const uint32_t q0 = align8(raw[1], raw[0], shq);
+        const uint32_t q1 = align8(raw[2], raw[1], shq);
+        const uint32_t sg = align8(raw[4], raw[3], shs);
+        const uint32_t qh = raw[5];
+        // byte address of word (qs byte | qh bit << 8) * 16 + sign nibble: qs byte << 6 (one
+        // SDWA shift), | nibble << 2, | qh bit << 14 (the table's own address is the constant
+        // offset of the LDS read)
+        const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint32_t*)sgrid;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t t = byte_shl6(e < 4 ? q0 : q1, e & 3);
+            const uint32_t a = (__builtin_amdgcn_ubfe(qh, e, 1) << 14) | ((__builtin_amdgcn_ubfe(sg, 4 * e, 4) << 2) | t);
+            W[e] = *(__attribute__((address_space(3))) const uint32_t*)(size_t)(base + a);
+        }
+        dw = raw[7];
+        mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
+    }
 };
+
+// The signed codebook: word 16 idx + n = codebook entry idx with the signs of nibble n applied.
+constexpr int kCB3SignedWords = 512 * 16;  // 32 KiB
 
 // ------------------------------------------------------------------ q8_1 quantization
 

@@ -199,8 +199,9 @@ constexpr int pick_cg() {
     return cg;
 }
 
+// SGRID (CB3): `grid` is the signed codebook (cb3_signed_word) rather than the plain one.
 template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerRow, bool VAR = false,
-          int BUDGET = 100>
+          int BUDGET = 100, bool SGRID = false>
 struct RowEngine {
     static constexpr int RAW = Unit<WT>::RAW;
     static constexpr int CGMAX = pick_cg<WT, NC, U, MULTI, BUDGET>();
@@ -300,7 +301,8 @@ struct RowEngine {
                 // mod 4 (the lane's blocks are an even number apart), so the realignment uses the
                 // lane's first block; a block past the row (loaded at the row's last block) may
                 // decode to garbage, which its zero scale discards.
-                if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
+                if constexpr (WT == kCB3 && SGRID) Unit<WT>::decode_signed(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
+                else if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
                 else Unit<WT>::decode(buf[u], unit_off(l16), W, dw, mult, kc);
             }
             const Cols<CG>& a = cols[kAhead ? (n & 1) : 0];

@@ -48,6 +48,12 @@ struct GroupInfo {
 // wave, a DPP row of 16 lanes each), so each lane holds one row engine.
 constexpr int kGuThreads = 1024;
 
+// The signed CB3 codebook of a gate/up workgroup (static LDS, beside the dynamic area).
+__device__ __forceinline__ uint32_t* cb3_signed_lds() {
+    __shared__ __attribute__((aligned(16))) uint32_t t[kCB3SignedWords];
+    return t;
+}
+
 template <int WT, int U, bool MULTI, int NS>
 __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
@@ -60,9 +66,14 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
 
     const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
-    uint32_t* lds_grid = act_lds_end<NS, kGuThreads>(act);
-    float* gl = (float*)(lds_grid + (WT == kCB3 ? 512 : 0));  // [8][32] gate sums
-    float* ul = gl + kGroupPass * 32;                            // [8][32] up sums
+    float* gl = (float*)act_lds_end<NS, kGuThreads>(act);  // [8][32] gate sums
+    float* ul = gl + kGroupPass * 32;                       // [8][32] up sums
+    // CB3: the signed codebook (16 sign variants of each entry), built in the first pass: thread
+    // t loads entry t / 2 with the activations and, once the weight loads are issued, writes its
+    // sign variants 8 (t mod 2) .. 8 (t mod 2) + 7
+    const uint32_t* sgrid = nullptr;
+    if constexpr (WT == kCB3) sgrid = cb3_signed_lds();
+    static_assert(WT != kCB3 || kCB3SignedWords == 8 * kGuThreads, "eight codebook words per thread");
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15;
@@ -82,25 +93,38 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         // The row engine is rebuilt each pass from values the compiler cannot see through, so
         // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
         // in registers, or spill it, across the whole loop).
-        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
+        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0, true> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
                                                        (int)IQ4Consts::opaque_u((uint32_t)l16));
         if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
         ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads> stage;
         stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
-        GridStage<kGuThreads> gstage;
-        if constexpr (WT == kCB3) gstage.load(grid);
+        const bool first = c0 == gi.k0;
+        uint32_t gword = 0;
+        if constexpr (WT == kCB3) {
+            if (first) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
+        }
         __builtin_amdgcn_sched_barrier(0);
         eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
         __builtin_amdgcn_sched_barrier(0);
         stage.store(act);
-        if constexpr (WT == kCB3) gstage.store(lds_grid);
+        if constexpr (WT == kCB3) {
+            if (first) {
+                const uint32_t n0 = 8u * (threadIdx.x & 1u);
+                uint32_t v[8];
+#pragma unroll
+                for (int n = 0; n < 8; ++n) v[n] = cb3_signed(gword, n0 + n);
+                u32x4* dst = (u32x4*)(cb3_signed_lds() + 8 * threadIdx.x);
+                dst[0] = u32x4{v[0], v[1], v[2], v[3]};
+                dst[1] = u32x4{v[4], v[5], v[6], v[7]};
+            }
+        }
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
 
         float acc[kGroupPass];
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
-        eng.run(act_view<kGroupPass>(act, l16), ncp, lds_grid, acc, nullptr, 0, true);
+        eng.run(act_view<kGroupPass>(act, l16), ncp, sgrid, acc, nullptr, 0, true);
         const float sum = row16_sums<kGroupPass>(acc, l16);
         const int c = row_col<kGroupPass>(l16);
         if ((l16 & 1) == 0 && c < ncp) {
@@ -180,8 +204,9 @@ static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nent
 // chunks of 2 for long rows; down: 512 threads).
 static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
 static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
-static size_t gu_lds_bytes(int wt, int64_t hidden) {
-    return gemv_lds_bytes(wt, hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, kGuThreads) +
+// (dynamic LDS: activations and the gate/up sums; the signed CB3 codebook is static)
+static size_t gu_lds_bytes(int64_t hidden) {
+    return act_lds_bytes(hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, kGuThreads) +
            2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
@@ -207,7 +232,7 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     const uint32_t xqbytes = (uint32_t)((uint64_t)a.xq_cols * (a.hidden / 32) * 36);
     {
-        const size_t lds = gu_lds_bytes(a.wtype_gu, a.hidden);
+        const size_t lds = gu_lds_bytes(a.hidden);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
             hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up,
@@ -271,7 +296,7 @@ extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const voi
         !aligned(ws, 16))
         return QMM_EALIGN;
     // a pass of 8 entries must fit the workgroup's LDS and staging slots
-    if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
+    if (gu_lds_bytes(hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
         gu_slots(hidden) == 0 || down_slots(inter) == 0)
         return QMM_EUNSUPPORTED;
     if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxActBytes || grouped_h_bytes(inter, nentries) > kMaxActBytes)
