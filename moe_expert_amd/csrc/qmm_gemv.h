@@ -392,7 +392,7 @@ __device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
 // the weights arrive, cross-lane row sums.
 template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
-          bool VAR = false>
+          bool VAR = false, int BUDGET = 100>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, uint32_t xbytes,
                                           int col0, int ncp, float* y, int64_t ldy, int32_t* sums, int row0,
                                           uint32_t* lds) {
@@ -412,7 +412,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
-    RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR> eng(wr, row_off, K, l16);
+    RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR, BUDGET> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
     stage.store(act);

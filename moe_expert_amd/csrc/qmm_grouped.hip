@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
     for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
         if (c0 != gi.k0) __syncthreads();
-        gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kGemvThreads, true>(
+        gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kGemvThreads, true, 40>(
             wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kGemvRowsPerWG, lds);
     }
 }
