@@ -266,8 +266,10 @@ template <>
 struct Unit<kCB3> {
     using Consts = NoConsts;
     static constexpr int RAW = 8;
-    // raw: [0..2] qs window, [3..4] signs window, [5] qh byte, [6] scales byte, [7] d
-    // `off` = byte offset of the super-block, `ss` = sub-block 0..7.
+    // raw: [0..2] qs window, [3..4] signs window, [5] the dword holding the qh byte, [6] the dword
+    // holding the scales byte, [7] the dword holding d.  `off` = byte offset of the super-block
+    // (even), `ss` = sub-block 0..7.  Whole dwords, no 8/16-bit loads: their zero-extension
+    // would be computed (and waited for) where the loaded values are first shared.
     __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, int ss, uint32_t* raw) {
         const uint32_t oq = off + kCB3Qs + 8 * ss;
         const u32x3 q = ld96(r, oq & ~3u);
@@ -275,9 +277,20 @@ struct Unit<kCB3> {
         const uint32_t os = off + kCB3Signs + 4 * ss;
         const u32x2 s = ld64(r, os & ~3u);
         raw[3] = s.x; raw[4] = s.y;
-        raw[5] = ld8(r, off + kCB3Qh + ss);
-        raw[6] = ld8(r, off + kCB3Scales + (ss >> 1));
-        raw[7] = ld16(r, off);
+        raw[5] = ld32(r, (off + kCB3Qh + ss) & ~3u);
+        raw[6] = ld32(r, (off + kCB3Scales + (ss >> 1)) & ~3u);
+        raw[7] = ld32(r, off & ~3u);
+    }
+    // qh byte, sub-block multiplier and d bits of a loaded sub-block
+    __device__ static __forceinline__ uint32_t qh_byte(const uint32_t* raw, uint32_t off, int ss) {
+        return raw[5] >> (8u * ((off + kCB3Qh + ss) & 3u));
+    }
+    __device__ static __forceinline__ int multiplier(const uint32_t* raw, uint32_t off, int ss) {
+        const uint32_t sh = 8u * ((off + kCB3Scales + (ss >> 1)) & 3u) + 4u * (ss & 1);
+        return 1 + 2 * (int)((raw[6] >> sh) & 15u);
+    }
+    __device__ static __forceinline__ uint32_t d_bits(const uint32_t* raw, uint32_t off) {
+        return (raw[7] >> (8u * (off & 2u))) & 0xFFFFu;
     }
     // grid: the 512 codebook words in LDS.  `off` and `ss` as in load (the low bits of the
     // field offsets give the realignment).
@@ -288,15 +301,15 @@ struct Unit<kCB3> {
         const uint32_t q0 = align8(raw[1], raw[0], shq);
         const uint32_t q1 = align8(raw[2], raw[1], shq);
         const uint32_t sg = align8(raw[4], raw[3], shs);
-        const uint32_t qh = raw[5];
+        const uint32_t qh = qh_byte(raw, off, ss);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t qb = ((e < 4 ? q0 : q1) >> (8 * (e & 3))) & 0xFFu;
             const uint32_t idx = qb | (((qh >> e) & 1u) << 8);
             W[e] = cb3_signed(grid[idx], (sg >> (4 * e)) & 15u);
         }
-        dw = raw[7];
-        mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
+        dw = d_bits(raw, off);
+        mult = multiplier(raw, off, ss);
     }
     // The same with the signs already applied: sgrid is the signed codebook in LDS.
     __device__ static __forceinline__ void decode_signed(const uint32_t* raw, uint32_t off, int ss, const uint32_t* sgrid,
@@ -306,7 +319,7 @@ struct Unit<kCB3> {
         const uint32_t q0 = align8(raw[1], raw[0], shq);
         const uint32_t q1 = align8(raw[2], raw[1], shq);
         const uint32_t sg = align8(raw[4], raw[3], shs);
-        const uint32_t qh = raw[5];
+        const uint32_t qh = qh_byte(raw, off, ss);
         // byte address of word (qs byte | qh bit << 8) * 16 + sign nibble: qs byte << 6 (one
         // SDWA shift), | nibble << 2, | qh bit << 14 (the table's own address is the constant
         // offset of the LDS read)
@@ -317,8 +330,8 @@ struct Unit<kCB3> {
             const uint32_t a = (__builtin_amdgcn_ubfe(qh, e, 1) << 14) | ((__builtin_amdgcn_ubfe(sg, 4 * e, 4) << 2) | t);
             W[e] = *(__attribute__((address_space(3))) const uint32_t*)(size_t)(base + a);
         }
-        dw = raw[7];
-        mult = 1 + 2 * (int)((raw[6] >> (4 * (ss & 1))) & 15u);
+        dw = d_bits(raw, off);
+        mult = multiplier(raw, off, ss);
     }
 };
 
@@ -362,6 +375,15 @@ __device__ __forceinline__ uint32_t pack4_lanes(int q) {
     const uint32_t b = (uint32_t)q & 0xFFu;
     const uint32_t b1 = __shfl_down(b, 1, 64), b2 = __shfl_down(b, 2, 64), b3 = __shfl_down(b, 3, 64);
     return b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Workgroup barrier for LDS written with ds_write: waits for this wave's LDS operations only
+// (a __syncthreads release fence would also wait for outstanding direct-to-LDS loads).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------ cross-lane sums

@@ -147,11 +147,17 @@ struct ActStage {
         load_blocks(xr, act, (uint32_t)((col0 + c) * act.nb + b0), b0, c < ncp, zero_off);
     }
     // Pass column c taken from activation column entry_col[c0 + c]; a column outside
-    // [0, ncols) reads zeros as well (zero_off: the buffer's size).
+    // [0, ncols) reads zeros as well (zero_off: the buffer's size).  The pass's entry indices
+    // are read as uniform (scalar) loads and picked per lane.
     __device__ __forceinline__ void load_entries(rsrc_t xr, const ActLds& act, int ncp, const int32_t* entry_col, int c0,
                                                  int ncols, uint32_t zero_off) {
         const int c = col(), b0 = block0();
-        const int src = entry_col[c0 + (c < ncp ? c : 0)];
+        int src = 0;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int e = entry_col[c0 + (k < ncp ? k : 0)];
+            src = c == k ? e : src;
+        }
         const bool ok = c < ncp && src >= 0 && src < ncols;
         load_blocks(xr, act, (uint32_t)((ok ? src : 0) * act.nb + b0), b0, ok, zero_off);
     }
@@ -296,14 +302,15 @@ struct RowEngine {
             }
             const int s = l16 + LPR * (i0 + u);
             if (g == 0) {
+                const uint32_t* rw = buf[u];
                 const int sc = clamp_unit(s);
                 // Q8_0 / IQ4_NL blocks (34 / 18 bytes) of one lane all start at the same offset
                 // mod 4 (the lane's blocks are an even number apart), so the realignment uses the
                 // lane's first block; a block past the row (loaded at the row's last block) may
                 // decode to garbage, which its zero scale discards.
-                if constexpr (WT == kCB3 && SGRID) Unit<WT>::decode_signed(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
-                else if constexpr (WT == kCB3) Unit<WT>::decode(buf[u], unit_off(sc), sc & 7, grid, W, dw, mult);
-                else Unit<WT>::decode(buf[u], unit_off(l16), W, dw, mult, kc);
+                if constexpr (WT == kCB3 && SGRID) Unit<WT>::decode_signed(rw, unit_off(sc), sc & 7, grid, W, dw, mult);
+                else if constexpr (WT == kCB3) Unit<WT>::decode(rw, unit_off(sc), sc & 7, grid, W, dw, mult);
+                else Unit<WT>::decode(rw, unit_off(l16), W, dw, mult, kc);
             }
             const Cols<CG>& a = cols[kAhead ? (n & 1) : 0];
             const bool ok = s < nunits;

@@ -48,6 +48,13 @@ struct GroupInfo {
 // wave, a DPP row of 16 lanes each), so each lane holds one row engine.
 constexpr int kGuThreads = 1024;
 
+// v_perm selector taking byte k from the second operand (k) or, where bit k of n is set, from
+// the first (k + 4).
+constexpr uint32_t sign_select(int n) {
+    return 0x03020100u | ((n & 1) ? 0x4u : 0u) | ((n & 2) ? 0x400u : 0u) | ((n & 4) ? 0x40000u : 0u) |
+           ((n & 8) ? 0x4000000u : 0u);
+}
+
 // The signed CB3 codebook of a gate/up workgroup (static LDS, beside the dynamic area).
 __device__ __forceinline__ uint32_t* cb3_signed_lds() {
     __shared__ __attribute__((aligned(16))) uint32_t t[kCB3SignedWords];
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         // in registers, or spill it, across the whole loop).
         RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0, true> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
                                                        (int)IQ4Consts::opaque_u((uint32_t)l16));
-        if (c0 != gi.k0) __syncthreads();  // the previous pass's LDS reads are done
+        if (c0 != gi.k0) lds_barrier();  // the previous pass's LDS reads are done
         ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads> stage;
         stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
         const bool first = c0 == gi.k0;
@@ -109,16 +116,23 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         stage.store(act);
         if constexpr (WT == kCB3) {
             if (first) {
-                const uint32_t n0 = 8u * (threadIdx.x & 1u);
+                // variant n: byte k negated where bit k of n is set; with every byte of the
+                // entry non-zero, ~g + 0x01010101 negates all four bytes without carries, and
+                // one v_perm picks each byte from g or from it
+                const uint32_t neg = ~gword + 0x01010101u;
+                const bool hi = threadIdx.x & 1u;
                 uint32_t v[8];
 #pragma unroll
-                for (int n = 0; n < 8; ++n) v[n] = cb3_signed(gword, n0 + n);
+                for (int n = 0; n < 8; ++n) {
+                    const uint32_t lo_sel = sign_select(n), hi_sel = sign_select(8 + n);
+                    v[n] = perm(neg, gword, hi ? hi_sel : lo_sel);
+                }
                 u32x4* dst = (u32x4*)(cb3_signed_lds() + 8 * threadIdx.x);
                 dst[0] = u32x4{v[0], v[1], v[2], v[3]};
                 dst[1] = u32x4{v[4], v[5], v[6], v[7]};
             }
         }
-        __syncthreads();
+        lds_barrier();
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
 
         float acc[kGroupPass];
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
             sums[c * 32 + rg] = sum;
             if (dbg) dbg[(int64_t)(c0 + c) * inter + i] = sum;
         }
-        __syncthreads();
+        lds_barrier();
         // SwiGLU -> q8_1: one half wave per entry (waves 0..3), value j = intermediate 32t + j
         if (threadIdx.x < kGroupPass * 32) {
             const int c = threadIdx.x >> 5, j = threadIdx.x & 31;
