@@ -181,6 +181,12 @@ __device__ __forceinline__ uint32_t iq4nl_lookup_u(uint32_t i7, uint32_t i8) {
 // Blocks of 34 and 18 bytes start on a 4-byte or a 2-byte boundary; the loads start at the
 // enclosing 4-byte boundary and one v_perm per dword realigns them (selector 0x05040302 when
 // the block is 4-byte aligned, 0x07060504 when it is 2 bytes past one).
+//
+// The blocks one lane takes from a row lie a whole number of dwords apart (16 or 64 blocks of
+// 34 or 18 bytes; 2 or 8 super-blocks of 110 bytes), so they share their offset mod 4: a
+// per-lane Frame holds the 4-byte-aligned field addresses and the realignment of the lane's
+// first block, and block j of the lane is read at those addresses plus j times the lane
+// stride (a constant the loads carry as their immediate offset).
 
 template <int WT>
 struct Unit;
@@ -188,22 +194,31 @@ struct Unit;
 __device__ __forceinline__ uint32_t realign_sel(uint32_t off) { return (off & 2u) ? 0x07060504u : 0x05040302u; }
 __device__ __forceinline__ uint32_t realign_scale(uint32_t w0, uint32_t off) { return (off & 2u) ? (w0 >> 16) : (w0 & 0xFFFFu); }
 
+// Q8_0 / IQ4_NL lane frame: the 4-byte boundary at or before the lane's first block, and 2 if
+// that block starts 2 bytes past it (else 0).
+struct AlignFrame {
+    uint32_t a, hi;
+    __device__ static __forceinline__ AlignFrame of(uint32_t off) { return {off & ~3u, off & 2u}; }
+};
+
 template <>
 struct Unit<kQ8_0> {
     using Consts = NoConsts;
     static constexpr int RAW = 9;
     static constexpr int BYTES = 34;
-    __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
-        const uint32_t a = off & ~3u;
+    using Frame = AlignFrame;
+    __device__ static __forceinline__ Frame frame(uint32_t off, int) { return AlignFrame::of(off); }
+    __device__ static __forceinline__ void load(rsrc_t r, const Frame& f, uint32_t jb, uint32_t* raw) {
+        const uint32_t a = f.a + jb;
         const u32x4 x = ld128(r, a), y = ld128(r, a + 16);
         raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
         raw[4] = y.x; raw[5] = y.y; raw[6] = y.z; raw[7] = y.w;
         raw[8] = ld32(r, a + 32);
     }
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
-                                                  const NoConsts&) {
-        const uint32_t sel = realign_sel(off);
-        dw = realign_scale(raw[0], off);
+    __device__ static __forceinline__ void decode(const uint32_t* raw, const Frame& f, uint32_t* W, uint32_t& dw,
+                                                  int& mult, const NoConsts&) {
+        const uint32_t sel = realign_sel(f.hi);
+        dw = realign_scale(raw[0], f.hi);
 #pragma unroll
         for (int i = 0; i < 8; ++i) W[i] = perm(raw[i + 1], raw[i], sel);
         mult = 1;
@@ -215,16 +230,18 @@ struct Unit<kIQ4_NL> {
     using Consts = IQ4Levels;
     static constexpr int RAW = 5;
     static constexpr int BYTES = 18;
-    __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t* raw) {
-        const uint32_t a = off & ~3u;
+    using Frame = AlignFrame;
+    __device__ static __forceinline__ Frame frame(uint32_t off, int) { return AlignFrame::of(off); }
+    __device__ static __forceinline__ void load(rsrc_t r, const Frame& f, uint32_t jb, uint32_t* raw) {
+        const uint32_t a = f.a + jb;
         const u32x4 x = ld128(r, a);
         raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
         raw[4] = ld32(r, a + 16);
     }
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, uint32_t* W, uint32_t& dw, int& mult,
-                                                  const IQ4Levels& k) {
-        const uint32_t sel = realign_sel(off);
-        dw = realign_scale(raw[0], off);
+    __device__ static __forceinline__ void decode(const uint32_t* raw, const Frame& f, uint32_t* W, uint32_t& dw,
+                                                  int& mult, const IQ4Levels& k) {
+        const uint32_t sel = realign_sel(f.hi);
+        dw = realign_scale(raw[0], f.hi);
 #pragma unroll
         for (int i = 0; i < 4; ++i) iq4nl_decode_word(perm(raw[i + 1], raw[i], sel), W[i], W[i + 4], k);
         mult = 1;
@@ -266,60 +283,67 @@ template <>
 struct Unit<kCB3> {
     using Consts = NoConsts;
     static constexpr int RAW = 8;
+    static_assert((kCB3Signs - kCB3Qs) % 4 == 0, "qs and sign windows share their realignment");
+    // Lane frame for sub-block ss of the super-block at byte `off` (even): the 4-byte-aligned
+    // addresses of the qs window, the sign window and the dwords holding the qh byte, the scales
+    // byte and d, and the shifts that realign them.
+    struct Frame {
+        uint32_t q, s, qh, sc, d;
+        uint32_t shq, shqh, shsc, shd;
+    };
+    __device__ static __forceinline__ Frame frame(uint32_t off, int ss) {
+        Frame f;
+        f.q = (off + kCB3Qs + 8 * ss) & ~3u;
+        f.s = (off + kCB3Signs + 4 * ss) & ~3u;
+        f.qh = (off + kCB3Qh + ss) & ~3u;
+        f.sc = (off + kCB3Scales + (ss >> 1)) & ~3u;
+        f.d = off & ~3u;
+        f.shq = (off + kCB3Qs) & 3u;  // 8 ss and 4 ss keep the low bits
+        f.shqh = 8u * ((off + kCB3Qh + ss) & 3u);
+        f.shsc = 8u * ((off + kCB3Scales + (ss >> 1)) & 3u) + 4u * (ss & 1);
+        f.shd = 8u * (off & 2u);
+        return f;
+    }
     // raw: [0..2] qs window, [3..4] signs window, [5] the dword holding the qh byte, [6] the dword
-    // holding the scales byte, [7] the dword holding d.  `off` = byte offset of the super-block
-    // (even), `ss` = sub-block 0..7.  Whole dwords, no 8/16-bit loads: their zero-extension
-    // would be computed (and waited for) where the loaded values are first shared.
-    __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, int ss, uint32_t* raw) {
-        const uint32_t oq = off + kCB3Qs + 8 * ss;
-        const u32x3 q = ld96(r, oq & ~3u);
+    // holding the scales byte, [7] the dword holding d.  Whole dwords, no 8/16-bit loads: their
+    // zero-extension would be computed (and waited for) where the loaded values are first
+    // shared.
+    __device__ static __forceinline__ void load(rsrc_t r, const Frame& f, uint32_t jb, uint32_t* raw) {
+        const u32x3 q = ld96(r, f.q + jb);
         raw[0] = q.x; raw[1] = q.y; raw[2] = q.z;
-        const uint32_t os = off + kCB3Signs + 4 * ss;
-        const u32x2 s = ld64(r, os & ~3u);
+        const u32x2 s = ld64(r, f.s + jb);
         raw[3] = s.x; raw[4] = s.y;
-        raw[5] = ld32(r, (off + kCB3Qh + ss) & ~3u);
-        raw[6] = ld32(r, (off + kCB3Scales + (ss >> 1)) & ~3u);
-        raw[7] = ld32(r, off & ~3u);
+        raw[5] = ld32(r, f.qh + jb);
+        raw[6] = ld32(r, f.sc + jb);
+        raw[7] = ld32(r, f.d + jb);
     }
-    // qh byte, sub-block multiplier and d bits of a loaded sub-block
-    __device__ static __forceinline__ uint32_t qh_byte(const uint32_t* raw, uint32_t off, int ss) {
-        return raw[5] >> (8u * ((off + kCB3Qh + ss) & 3u));
+    // realigned qs and sign words, qh byte, multiplier and d bits of a loaded sub-block
+    __device__ static __forceinline__ void fields(const uint32_t* raw, const Frame& f, uint32_t& q0, uint32_t& q1,
+                                                  uint32_t& sg, uint32_t& qh, uint32_t& dw, int& mult) {
+        q0 = align8(raw[1], raw[0], f.shq);
+        q1 = align8(raw[2], raw[1], f.shq);
+        sg = align8(raw[4], raw[3], f.shq);
+        qh = raw[5] >> f.shqh;
+        mult = 1 + 2 * (int)((raw[6] >> f.shsc) & 15u);
+        dw = (raw[7] >> f.shd) & 0xFFFFu;
     }
-    __device__ static __forceinline__ int multiplier(const uint32_t* raw, uint32_t off, int ss) {
-        const uint32_t sh = 8u * ((off + kCB3Scales + (ss >> 1)) & 3u) + 4u * (ss & 1);
-        return 1 + 2 * (int)((raw[6] >> sh) & 15u);
-    }
-    __device__ static __forceinline__ uint32_t d_bits(const uint32_t* raw, uint32_t off) {
-        return (raw[7] >> (8u * (off & 2u))) & 0xFFFFu;
-    }
-    // grid: the 512 codebook words in LDS.  `off` and `ss` as in load (the low bits of the
-    // field offsets give the realignment).
-    __device__ static __forceinline__ void decode(const uint32_t* raw, uint32_t off, int ss, const uint32_t* grid,
-                                                  uint32_t* W, uint32_t& dw, int& mult) {
-        const uint32_t shq = (off + kCB3Qs) & 3u;  // 8*ss keeps the low bits
-        const uint32_t shs = (off + kCB3Signs) & 3u;
-        const uint32_t q0 = align8(raw[1], raw[0], shq);
-        const uint32_t q1 = align8(raw[2], raw[1], shq);
-        const uint32_t sg = align8(raw[4], raw[3], shs);
-        const uint32_t qh = qh_byte(raw, off, ss);
+    // grid: the 512 codebook words in LDS
+    __device__ static __forceinline__ void decode(const uint32_t* raw, const Frame& f, const uint32_t* grid, uint32_t* W,
+                                                  uint32_t& dw, int& mult) {
+        uint32_t q0, q1, sg, qh;
+        fields(raw, f, q0, q1, sg, qh, dw, mult);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t qb = ((e < 4 ? q0 : q1) >> (8 * (e & 3))) & 0xFFu;
             const uint32_t idx = qb | (((qh >> e) & 1u) << 8);
             W[e] = cb3_signed(grid[idx], (sg >> (4 * e)) & 15u);
         }
-        dw = d_bits(raw, off);
-        mult = multiplier(raw, off, ss);
     }
     // The same with the signs already applied: sgrid is the signed codebook in LDS.
-    __device__ static __forceinline__ void decode_signed(const uint32_t* raw, uint32_t off, int ss, const uint32_t* sgrid,
+    __device__ static __forceinline__ void decode_signed(const uint32_t* raw, const Frame& f, const uint32_t* sgrid,
                                                          uint32_t* W, uint32_t& dw, int& mult) {
-        const uint32_t shq = (off + kCB3Qs) & 3u;
-        const uint32_t shs = (off + kCB3Signs) & 3u;
-        const uint32_t q0 = align8(raw[1], raw[0], shq);
-        const uint32_t q1 = align8(raw[2], raw[1], shq);
-        const uint32_t sg = align8(raw[4], raw[3], shs);
-        const uint32_t qh = qh_byte(raw, off, ss);
+        uint32_t q0, q1, sg, qh;
+        fields(raw, f, q0, q1, sg, qh, dw, mult);
         // byte address of word (qs byte | qh bit << 8) * 16 + sign nibble: qs byte << 6 (one
         // SDWA shift), | nibble << 2, | qh bit << 14 (the table's own address is the constant
         // offset of the LDS read)
@@ -330,13 +354,24 @@ struct Unit<kCB3> {
             const uint32_t a = (__builtin_amdgcn_ubfe(qh, e, 1) << 14) | ((__builtin_amdgcn_ubfe(sg, 4 * e, 4) << 2) | t);
             W[e] = *(__attribute__((address_space(3))) const uint32_t*)(size_t)(base + a);
         }
-        dw = d_bits(raw, off);
-        mult = multiplier(raw, off, ss);
     }
 };
 
 // The signed codebook: word 16 idx + n = codebook entry idx with the signs of nibble n applied.
 constexpr int kCB3SignedWords = 512 * 16;  // 32 KiB
+
+// ------------------------------------------------------------------ DPP lane moves
+
+// The value of the lane that DPP control CTRL selects within this lane's row of 16 (quad_perm
+// 0x00-0xFF, row_mirror 0x140, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
 
 // ------------------------------------------------------------------ q8_1 quantization
 
@@ -353,9 +388,15 @@ __device__ __forceinline__ int round_away(float v) {
 // s = fp16(d * sum q) with the product in binary32; an all-zero block is all zeros.  Returns
 // q_j; `hdr` (d | s << 16) is the same in all 32 lanes.  Every lane of the wave must call it.
 __device__ __forceinline__ int quantize_lanes32(float v, uint32_t& hdr) {
+    // the maximum and the integer sum over the half wave: within a row of 16 lanes by DPP (quad
+    // partners, then the other quad of the half row, then the other half row), then across the
+    // two rows with one lane exchange; both are exact in any order
     float amax = __builtin_fabsf(v);
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 64));
+    amax = __builtin_fmaxf(amax, dpp<0xB1>(amax));
+    amax = __builtin_fmaxf(amax, dpp<0x4E>(amax));
+    amax = __builtin_fmaxf(amax, dpp<0x141>(amax));
+    amax = __builtin_fmaxf(amax, dpp<0x140>(amax));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
     const float d = amax / 127.0f;
     const bool zero = amax == 0.0f || d == 0.0f;
     int q = 0;
@@ -364,18 +405,28 @@ __device__ __forceinline__ int quantize_lanes32(float v, uint32_t& hdr) {
         q = q > 127 ? 127 : (q < -127 ? -127 : q);
     }
     int sum = q;
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) sum += __shfl_xor(sum, m, 64);
+    sum += dpp_i<0xB1>(sum);
+    sum += dpp_i<0x4E>(sum);
+    sum += dpp_i<0x141>(sum);
+    sum += dpp_i<0x140>(sum);
+    sum += __shfl_xor(sum, 16, 64);
     hdr = zero ? 0u : (f2h(d) | (f2h(opaque(d * (float)sum)) << 16));
     return q;
 }
 
-// Pack the int8 q of lanes j..j+3 (j a multiple of 4) into one dword, valid in lane j.
+// Pack the int8 q of lanes j..j+3 (j a multiple of 4) into one dword, valid in lane j (DPP
+// quad broadcasts of lanes 1, 2, 3 of the quad).
 __device__ __forceinline__ uint32_t pack4_lanes(int q) {
-    const uint32_t b = (uint32_t)q & 0xFFu;
-    const uint32_t b1 = __shfl_down(b, 1, 64), b2 = __shfl_down(b, 2, 64), b3 = __shfl_down(b, 3, 64);
-    return b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    const int b = q & 0xFF;
+    const uint32_t b1 = (uint32_t)dpp_i<0x55>(b), b2 = (uint32_t)dpp_i<0xAA>(b), b3 = (uint32_t)dpp_i<0xFF>(b);
+    return (uint32_t)b | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
+
+// Wait for every vector memory operation of this wave (vmcnt 0; expcnt and lgkmcnt not
+// waited).  Used on the back edge of a pass loop: with nothing outstanding when a pass starts,
+// the compiler's wait counting does not carry the previous pass's loads into the next pass
+// (where it would wait for them between the next pass's loads).
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier for LDS written with ds_write: waits for this wave's LDS operations only
 // (a __syncthreads release fence would also wait for outstanding direct-to-LDS loads).
@@ -388,10 +439,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ------------------------------------------------------------------ cross-lane sums
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
 
 // Lane l (of a 16-lane DPP row) pairs with lane l ^ m in the four steps m = 15, 7, 2, 1
 // (row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]).  One step adds the

@@ -55,82 +55,66 @@ constexpr uint32_t sign_select(int n) {
            ((n & 8) ? 0x4000000u : 0u);
 }
 
+constexpr bool high_variants_set_bit26() {
+    for (int n = 0; n < 8; ++n)
+        if (sign_select(8 + n) != (sign_select(n) | (1u << 26)) || (sign_select(n) & (1u << 26))) return false;
+    return true;
+}
+static_assert(high_variants_set_bit26(), "variants 8..15 take byte 3 from the negated entry");
+
 // The signed CB3 codebook of a gate/up workgroup (static LDS, beside the dynamic area).
 __device__ __forceinline__ uint32_t* cb3_signed_lds() {
     __shared__ __attribute__((aligned(16))) uint32_t t[kCB3SignedWords];
     return t;
 }
 
+// State of one gate/up workgroup and one pass over entries [c0, c0 + 8) of its group.
 template <int WT, int U, bool MULTI, int NS>
-__global__ __launch_bounds__(kGuThreads) void gu_kernel(
-    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
-    int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
-    uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
-    const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
-    float* __restrict__ dbg_u) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    GroupInfo gi;
-    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
+struct GuWorkgroup {
+    const ActLds act;
+    float* gl;  // [8][32] gate sums
+    float* ul;  // [8][32] up sums
+    const uint32_t* sgrid;
+    int l16, rg, i, inter, hidden, xq_cols, nbh, k1;
+    uint32_t rb, xqbytes;
+    rsrc_t xr, wr;
+    const uint8_t* grid;
+    const int32_t* entry_col;
+    uint8_t* hq;
+    float *sums, *dbg;
 
-    const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
-    float* gl = (float*)act_lds_end<NS, kGuThreads>(act);  // [8][32] gate sums
-    float* ul = gl + kGroupPass * 32;                       // [8][32] up sums
-    // CB3: the signed codebook (16 sign variants of each entry), built in the first pass: thread
-    // t loads entry t / 2 with the activations and, once the weight loads are issued, writes its
-    // sign variants 8 (t mod 2) .. 8 (t mod 2) + 7
-    const uint32_t* sgrid = nullptr;
-    if constexpr (WT == kCB3) sgrid = cb3_signed_lds();
-    static_assert(WT != kCB3 || kCB3SignedWords == 8 * kGuThreads, "eight codebook words per thread");
-
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const bool up = wave >= 8;
-    const int rg = (wave & 7) * 4 + (lane >> 4);  // 0..31
-    const int i = blockIdx.x * 32 + rg;           // intermediate index
-    const uint32_t rb = (uint32_t)row_bytes_dev<WT>(hidden);
-    const rsrc_t xr = make_rsrc(xq, xqbytes);
-    const rsrc_t wr = make_rsrc_dw((up ? wu : wg) + gi.e * gu_stride, expert_bytes);
-    const int nbh = inter / 32;
-    float* sums = up ? ul : gl;
-    float* dbg = up ? dbg_u : dbg_g;
-
-    for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
-        const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
+    // FIRST: the workgroup's first pass (builds the signed codebook); VAR: the row engine's
+    // straight-line copies per pass width (the later passes, rare, take the full-width copy,
+    // whose columns are bitwise the same).
+    template <bool FIRST, bool VAR>
+    __device__ __forceinline__ void pass(int c0) {
+        const int ncp = k1 - c0 < kGroupPass ? k1 - c0 : kGroupPass;
         // The row engine is rebuilt each pass from values the compiler cannot see through, so
         // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
         // in registers, or spill it, across the whole loop).
-        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, true, 0, true> eng(wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden,
-                                                       (int)IQ4Consts::opaque_u((uint32_t)l16));
-        if (c0 != gi.k0) lds_barrier();  // the previous pass's LDS reads are done
+        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, VAR, 0, true> eng(
+            wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden, (int)IQ4Consts::opaque_u((uint32_t)l16));
         ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads> stage;
         stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
-        const bool first = c0 == gi.k0;
         uint32_t gword = 0;
-        if constexpr (WT == kCB3) {
-            if (first) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
-        }
+        if constexpr (WT == kCB3 && FIRST) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
         __builtin_amdgcn_sched_barrier(0);
         eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
         __builtin_amdgcn_sched_barrier(0);
         stage.store(act);
-        if constexpr (WT == kCB3) {
-            if (first) {
-                // variant n: byte k negated where bit k of n is set; with every byte of the
-                // entry non-zero, ~g + 0x01010101 negates all four bytes without carries, and
-                // one v_perm picks each byte from g or from it
-                const uint32_t neg = ~gword + 0x01010101u;
-                const bool hi = threadIdx.x & 1u;
-                uint32_t v[8];
+        if constexpr (WT == kCB3 && FIRST) {
+            // variant n: byte k negated where bit k of n is set; with every byte of the entry
+            // non-zero, ~g + 0x01010101 negates all four bytes without carries, and one v_perm
+            // picks each byte from g or from it.  Thread t writes variants 8 (t mod 2) + n:
+            // selector sign_select(n) with bit 26 for the odd threads.
+            const uint32_t neg = ~gword + 0x01010101u;
+            const uint32_t hsel = (threadIdx.x & 1u) << 26;
+            uint32_t v[8];
 #pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const uint32_t lo_sel = sign_select(n), hi_sel = sign_select(8 + n);
-                    v[n] = perm(neg, gword, hi ? hi_sel : lo_sel);
-                }
-                u32x4* dst = (u32x4*)(cb3_signed_lds() + 8 * threadIdx.x);
-                dst[0] = u32x4{v[0], v[1], v[2], v[3]};
-                dst[1] = u32x4{v[4], v[5], v[6], v[7]};
-            }
+            for (int n = 0; n < 8; ++n) v[n] = perm(neg, gword, sign_select(n) | hsel);
+            u32x4* dst = (u32x4*)(cb3_signed_lds() + 8 * threadIdx.x);
+            dst[0] = u32x4{v[0], v[1], v[2], v[3]};
+            dst[1] = u32x4{v[4], v[5], v[6], v[7]};
         }
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
@@ -160,6 +144,45 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
                 if ((j & 3) == 0) dst[1 + (j >> 2)] = word;
             }
         }
+    }
+};
+
+template <int WT, int U, bool MULTI, int NS>
+__global__ __launch_bounds__(kGuThreads) void gu_kernel(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
+    int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
+    uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
+    const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
+    float* __restrict__ dbg_u) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    GroupInfo gi;
+    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
+    static_assert(WT != kCB3 || kCB3SignedWords == 8 * kGuThreads, "eight codebook words per thread");
+
+    const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
+    float* gl = (float*)act_lds_end<NS, kGuThreads>(act);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool up = wave >= 8;
+    const int rg = (wave & 7) * 4 + (lane >> 4);  // 0..31
+    GuWorkgroup<WT, U, MULTI, NS> w{act, gl, gl + kGroupPass * 32,
+                                    // CB3: the signed codebook (16 sign variants of each entry),
+                                    // built in the first pass: thread t loads entry t / 2 with
+                                    // the activations and, once the weight loads are issued,
+                                    // writes its sign variants 8 (t mod 2) .. 8 (t mod 2) + 7
+                                    WT == kCB3 ? cb3_signed_lds() : nullptr,
+                                    lane & 15, rg, (int)blockIdx.x * 32 + rg, inter, hidden, xq_cols, inter / 32,
+                                    gi.k1, (uint32_t)row_bytes_dev<WT>(hidden), xqbytes, make_rsrc(xq, xqbytes),
+                                    make_rsrc_dw((up ? wu : wg) + gi.e * gu_stride, expert_bytes), grid, entry_col,
+                                    hq, up ? gl + kGroupPass * 32 : gl, up ? dbg_u : dbg_g};
+    // The first pass outside the loop: its loads start with nothing outstanding.  Later passes
+    // first wait for the previous pass's memory operations (which the compiler would otherwise
+    // count as outstanding across the loop) and LDS reads.
+    w.template pass<true, true>(gi.k0);
+    for (int c0 = gi.k0 + kGroupPass; c0 < gi.k1; c0 += kGroupPass) {
+        vm_drain();
+        lds_barrier();
+        w.template pass<false, false>(c0);
     }
 }
 
