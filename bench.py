@@ -232,8 +232,11 @@ def grouped_bytes(hidden, inter, ngroups, m, expert_bytes):
 
 
 def grouped_setup(torch, M):
-    """Weights (expert sets in rotation), routing and buffers of the grouped decode workload;
-    returns (sets, calls, call(m, set), host weights, grid, sizes)."""
+    """Weights (expert sets in rotation), routings and buffers of the grouped decode workload;
+    returns (slots, calls, call(m, slot), host weights, grid, sizes).  A slot is an (expert set,
+    routing) pair: the routings of one m take disjoint experts, so the rotation over the slots
+    reads nsets * nexp / ngroups distinct groups of experts (over twice the memory-side cache)
+    and every call starts from HBM."""
     import numpy as np
 
     import synth
@@ -243,7 +246,10 @@ def grouped_setup(torch, M):
     grid = synth.cb3_grid(synth.rng_for(synth.SEEDS["cb3_grid"]))
     dev = torch.device("cuda", 0)
     expert_bytes = 2 * synth.row_bytes(synth.CB3, hidden) * inter + synth.row_bytes(synth.IQ4_NL, inter) * hidden
-    nsets = max(2, -(-2 * MALL_BYTES // (nexp * expert_bytes)) + 1)   # expert sets in rotation
+    nroutes = nexp // ngroups                                          # disjoint routings per m
+    touched = nroutes * ngroups * expert_bytes                         # distinct bytes per set
+    nsets = max(2, -(-2 * MALL_BYTES // touched) + 1)                  # expert sets in rotation
+    slots = [(s, r) for r in range(nroutes) for s in range(nsets)]
     host = dict(wg=np.stack([synth.cb3_weights(rng, inter, hidden) for _ in range(nexp)]),
                 wu=np.stack([synth.cb3_weights(rng, inter, hidden) for _ in range(nexp)]),
                 wd=np.stack([synth.iq4nl_weights(rng, hidden, inter) for _ in range(nexp)]))
@@ -251,48 +257,49 @@ def grouped_setup(torch, M):
     gd = torch.from_numpy(grid).to(dev)
     calls = {}
     for m in GROUPED_M:
-        ge, go, ec = synth.decode_routing(synth.rng_for(seed + m), nexp, ngroups, m)
+        routes = synth.decode_routings(synth.rng_for(seed + m), nexp, ngroups, m, nroutes)
         x = synth.activations(synth.rng_for(seed + 100 + m), m, hidden)
         xd = torch.from_numpy(x).to(dev)
         xq = M.qmm_quantize_q8_1(xd)
         y = torch.empty((ngroups * m, hidden), dtype=torch.float32, device=dev)
         ws = torch.empty(max(16, M.qgemv_grouped_experts_workspace(inter, ngroups * m)), dtype=torch.uint8, device=dev)
-        calls[m] = dict(ge=torch.from_numpy(ge).to(dev), go=torch.from_numpy(go).to(dev),
-                        ec=torch.from_numpy(ec).to(dev), x=xd, xq=xq, y=y, ws=ws, host=(ge, go, ec, x))
+        calls[m] = dict(routes=[tuple(torch.from_numpy(a).to(dev) for a in r) for r in routes],
+                        x=xd, xq=xq, y=y, ws=ws, host=routes[0] + (x,))
 
-    def call(m, s):
+    def call(m, slot):
         c = calls[m]
-        M.qgemv_grouped_experts(synth.CB3, s["wg"], s["wu"], synth.IQ4_NL, s["wd"], hidden, inter, c["xq"], c["ge"],
-                                c["go"], c["ec"], grid=gd, y=c["y"], ws=c["ws"])
+        s, r = sets[slot[0]], c["routes"][slot[1]]
+        M.qgemv_grouped_experts(synth.CB3, s["wg"], s["wu"], synth.IQ4_NL, s["wd"], hidden, inter, c["xq"], r[0],
+                                r[1], r[2], grid=gd, y=c["y"], ws=c["ws"])
 
-    sizes = dict(nexp=nexp, hidden=hidden, inter=inter, ngroups=ngroups, expert_bytes=expert_bytes, nsets=nsets)
-    return sets, calls, call, host, grid, sizes
+    sizes = dict(nexp=nexp, hidden=hidden, inter=inter, ngroups=ngroups, expert_bytes=expert_bytes, nsets=nsets,
+                 nroutes=nroutes, touched=touched)
+    return slots, calls, call, host, grid, sizes
 
 
 def bench_grouped(args, torch, M):
     import synth
     ms_list = GROUPED_M
-    sets, calls, call, host, grid, z = grouped_setup(torch, M)
+    slots, calls, call, host, grid, z = grouped_setup(torch, M)
     hidden, inter, ngroups, expert_bytes, nsets, nexp = (z["hidden"], z["inter"], z["ngroups"], z["expert_bytes"],
                                                          z["nsets"], z["nexp"])
     use_graph = not args.no_graph
 
-    def step(slot):
-        s = sets[slot % nsets]
+    def step(i):
         for m in ms_list:
             M.qmm_quantize_q8_1(calls[m]["x"], out=calls[m]["xq"])
-            call(m, s)
+            call(m, slots[i % len(slots)])
 
-    run_step = capture_slots(torch, step, nsets) if use_graph else step
+    run_step = capture_slots(torch, step, len(slots)) if use_graph else step
     ms = contract_steps(torch, run_step, args.steps, args.warmup)
     step_bytes = sum(grouped_bytes(hidden, inter, ngroups, m, expert_bytes) + quant_bytes(hidden, m) for m in ms_list)
     us, gbps = {}, {}
     tot_b = tot_us = 0.0
     for m in ms_list:
         def batch(m=m):
-            for s in sets:
-                call(m, s)
-        t = timed_graph(torch, batch, args.batch_reps, use_graph) * 1e3 / nsets
+            for sl in slots:
+                call(m, sl)
+        t = timed_graph(torch, batch, args.batch_reps, use_graph) * 1e3 / len(slots)
         b = grouped_bytes(hidden, inter, ngroups, m, expert_bytes)
         us[str(m)] = round(t, 3)
         gbps[str(m)] = round(b / (t * 1e-6) / 1e9, 1)
@@ -304,8 +311,10 @@ def bench_grouped(args, torch, M):
     out = base_line("µs/call and achieved HBM GB/s, grouped MoE decode (16 groups x m entries, 128 experts)",
                     step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
                     {"workload": "grouped MoE decode: hidden 2560, 128 experts, CB3 gate/up 2560->1024, IQ4_NL down "
-                                 f"1024->2560, 16 groups x m entries (m = 1/4/8); {nsets} expert sets in rotation "
-                                 f"({nsets * nexp * expert_bytes / 1e6:.0f} MB)", "entries_per_group": list(ms_list),
+                                 f"1024->2560, 16 groups x m entries (m = 1/4/8); calls rotate over {len(slots)} "
+                                 f"(expert set, routing) pairs, {nsets} sets x {z['nroutes']} routings with disjoint "
+                                 f"experts ({nsets * z['touched'] / 1e6:.0f} MB read per rotation)",
+                     "entries_per_group": list(ms_list),
                      "hip_graph": use_graph})
     out.update({"us_per_call": us, "gbps_per_call": gbps,
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -421,7 +430,8 @@ GROUPED_M = (1, 4, 8)
 def pmc_probe(torch, M, workload):
     """Three plain device copies of CALIB_BYTES, then one cold pass of `workload` with no graphs,
     so that every launch is a dispatch of its own: the headline GEMV once per weight copy at 1, 4
-    and 8 columns; the grouped decode once per expert set at m = 1, 4, 8; the prefill call twice."""
+    and 8 columns; the grouped decode once per rotation slot at m = 1, 4, 8; the prefill call
+    twice."""
     import synth
     dev = torch.device("cuda", 0)
     if workload == "gemv":
@@ -439,12 +449,12 @@ def pmc_probe(torch, M, workload):
                 for w in copies:
                     M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
     elif workload == "grouped":
-        sets, _, call, _, _, _ = grouped_setup(torch, M)
+        slots, _, call, _, _, _ = grouped_setup(torch, M)
 
         def run():
             for m in GROUPED_M:
-                for st in sets:
-                    call(m, st)
+                for sl in slots:
+                    call(m, sl)
     elif workload == "prefill":
         call, _, _ = prefill_setup(torch, M)
 

@@ -25,7 +25,7 @@ Q8_1_BYTES = 36
 __all__ = [
     "Q8_0", "IQ4_NL", "CB3", "BLOCK_VALUES", "BLOCK_BYTES", "Q8_1_BYTES",
     "rng_for", "row_bytes", "fp16_scales", "q8_0_weights", "iq4nl_weights",
-    "cb3_weights", "cb3_grid", "weights", "activations", "decode_routing",
+    "cb3_weights", "cb3_grid", "weights", "activations", "decode_routing", "decode_routings",
     "prefill_routing", "prefill_tokens", "SEEDS",
 ]
 
@@ -108,6 +108,21 @@ def decode_routing(rng: np.random.Generator, nexperts: int, ngroups: int, m: int
     off = (np.arange(ngroups + 1, dtype=np.int32) * m).astype(np.int32)
     cols = np.tile(np.arange(m, dtype=np.int32), ngroups)
     return experts, off, cols
+
+
+def decode_routings(rng: np.random.Generator, nexperts: int, ngroups: int, m: int, count: int):
+    """``count`` grouped decode routings as decode_routing, the experts of successive routings
+    drawn without replacement from one permutation of all experts (disjoint while
+    ``count * ngroups <= nexperts``; a fresh permutation after that)."""
+    out, perm = [], np.empty(0, dtype=np.int32)
+    for _ in range(count):
+        if perm.size < ngroups:
+            perm = rng.permutation(nexperts).astype(np.int32)
+        experts, perm = perm[:ngroups].copy(), perm[ngroups:]
+        off = (np.arange(ngroups + 1, dtype=np.int32) * m).astype(np.int32)
+        cols = np.tile(np.arange(m, dtype=np.int32), ngroups)
+        out.append((experts, off, cols))
+    return out
 
 
 def prefill_routing(rng: np.random.Generator, ntok: int, nexperts: int, topk: int):
