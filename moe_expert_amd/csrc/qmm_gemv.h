@@ -161,18 +161,58 @@ struct ActStage {
         const bool ok = c < ncp && src >= 0 && src < ncols;
         load_blocks(xr, act, (uint32_t)((ok ? src : 0) * act.nb + b0), b0, ok, zero_off);
     }
+    // A use of every loaded value (on a path that needs none of them, so that the loads are not
+    // moved onto the other paths).
+    __device__ __forceinline__ void keep() const {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) asm volatile("" ::"v"(h[j]), "v"(q0[j]), "v"(q1[j]));
+    }
+    // LDS addresses of the first pair of thread t: its int8 values, (si NC + c) 32 L + 16 l, and
+    // its scale (the next pairs lie 32 TH and 4 TH bytes on).
+    __device__ __forceinline__ static uint8_t* q_at(const ActLds& act, uint32_t t) {
+        return act.base + 16u * (t + (t & ~(uint32_t)(LPR - 1)));
+    }
+    __device__ __forceinline__ static float* d_at(const ActLds& act, uint32_t t) {
+        const uint32_t c = (t >> kLogL) & (NC - 1), l = t & (LPR - 1), si = t >> (kLogL + kLogN);
+        return (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
+    }
     // Unconditional too: keeping the stores unconditional keeps the loads where they are
     // written (otherwise the compiler sinks them into the store's branch, behind the weight
     // loads).
     __device__ __forceinline__ void store(const ActLds& act) {
-        const uint32_t t = threadIdx.x, c = (uint32_t)col(), l = t & (LPR - 1), si = t >> (kLogL + kLogN);
-        uint8_t* dq = act.base + 16u * (t + (t & ~(uint32_t)(LPR - 1)));  // (si NC + c) 32 L + 16 l
-        float* dd = (float*)(act.base + act.dbyte + ((si * (NC / G) + c / G) * LPR + l) * (4u * G) + 4u * (c % G));
+        uint8_t* dq = q_at(act, threadIdx.x);
+        float* dd = d_at(act, threadIdx.x);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             *(u32x4*)(dq + 32 * TH * j) = q0[j];
             *(u32x4*)(dq + 32 * TH * j + 16 * LPR) = q1[j];
             dd[TH * j] = h2f(h[j]);
+        }
+    }
+    // Re-staging within the area: pass column col() takes the pairs that column `src` of the
+    // area holds (zeros where !ok).  Every thread reads (read_column), a barrier, every thread
+    // writes (store_column): a column may feed several pass columns, or none.
+    __device__ __forceinline__ void read_column(const ActLds& act, int src, bool ok, float (&d)[NS]) {
+        const uint32_t t = threadIdx.x;
+        const uint32_t ts = (t & ~((uint32_t)(NC - 1) << kLogL)) | ((uint32_t)(ok ? src : 0) << kLogL);
+        const uint8_t* sq = q_at(act, ts);
+        const float* sd = d_at(act, ts);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            q0[j] = ok ? *(const u32x4*)(sq + 32 * TH * j) : z;
+            q1[j] = ok ? *(const u32x4*)(sq + 32 * TH * j + 16 * LPR) : z;
+            d[j] = ok ? sd[TH * j] : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void store_column(const ActLds& act, const float (&d)[NS]) {
+        uint8_t* dq = q_at(act, threadIdx.x);
+        float* dd = d_at(act, threadIdx.x);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            *(u32x4*)(dq + 32 * TH * j) = q0[j];
+            *(u32x4*)(dq + 32 * TH * j + 16 * LPR) = q1[j];
+            dd[TH * j] = d[j];
         }
     }
 };

@@ -71,6 +71,7 @@ __device__ __forceinline__ uint32_t* cb3_signed_lds() {
 // State of one gate/up workgroup and one pass over entries [c0, c0 + 8) of its group.
 template <int WT, int U, bool MULTI, int NS>
 struct GuWorkgroup {
+    using Stage = ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads>;
     const ActLds act;
     float* gl;  // [8][32] gate sums
     float* ul;  // [8][32] up sums
@@ -83,21 +84,31 @@ struct GuWorkgroup {
     uint8_t* hq;
     float *sums, *dbg;
 
-    // FIRST: the workgroup's first pass (builds the signed codebook); VAR: the row engine's
-    // straight-line copies per pass width (the later passes, rare, take the full-width copy,
-    // whose columns are bitwise the same).
-    template <bool FIRST, bool VAR>
-    __device__ __forceinline__ void pass(int c0) {
+    // FIRST: the workgroup's first pass (builds the signed codebook from gword); VAR: the row
+    // engine's straight-line copies per pass width (the later passes, rare, take the full-width
+    // copy, whose columns are bitwise the same); DENSE (first pass only): `pre` holds the loads
+    // of activation columns 0 .. 7 (all of them), issued before the group was known; they are
+    // staged as they are and re-staged in LDS to the pass's entry columns unless those are
+    // 0, 1, 2, ... already.  Otherwise the pass loads its entry columns once their indices are
+    // known.
+    template <bool FIRST, bool VAR, bool DENSE>
+    __device__ __forceinline__ void pass(int c0, Stage& pre, uint32_t gword) {
+        static_assert(FIRST || !DENSE, "the activations loaded up front serve the first pass");
         const int ncp = k1 - c0 < kGroupPass ? k1 - c0 : kGroupPass;
         // The row engine is rebuilt each pass from values the compiler cannot see through, so
         // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
         // in registers, or spill it, across the whole loop).
         RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, VAR, 0, true> eng(
             wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden, (int)IQ4Consts::opaque_u((uint32_t)l16));
-        ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads> stage;
-        stage.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
-        uint32_t gword = 0;
-        if constexpr (WT == kCB3 && FIRST) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
+        Stage own;
+        int ecol[kGroupPass];  // DENSE: the pass's entry columns, read now, needed after the staging
+        if constexpr (DENSE) {
+#pragma unroll
+            for (int k = 0; k < kGroupPass; ++k) ecol[k] = entry_col[c0 + (k < ncp ? k : 0)];
+        } else {
+            own.load_entries(xr, act, ncp, entry_col, c0, xq_cols, xqbytes);
+        }
+        Stage& stage = DENSE ? pre : own;
         __builtin_amdgcn_sched_barrier(0);
         eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
         __builtin_amdgcn_sched_barrier(0);
@@ -117,6 +128,26 @@ struct GuWorkgroup {
             dst[1] = u32x4{v[4], v[5], v[6], v[7]};
         }
         lds_barrier();
+        if constexpr (DENSE) {
+            // pass column k reads activation column ecol[k] (zeros outside [0, xq_cols))
+            const int cl = Stage::col();
+            int src = 0, moved = 0;
+#pragma unroll
+            for (int k = 0; k < kGroupPass; ++k) {
+                // (kept here: computed early, each use would wait for its load before the next
+                // load was issued)
+                asm volatile("" : "+s"(ecol[k]));
+                src = cl == k ? ecol[k] : src;
+                moved |= k < ncp ? ecol[k] ^ k : 0;
+            }
+            if (moved) {
+                float d[NS];
+                stage.read_column(act, src, cl < ncp && src >= 0 && src < xq_cols, d);
+                lds_barrier();
+                stage.store_column(act, d);
+                lds_barrier();
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
 
         float acc[kGroupPass];
@@ -147,7 +178,7 @@ struct GuWorkgroup {
     }
 };
 
-template <int WT, int U, bool MULTI, int NS>
+template <int WT, int U, bool MULTI, int NS, bool DENSE>
 __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
     int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
@@ -155,11 +186,23 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
     float* __restrict__ dbg_u) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    GroupInfo gi;
-    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
     static_assert(WT != kCB3 || kCB3SignedWords == 8 * kGuThreads, "eight codebook words per thread");
-
     const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
+    // Loads that need nothing from the group first (their latency then overlaps the group
+    // lookup's): with at most 8 activation columns (DENSE), all of them; the codebook entry.
+    typename GuWorkgroup<WT, U, MULTI, NS>::Stage pre;
+    if constexpr (DENSE) pre.load(make_rsrc(xq, xqbytes), act, 0, xq_cols, xqbytes);
+    uint32_t gword = 0;
+    if constexpr (WT == kCB3) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
+    __builtin_amdgcn_sched_barrier(0);
+    GroupInfo gi;
+    if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) {
+        // (a use on this path too, so the loads above are not moved behind the group lookup)
+        if constexpr (DENSE) pre.keep();
+        asm volatile("" ::"v"(gword));
+        return;
+    }
+
     float* gl = (float*)act_lds_end<NS, kGuThreads>(act);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -178,11 +221,11 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
     // The first pass outside the loop: its loads start with nothing outstanding.  Later passes
     // first wait for the previous pass's memory operations (which the compiler would otherwise
     // count as outstanding across the loop) and LDS reads.
-    w.template pass<true, true>(gi.k0);
+    w.template pass<true, true, DENSE>(gi.k0, pre, gword);
     for (int c0 = gi.k0 + kGroupPass; c0 < gi.k1; c0 += kGroupPass) {
         vm_drain();
         lds_barrier();
-        w.template pass<false, false>(c0);
+        w.template pass<false, false, false>(c0, pre, 0);
     }
 }
 
@@ -271,10 +314,13 @@ static int launch_grouped(const GroupedArgs& a) {
     {
         const size_t lds = gu_lds_bytes(a.hidden);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
+        // at most 8 activation columns: load them all before the group lookup
+        const bool dense = a.xq_cols <= kGroupPass;
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
-            hipLaunchKernelGGL((gu_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up,
-                               a.gu_stride, gu_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes,
-                               a.xq_cols, a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
+            auto kern = dense ? gu_kernel<WT, U, MULTI, NS, true> : gu_kernel<WT, U, MULTI, NS, false>;
+            hipLaunchKernelGGL(kern, grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up, a.gu_stride, gu_bytes,
+                               a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes, a.xq_cols,
+                               a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
         const Chunk ch = gu_chunk(a.hidden);
         const int ns = gu_slots(a.hidden);

@@ -164,3 +164,30 @@ def test_grouped_skips_bad_groups_and_columns():
     assert np.isnan(yh[2:4]).all()
     assert (yh[5] == 0).all()
     assert np.isfinite(yh[[0, 1, 4]]).all()
+
+
+@pytest.mark.parametrize("ncols", [6, 12])
+def test_grouped_column_maps(ncols):
+    """Entry columns in any order, repeated and out of range, with at most 8 activation columns
+    (all staged before the group lookup, then re-staged in LDS to the pass's entry columns) and
+    with more (each pass loads its entry columns); groups of 4, 9 (two passes) and 2 entries.
+    The oracle reads an out-of-range entry from an appended all-zero q8_1 column."""
+    print(f"grouped column maps: {ncols} activation columns", flush=True)
+    ex = Experts(860, 4, 1024, 64)
+    ge = np.array([1, 3, 0], np.int32)
+    go = np.array([0, 4, 13, 15], np.int32)
+    ec = synth.rng_for(861 + ncols).integers(-2, ncols + 2, size=15).astype(np.int32)
+    ec[0], ec[1] = ec[1], ec[1]                   # a repeated column in the first pass
+    x = synth.activations(synth.rng_for(862 + ncols), ncols, ex.hidden)
+    xq = M.qmm_quantize_q8_1(dev(x))
+    xq_h = host(xq)
+    y, ws = ex.run_gpu(xq, ge, go, ec)
+    hq, g, u = ex.split_ws(ws, ec.size)
+    xq_z = np.concatenate([xq_h, np.zeros((1, xq_h.shape[1]), np.uint8)])
+    ec_z = np.where((ec >= 0) & (ec < ncols), ec, ncols).astype(np.int32)
+    ref = ex.oracle(xq_z, ge, go, ec_z)
+    entry_expert = np.repeat(ge, np.diff(go))
+    stats = check_grouped(ref, host(y), hq, g.astype(np.float64), u.astype(np.float64),
+                          lambda k: ex.wd_exact(int(entry_expert[k])), ex.inter, depth_of(ex.hidden))
+    print("grouped check:", stats, flush=True)
+    assert ((ec < 0) | (ec >= ncols)).any() and (ec[:4] != np.arange(4)).any()
