@@ -135,6 +135,27 @@ def quant_bytes(k, n):
     return n * k * 4 + n * (k // 32) * 36
 
 
+def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
+    """The same cold rotation read by the library's plain streaming-read kernel (one launch per
+    copy, no compute): the best per-launch time over a few grid sizes, the reference for what
+    one launch reading this many bytes can reach."""
+    n16 = nbytes // 16 * 16
+    best = None
+    for grid in (256, 512, 1024, 2048):
+        out = torch.empty(grid * 256, dtype=torch.int32, device=copies[0].device)
+
+        def batch():
+            for w in copies:
+                M.qmm_debug_stream_read(w, n16, grid, out=out)
+        t = timed_graph(torch, batch, reps, use_graph) * 1e3 / len(copies)
+        if best is None or t < best[0]:
+            best = (t, grid)
+    us, grid = best
+    gbps = n16 / (us * 1e-6) / 1e9
+    return {"bytes": n16, "us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "grid": grid, "kernel": "qmm_debug_stream_read (16-byte loads, 8 in flight per thread)"}
+
+
 def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndistinct=6):
     import synth
     wbytes = nrows * synth.row_bytes(wtype, k)
@@ -183,6 +204,7 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                 M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
         literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
+    floor = stream_read_reference(torch, M, copies, wbytes, use_graph, args.batch_reps)
     rec = recorded_traffic(f"gemv:{wtype}:{nrows}x{k}")
     traffic = None
     if rec and all(str(n) in rec["bytes_per_launch"] for n in cols):
@@ -192,7 +214,7 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                                  f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
                      "weight_copies": ncopies, "hip_graph": use_graph})
     out.update({"us_per_call": us, "gbps_per_call": gbps, "warm_us_per_call": warm,
-                f"rotation_{ndistinct}_copies_us_per_call": literal,
+                f"rotation_{ndistinct}_copies_us_per_call": literal, "hbm_read_reference": floor,
                 "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                              "algorithmic_bytes_per_launch": round(tot_b / len(cols)),

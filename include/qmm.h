@@ -111,6 +111,15 @@ int qgemv_dense(int wtype, const void* w, const uint8_t* grid, int64_t nrows, in
 int qmm_debug_block_sums(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
                          const void* xq, int ncols, int32_t* sums, void* stream);
 
+/* Measurement hook: a plain streaming read of nbytes from p in one launch of `grid`
+ * workgroups of 256 threads (16-byte loads, eight in flight per thread, no other work): the
+ * reference for the HBM time of the decode kernels at the same byte count.  Thread t writes the
+ * XOR of the words it read to out[t].
+ *   p    : device, 16-byte aligned; nbytes a multiple of 16.
+ *   out  : device uint32 [grid * 256], 4-byte aligned.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EHIP. */
+int qmm_debug_stream_read(const void* p, uint64_t nbytes, uint32_t* out, int grid, void* stream);
+
 /* Workspace bytes qgemv_grouped_experts needs (host). */
 size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned flags);
 

@@ -22,7 +22,7 @@ QMM_FLAG_DEBUG_INTERMEDIATES = 1
 BLOCK_VALUES = {QMM_Q8_0: 32, QMM_IQ4_NL: 32, QMM_CB3: 256}
 BLOCK_BYTES = {QMM_Q8_0: 34, QMM_IQ4_NL: 18, QMM_CB3: 110}
 
-_P, _I64, _I32, _U32, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_uint, C.c_size_t
+_P, _I64, _I32, _U32, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_uint, C.c_uint64, C.c_size_t
 SIGNATURES = {
     "qmm_version": (_I32, []),
     "qmm_status_str": (C.c_char_p, [_I32]),
@@ -31,6 +31,7 @@ SIGNATURES = {
     "qmm_dequant_f16": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I64, _P]),
     "qgemv_dense": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qmm_debug_block_sums": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
+    "qmm_debug_stream_read": (_I32, [_P, _U64, _P, _I32, _P]),
     "qgemv_grouped_experts_workspace": (_SZ, [_I64, _I32, _U32]),
     "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
                                      _P, _P, _I32, _P, _I32, _P, _P, _SZ, _U32, _P]),
@@ -140,6 +141,17 @@ def qmm_debug_block_sums(wtype, w, nrows, k, xq, ncols, grid=None, out=None, str
         out = torch.empty((ncols, nrows, k // 32), dtype=torch.int32, device=w.device)
     _check("qmm_debug_block_sums", lib().qmm_debug_block_sums(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(xq), ncols,
                                                              _ptr(out), _stream(stream)))
+    return out
+
+
+def qmm_debug_stream_read(p, nbytes, grid, out=None, stream=None):
+    """Plain streaming read of the first nbytes of device tensor p in one launch of `grid`
+    256-thread workgroups (the HBM reference); returns out (uint32 [grid * 256])."""
+    import torch
+    _dev(p, "p")
+    if out is None:
+        out = torch.empty(grid * 256, dtype=torch.int32, device=p.device)
+    _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid, _stream(stream)))
     return out
 
 

@@ -114,3 +114,21 @@ def test_ldy_padding():
     assert (yh[:, 50:] == 7.0).all()
     ref, a = oracle.gemv(M.QMM_IQ4_NL, w, 512, host(xq))
     check_tol(yh[:, :50], ref, a)
+
+
+def test_stream_read_reference():
+    """The streaming-read reference kernel reads every 16-byte chunk once: thread t's word is the
+    XOR of the chunks t, t + T, t + 2T, ... (T = grid * 256 threads)."""
+    import torch
+    print("stream read reference", flush=True)
+    rng = np.random.default_rng(5)
+    nbytes, grid = 3 * 65536 + 48, 3
+    buf = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    out = host(M.qmm_debug_stream_read(dev(buf), nbytes, grid)).view(np.uint32)
+    words = buf.view(np.uint32).reshape(-1, 4)
+    chunk = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
+    nt = grid * 256
+    ref = np.zeros(nt, np.uint32)
+    for t in range(nt):
+        ref[t] = np.bitwise_xor.reduce(chunk[t::nt]) if t < chunk.size else 0
+    assert np.array_equal(out, ref)
