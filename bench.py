@@ -393,6 +393,21 @@ def prefill_setup(torch, M):
     return call, host, dict(nexp=nexp, ntok=ntok, topk=topk, hidden=hidden, inter=inter, nent=nent)
 
 
+def mfma_reference(torch, M, reps):
+    """Rate of the prefill GEMM's MFMA instruction in the library's register-only loop (8
+    independent accumulators per wave, 4 waves per workgroup, 8 workgroups per CU, no memory):
+    the rate this chip sustains for that instruction, set beside the published peak."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 8 * ncu, 4000
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    M.qmm_debug_mfma_loop(grid, iters, out=out)
+    ms = timed_graph(torch, lambda: M.qmm_debug_mfma_loop(grid, iters, out=out), reps, False)
+    flops = grid * 4 * 8 * iters * 32 * 32 * 16 * 2
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "ms": round(ms, 3),
+            "kernel": "qmm_debug_mfma_loop (v_mfma_f32_32x32x16_f16, 8 accumulators per wave, registers only)"}
+
+
 def bench_prefill(args, torch, M):
     import numpy as np
 
@@ -411,6 +426,7 @@ def bench_prefill(args, torch, M):
                                  "IQ4_NL gate/up 2560->1024, Q8_0 down 1024->2560, FP16 dequant in LDS + fp16 MFMA",
                      "tokens": ntok, "entries": int(nent), "hip_graph": use_graph})
     rec = recorded_traffic("prefill")
+    out["mfma_reference"] = mfma_reference(torch, M, args.batch_reps)
     out.update({"us_per_call": round(ms * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),

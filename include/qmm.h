@@ -120,6 +120,13 @@ int qmm_debug_block_sums(int wtype, const void* w, const uint8_t* grid, int64_t 
  * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EHIP. */
 int qmm_debug_stream_read(const void* p, uint64_t nbytes, uint32_t* out, int grid, void* stream);
 
+/* Measurement hook: `grid` workgroups of 256 threads, each wave running 8 independent fp16 MFMA
+ * accumulators (v_mfma_f32_32x32x16_f16, 32768 FLOP each) for `iters` rounds from registers
+ * only: grid * 4 * 8 * iters * 32768 FLOP, the reference for the prefill GEMM's MFMA rate.
+ *   out : device float [grid * 256] (the lanes' accumulator sums), 4-byte aligned.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EHIP. */
+int qmm_debug_mfma_loop(float* out, int grid, int iters, void* stream);
+
 /* Workspace bytes qgemv_grouped_experts needs (host). */
 size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, unsigned flags);
 

@@ -32,6 +32,7 @@ SIGNATURES = {
     "qgemv_dense": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qmm_debug_block_sums": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "qmm_debug_stream_read": (_I32, [_P, _U64, _P, _I32, _P]),
+    "qmm_debug_mfma_loop": (_I32, [_P, _I32, _I32, _P]),
     "qgemv_grouped_experts_workspace": (_SZ, [_I64, _I32, _U32]),
     "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
                                      _P, _P, _I32, _P, _I32, _P, _P, _SZ, _U32, _P]),
@@ -152,6 +153,16 @@ def qmm_debug_stream_read(p, nbytes, grid, out=None, stream=None):
     if out is None:
         out = torch.empty(grid * 256, dtype=torch.int32, device=p.device)
     _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid, _stream(stream)))
+    return out
+
+
+def qmm_debug_mfma_loop(grid, iters, out=None, device="cuda", stream=None):
+    """Register-only fp16 MFMA loop (grid * 4 * 8 * iters * 32768 FLOP); returns out (float
+    [grid * 256])."""
+    import torch
+    if out is None:
+        out = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    _check("qmm_debug_mfma_loop", lib().qmm_debug_mfma_loop(_ptr(out), grid, iters, _stream(stream)))
     return out
 
 

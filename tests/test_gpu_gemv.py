@@ -132,3 +132,28 @@ def test_stream_read_reference():
     for t in range(nt):
         ref[t] = np.bitwise_xor.reduce(chunk[t::nt]) if t < chunk.size else 0
     assert np.array_equal(out, ref)
+
+
+def test_mfma_loop_reference():
+    """The MFMA reference loop computes what its operands give: thread t (lane l = t mod 64 of
+    its wave) holds A[l mod 32][8 (l div 32) + e] = (t + e) mod 8 and B[8 (l div 32) + e][l mod
+    32] = (3 t + e) mod 8, and D register r is D[8 (r div 4) + 4 (l div 32) + r mod 4][l mod 32];
+    out[t] = 8 chains x iters x the sum of its D registers (small integers: exact)."""
+    print("mfma loop reference", flush=True)
+    grid, iters = 2, 3
+    out = host(M.qmm_debug_mfma_loop(grid, iters))
+    ref = np.zeros(grid * 256)
+    for w0 in range(0, 256, 64):
+        t = np.arange(w0, w0 + 64)
+        l = t % 64
+        A = np.zeros((32, 16))
+        B = np.zeros((16, 32))
+        for e in range(8):
+            A[l % 32, 8 * (l // 32) + e] = (t + e) % 8
+            B[8 * (l // 32) + e, l % 32] = (3 * t + e) % 8
+        D = A @ B
+        for li in range(64):
+            rows = [8 * (r // 4) + 4 * (li // 32) + r % 4 for r in range(16)]
+            ref[w0 + li] = 8 * iters * D[rows, li % 32].sum()
+    ref[256:] = ref[:256]
+    assert np.array_equal(out, ref.astype(np.float32))
