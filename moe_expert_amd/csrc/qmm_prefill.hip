@@ -442,7 +442,8 @@ __device__ __forceinline__ void epi_put(const f32x16 (&acc)[MB], int q, float* t
 // (H16 = fp16(silu(G) U)) and writes them with one 16-byte store.
 template <int WT, int MB>
 __device__ __forceinline__ void gateup_tile(const GuArgs& p, const Tile& t, int y, uint8_t* lds) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: the weight resource is picked per wave
     uint32_t a_off[4];
     token_rows(p.sorted_tok, t, p.ntok, p.hidden, p.xbytes, a_off);
     const int col = y * kPfGuCols + 32 * (w & 3) + (lane & 31);

@@ -103,6 +103,29 @@ def test_onehot_rows_exact(wtype):
     assert np.array_equal(y, ref.astype(np.float32)), np.abs(y - ref).max()
 
 
+@pytest.mark.parametrize("wtype,nrows,k,cols,key", [
+    (M.QMM_Q8_0, 512, 2560, (1,), "q8_0_tiny"),
+    (M.QMM_IQ4_NL, 8192, 2560, (1, 2, 4, 8), "iq4nl_8192x2560"),
+    (M.QMM_Q8_0, 12288, 2560, (1, 2, 3, 4), "q8_0_12288x2560"),
+    (M.QMM_Q8_0, 2560, 6144, (7, 8), "q8_0_2560x6144"),
+])
+def test_gemv_full_sizes(wtype, nrows, k, cols, key):
+    """The benchmark's GEMV workloads at their full sizes and column counts, with the benchmark's
+    first weight copy and activations: every output within the fp32 tolerance of the oracle."""
+    print(f"gemv full size {key}: {nrows}x{k} at {cols} columns", flush=True)
+    seed = synth.SEEDS[key]
+    w = synth.weights(wtype, synth.rng_for(seed), nrows, k)
+    x = synth.activations(synth.rng_for(seed + 100), max(cols), k)
+    wd = dev(w)
+    for n in cols:
+        xq = M.qmm_quantize_q8_1(dev(x[:n]))
+        y = host(M.qgemv_dense(wtype, wd, nrows, k, xq, n))
+        xq_h = host(xq)
+        assert np.array_equal(xq_h, oracle.quantize_q8_1(x[:n]))
+        ref, a = oracle.gemv(wtype, w, k, xq_h)
+        check_tol(y, ref, a, what=f"gemv {key} n={n}")
+
+
 def test_ldy_padding():
     print("ldy padding", flush=True)
     import torch
