@@ -4,8 +4,9 @@ G, U: within the fp32 error of the MFMA accumulation (each product is exact in b
 passes through at most K/16 + 16 additions), asserted.  H16 = fp16(silu(G) U): equal to the
 oracle's where the binary16 rounding is decided by the oracle's G, U alone, otherwise inside the
 interval the bound allows; the interval is widened by 8 binary32 ulp for the device's binary32
-silu (expf within 1 ulp, one division, one product) against the oracle's binary64 exp.  Y:
-within 1e-4 * sum|w h| plus the effect of the validated H16 differences.  Full size (8192
+silu (expf within 1 ulp, v_rcp_f32 of 1 + e within 1 ulp, two products) against the
+oracle's binary64 exp.  Y: within 1e-4 * sum|w h| plus the effect of the validated H16
+differences.  Full size (8192
 tokens x 2560, 128 experts, top-8) is checked on sampled entries, including every entry of
 an expert split into several tiles."""
 import numpy as np
