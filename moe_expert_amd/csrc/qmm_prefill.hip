@@ -351,20 +351,32 @@ __device__ __forceinline__ void pf_gemm(rsrc_t ar, const uint32_t (&a_off)[4], r
     BPrep<WT> P;
     u32x4 Fa, Fb;
     half8 a0[MB], a1[MB];
-    // prologue: stages 0, 1, 2 filled; step 0's weights prepared and fragment 0 converted; raw
-    // weights of steps 1 and 2 loaded
+    // prologue, issued in this order: step 0's raw weights, stages 0, 1, 2, step 1's raw
+    // weights, then (once step 0's have landed and are prepared) step 2's.  Step 0 starts once
+    // stages 0 and 1 have landed (it reads slice 0 of stage 1 last), with stage 2 and the later
+    // weights still in flight: vmcnt(4 + 2 kBLoads) leaves outstanding only what was issued
+    // after stage 1.  Step 0's barrier waits for stage 2 (kWait, as in every step: issued after
+    // stage 2 are the raw weights of steps 1 and 2 and step 0's own loads).
+    R0.load(wr, b_row, 0, L.hh);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 3; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) L.fill(i, s * kPfStage, (uint32_t)min(s, L.last) * 128u);
-    R0.load(wr, b_row, 0, L.hh);
+    __builtin_amdgcn_sched_barrier(0);
     R1.load(wr, b_row, 2 * min(1, L.last), L.hh);
+    __builtin_amdgcn_sched_barrier(0);
     R0.prepare(b_row, 0, L.hh, P);
     R0.load(wr, b_row, 2 * min(2, L.last), L.hh);
+    __builtin_amdgcn_sched_barrier(0);
     P.convert(0, 0, L.kc, Fa);
     P.convert(0, 1, L.kc, Fa);
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the stage fills are not tracked
-    __syncthreads();
+    // (a plain barrier: a workgroup fence would wait for every stage fill)
+    constexpr int kPro = 4 + 2 * BRow<WT>::kLoads;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((kPro & 15) | ((kPro >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int m = 0; m < MB; ++m) a0[m] = L.read_a(0, 0, m);
     int ks = 0;
