@@ -548,22 +548,18 @@ __device__ __forceinline__ void down_tile(const DownArgs& p, const Tile& t, int 
     pf_gemm<WT, MB>(make_rsrc(p.h16, p.hbytes), a_off, make_rsrc_dw(p.wd + (int64_t)t.e * p.stride, p.expert_bytes),
                     roff, p.inter / kPfStepK, lds, acc);
 
-    // per 64-row quarter through LDS; each thread stores 4 consecutive outputs of a row at once
-    float* tile = (float*)lds;
-    const int c4 = (int)(threadIdx.x & 63) * 4;  // 4 columns of the 256
-    const int c0 = y * kPfDownCols + c4;
+    // Straight from the accumulators: register r of block m holds row 32 m + acc_row(lane, r),
+    // column col, so one store instruction writes 32 consecutive floats (128 bytes) of each of
+    // two rows.  No LDS round trip and no barrier.
+    if (col < p.hidden) {
+        float* yc = p.y + (int64_t)t.row0 * p.hidden + col;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (2 * q >= MB) break;
-        epi_put<MB>(acc, q, tile);
-        __syncthreads();
-#pragma unroll 1
-        for (int rr = (int)(threadIdx.x >> 6); rr < 64; rr += kPfThreads / 64) {
-            const int row = 64 * q + rr;
-            if (row < t.nrows && c0 < p.hidden)
-                *(f32x4*)(p.y + (int64_t)(t.row0 + row) * p.hidden + c0) = *(const f32x4*)(tile + rr * kPfEpiLd + c4);
-        }
-        __syncthreads();
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * m + acc_row(lane, r);
+                if (row < t.nrows) yc[(int64_t)row * p.hidden] = acc[m][r];
+            }
     }
 }
 
