@@ -135,6 +135,13 @@ def quant_bytes(k, n):
     return n * k * 4 + n * (k // 32) * 36
 
 
+def fused_bytes(wtype, nrows, k):
+    """Algorithmic bytes of the fused one-column call: every weight byte once, the fp32 column,
+    the fp32 outputs (the q8_1 column never leaves the workgroup)."""
+    import synth
+    return nrows * synth.row_bytes(wtype, k) + k * 4 + nrows * 4
+
+
 def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
     """The same cold rotation read by the library's plain streaming-read kernel (one launch per
     copy, no compute): the best per-launch time over a few grid sizes, the reference for what
@@ -171,16 +178,22 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
         M.qmm_quantize_q8_1(xs[n], out=xqs[n])
     torch.cuda.synchronize()
     use_graph = not args.no_graph
+    # one column: the call that quantizes inside the GEMV (rows of at most 96 blocks)
+    fused = not args.unfused and 1 in cols and k <= 3072
 
     def step(slot):
         w = copies[slot % ncopies]
         for n in cols:
+            if fused and n == 1:
+                M.qgemv_dense_f32(wtype, w, nrows, k, xs[1][0], y=ys[1][0])
+                continue
             M.qmm_quantize_q8_1(xs[n], out=xqs[n])
             M.qgemv_dense(wtype, w, nrows, k, xqs[n], n, y=ys[n])
 
     run_step = capture_slots(torch, step, ncopies) if use_graph else step
     ms = contract_steps(torch, run_step, args.steps, args.warmup)
-    step_bytes = sum(gemv_bytes(wtype, nrows, k, n) + quant_bytes(k, n) for n in cols)
+    step_bytes = sum(fused_bytes(wtype, nrows, k) if fused and n == 1 else gemv_bytes(wtype, nrows, k, n) +
+                     quant_bytes(k, n) for n in cols)
 
     us, gbps, warm, literal = {}, {}, {}, {}
     tot_b = tot_us = 0.0
@@ -204,6 +217,12 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                 M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
         literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
+    fused_us = None
+    if fused:
+        def fused_batch():
+            for w in copies:
+                M.qgemv_dense_f32(wtype, w, nrows, k, xs[1][0], y=ys[1][0])
+        fused_us = round(timed_graph(torch, fused_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     floor = stream_read_reference(torch, M, copies, wbytes, use_graph, args.batch_reps)
     rec = recorded_traffic(f"gemv:{wtype}:{nrows}x{k}")
     traffic = None
@@ -212,7 +231,10 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
     out = base_line(metric, step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
                     {"workload": f"{name}, cold rotation of {ncopies} weight copies "
                                  f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
-                     "weight_copies": ncopies, "hip_graph": use_graph})
+                     "weight_copies": ncopies, "hip_graph": use_graph,
+                     "one_column_call": "fp32 column, q8_1 inside the GEMV" if fused else "q8_1 quantizer + GEMV"})
+    if fused:
+        out["fused_1col_us_per_call"] = fused_us
     out.update({"us_per_call": us, "gbps_per_call": gbps, "warm_us_per_call": warm,
                 f"rotation_{ndistinct}_copies_us_per_call": literal, "hbm_read_reference": floor,
                 "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -593,6 +615,7 @@ def main() -> int:
     ap.add_argument("--workload", default="gemv", choices=["gemv", "q8_0", "grouped", "prefill"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="one-column GEMV calls as quantizer + q8_1 GEMV")
     ap.add_argument("--batch-reps", type=int, default=5)
     ap.add_argument("--pmc-probe", action="store_true", help="launch sequence for the counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

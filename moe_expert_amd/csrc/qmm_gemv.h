@@ -447,15 +447,75 @@ __device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
     return v;
 }
 
+// One fp32 activation column quantized to q8_1 inside the workgroup, into the layout the
+// one-column ActStage writes (16 lanes per row, one staging slot: block b's int8 values at
+// q_at(b), q_at(b) + 16 LPR, its scale at d_at(b)).  Eight lanes per 32-value block, four
+// consecutive values per lane (one 16-byte load), 32 blocks a pass over the 256 threads;
+// blocks past the column (up to 96) read and stage zeros.  The arithmetic is the q8_1
+// quantizer's [DQ, Change]: amax over the block (exact in any order), d = amax / 127 and
+// q = x / d rounded half away from zero, IEEE binary32, clamped to +-127, so the staged bytes
+// equal the ones the standalone quantizer writes; only d (as fp16) is staged.
+template <int TH>
+struct F32Stage {
+    static constexpr int kBlocks = TH / 8;                       // per pass
+    static constexpr int kPass = (96 + kBlocks - 1) / kBlocks;  // rows of at most 96 blocks
+    u32x4 v[kPass];
+    __device__ __forceinline__ void load(rsrc_t xr, int nb, uint32_t zero_off) {
+        const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
+#pragma unroll
+        for (int p = 0; p < kPass; ++p) {
+            const uint32_t b = (uint32_t)p * kBlocks + h;
+            v[p] = ld128(xr, b < (uint32_t)nb ? b * 128u + 16u * j : zero_off);
+        }
+    }
+    template <int NS, int NC, int LPR>
+    __device__ __forceinline__ void store(const ActLds& act) {
+        static_assert(NC == 1 && NS == 1 && LPR == 16 && TH == 256, "one column, 16 lanes per row, one slot");
+        const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
+#pragma unroll
+        for (int p = 0; p < kPass; ++p) {
+            const uint32_t b = (uint32_t)p * kBlocks + h;
+            // (each element copied out first: __builtin_bit_cast of a vector element in place
+            // reads element 0 with this compiler)
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t e = v[p][i];
+                x[i] = __builtin_bit_cast(float, e);
+            }
+            float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                                         __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
+            // over the 8 lanes of the block: quad partners, the other pair of the quad, then the
+            // mirrored lane of the other quad in the half row
+            amax = __builtin_fmaxf(amax, dpp<0xB1>(amax));
+            amax = __builtin_fmaxf(amax, dpp<0x4E>(amax));
+            amax = __builtin_fmaxf(amax, dpp<0x141>(amax));
+            const float d = amax / 127.0f;
+            const bool zero = amax == 0.0f || d == 0.0f;
+            uint32_t w4 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int q = zero ? 0 : round_away(x[i] / d);
+                q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                w4 |= (uint32_t)(q & 0xFF) << (8 * i);
+            }
+            uint8_t* dq = ActStage<NS, NC, LPR, TH>::q_at(act, b);
+            *(uint32_t*)(dq + (j < 4 ? 4u * j : 16u * LPR + 4u * (j - 4))) = w4;
+            if (j == 0) *ActStage<NS, NC, LPR, TH>::d_at(act, b) = zero ? 0.0f : h2f(f2h(d));
+        }
+    }
+};
+
 // One workgroup's TH / 64 * (64 / LPR) rows starting at row0 of a decode GEMV pass: columns
 // [col0, col0 + ncp) of the q8_1 activations behind `xr` (xbytes long; column c is q8_1 blocks
 // c*K/32 ...),
 // results to y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  LPR lanes per
 // row (16 or 64).  Order of work: activation loads, then this lane's weight loads, then the
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
-// the weights arrive, cross-lane row sums.
+// the weights arrive, cross-lane row sums.  F32: `xr` holds one fp32 column instead, which
+// the workgroup quantizes to q8_1 itself (F32Stage).
 template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
-          bool VAR = false, int BUDGET = 100>
+          bool VAR = false, int BUDGET = 100, bool F32 = false>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, uint32_t xbytes,
                                           int col0, int ncp, float* y, int64_t ldy, int32_t* sums, int row0,
                                           uint32_t* lds) {
@@ -473,14 +533,17 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const uint32_t row_off = IQ4Consts::opaque_u((uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K));
 
     ActStage<NS, NC, LPR, TH> stage;
-    stage.load(xr, act, col0, ncp, xbytes);
+    F32Stage<TH> fstage;
+    if constexpr (F32) fstage.load(xr, act.nb, xbytes);
+    else stage.load(xr, act, col0, ncp, xbytes);
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
     RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR, BUDGET> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
-    stage.store(act);
+    if constexpr (F32) fstage.template store<NS, NC, LPR>(act);
+    else stage.store(act);
     if constexpr (WT == kCB3) gstage.store(lds_grid);
     __syncthreads();
     // the weight decode stays after the barrier (hoisted above it, each wave would wait for its

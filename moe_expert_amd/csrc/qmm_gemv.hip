@@ -31,6 +31,17 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                    xqbytes, col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
 }
 
+// One fp32 column, quantized to q8_1 by every workgroup for itself (16 x 256 shape, one slot).
+template <int WT, int U>
+__global__ __launch_bounds__(256) void gemv_f32_kernel(const uint8_t* __restrict__ w, uint32_t wbytes, int nrows, int K,
+                                                       const uint8_t* __restrict__ grid, const float* __restrict__ x,
+                                                       uint32_t xbytes, float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    gemv_tile<WT, false, 1, U, false, 1, 16, 256, false, 100, true>(make_rsrc_dw(w, wbytes), nrows, K, grid,
+                                                                    make_rsrc(x, xbytes), xbytes, 0, 1, y, nrows,
+                                                                    nullptr, blockIdx.x * 16, lds);
+}
+
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
 //   kWide   16 x 512: 32 rows, where 256 threads cannot stage the pass (and the block-sum hook)
 //   kNarrow 16 x 256: 16 rows, the default
@@ -140,9 +151,45 @@ static int check_gemv_args(int wtype, const void* w, const uint8_t* grid, int64_
     return QMM_OK;
 }
 
+// The fused one-column GEMV: rows of at most 96 blocks (16 lanes per row, chunks of 2, 5 or 6
+// blocks), in the 256-thread shape with one staging slot.
+template <int WT>
+static int launch_gemv_f32(const void* w, uint64_t wbytes, const uint8_t* grid, int64_t nrows, int64_t k,
+                           const float* x, float* y, hipStream_t st) {
+    const Chunk ch = pass_chunk(false, k);
+    if (pass_lpr(false, k) != 16 || ch.multi || k / 32 > 96) return QMM_EUNSUPPORTED;
+    if (gemv_shape(WT, false, k, 1) != kNarrow || stage_slots(k, 1, 256, 16, ch.u) != 1) return QMM_EUNSUPPORTED;
+    const dim3 grid_dim((unsigned)((nrows + 15) / 16));
+    const size_t lds = gemv_lds_bytes(WT, k, 1, 16, ch.u, 256);
+    const uint32_t xbytes = (uint32_t)(k * 4);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid_dim, dim3(256), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows, (int)k,
+                           grid, x, xbytes, y);
+    };
+    if (ch.u == 2) go(gemv_f32_kernel<WT, 2>);
+    else if (ch.u == 5) go(gemv_f32_kernel<WT, 5>);
+    else go(gemv_f32_kernel<WT, 6>);
+    return launch_status();
+}
+
 }  // namespace qmm
 
 using namespace qmm;
+
+extern "C" int qgemv_dense_f32(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k, const float* x,
+                               float* y, void* stream) {
+    uint64_t wbytes, xqbytes;
+    // (the shape and weight checks of the q8_1 GEMV; the column is at most 3072 fp32 values)
+    const int rc = check_gemv_args(wtype, w, grid, nrows, k, x, 1, y, &wbytes, &xqbytes);
+    if (rc) return rc;
+    if (!aligned(x, 4)) return QMM_EALIGN;
+    const hipStream_t st = as_stream(stream);
+    switch (wtype) {
+        case QMM_Q8_0: return launch_gemv_f32<kQ8_0>(w, wbytes, grid, nrows, k, x, y, st);
+        case QMM_IQ4_NL: return launch_gemv_f32<kIQ4_NL>(w, wbytes, grid, nrows, k, x, y, st);
+        default: return launch_gemv_f32<kCB3>(w, wbytes, grid, nrows, k, x, y, st);
+    }
+}
 
 extern "C" int qgemv_dense(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k, const void* xq,
                            int ncols, float* y, int64_t ldy, void* stream) {

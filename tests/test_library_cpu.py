@@ -63,6 +63,17 @@ def test_qgemv_dense_rejects(args, expect):
     assert M.lib().qgemv_dense(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, None, FAKE, None), -1),      # null activations
+    ((M.QMM_Q8_0, FAKE, None, 64, 2561, FAKE, FAKE, None), -1),      # k not a block multiple
+    ((M.QMM_CB3, FAKE, None, 64, 2560, FAKE, FAKE, None), -1),       # CB3 without a grid
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, ODD, FAKE, None), -3),       # misaligned activations
+    ((M.QMM_Q8_0, FAKE, None, 64, 3104, FAKE, FAKE, None), -2),      # rows of more than 96 blocks
+])
+def test_qgemv_dense_f32_rejects(args, expect):
+    assert M.lib().qgemv_dense_f32(*args) == expect
+
+
 def test_quantize_and_dequant_reject():
     L = M.lib()
     assert L.qmm_quantize_q8_1(None, 64, 1, 64, FAKE, None) == -1
