@@ -485,13 +485,20 @@ def bench_prefill(args, torch, M):
 
 PROBE_COLS = (1, 4, 8)
 GROUPED_M = (1, 4, 8)
+# the Q8_0 workloads: (rows, k, columns, seed key)
+Q8_SPECS = ((12288, 2560, (1, 2, 3, 4), "q8_0_12288x2560"), (2560, 6144, (7, 8), "q8_0_2560x6144"))
+
+
+def cold_copies(wbytes):
+    """Weight copies of a cold rotation: more than twice the memory-side cache, at least 6."""
+    return max(6, -(-2 * MALL_BYTES // wbytes) + 1)
 
 
 def pmc_probe(torch, M, workload):
     """Three plain device copies of CALIB_BYTES, then one cold pass of `workload` with no graphs,
     so that every launch is a dispatch of its own: the headline GEMV once per weight copy at 1, 4
-    and 8 columns; the grouped decode once per rotation slot at m = 1, 4, 8; the prefill call
-    twice."""
+    and 8 columns (the Q8_0 GEMVs likewise at their column counts); the grouped decode once per
+    rotation slot at m = 1, 4, 8; the prefill call twice."""
     import synth
     dev = torch.device("cuda", 0)
     if workload == "gemv":
@@ -508,6 +515,24 @@ def pmc_probe(torch, M, workload):
             for n in PROBE_COLS:
                 for w in copies:
                     M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
+    elif workload == "q8_0":
+        wt = synth.Q8_0
+        sets = []
+        for nrows, k, cols, key in Q8_SPECS:
+            wbytes = nrows * synth.row_bytes(wt, k)
+            host = [synth.weights(wt, synth.rng_for(synth.SEEDS[key] + i), nrows, k) for i in range(6)]
+            copies = [torch.from_numpy(host[i % 6]).to(dev) for i in range(cold_copies(wbytes))]
+            rng = synth.rng_for(synth.SEEDS[key] + 100)
+            xs = synth.activations(rng, max(cols), k)
+            xq = {n: M.qmm_quantize_q8_1(torch.from_numpy(xs[:n].copy()).to(dev)) for n in cols}
+            y = {n: torch.empty((n, nrows), dtype=torch.float32, device=dev) for n in cols}
+            sets.append((nrows, k, cols, copies, xq, y))
+
+        def run():
+            for nrows, k, cols, copies, xq, y in sets:
+                for n in cols:
+                    for w in copies:
+                        M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
     elif workload == "grouped":
         slots, _, call, _, _, _ = grouped_setup(torch, M)
 
@@ -541,7 +566,8 @@ def pmc_summary(workload, fetch_csv, write_csv):
     import re
 
     import synth
-    pattern = {"gemv": r"gemv_kernel<\d+, false, (\d+),", "grouped": r"(gu_kernel|down_kernel)",
+    pattern = {"gemv": r"gemv_kernel<\d+, false, (\d+),", "q8_0": r"gemv_kernel<\d+, false, (\d+),",
+               "grouped": r"(gu_kernel|down_kernel)",
                "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)"}[workload]
 
     def per_kernel(path, counter):
@@ -565,6 +591,26 @@ def pmc_summary(workload, fetch_csv, write_csv):
         return sum(v) / len(v)
 
     rec = {"fetch_scale": round(ff, 4), "write_scale": round(wf, 4), "calibration_bytes": CALIB_BYTES}
+    if workload == "q8_0":
+        # dispatch order: per matrix, per column count, one launch per weight copy
+        i = 0
+        for nrows, k, cols, _ in Q8_SPECS:
+            nc = cold_copies(nrows * synth.row_bytes(synth.Q8_0, k))
+            r = dict(rec)
+            fetch, write = {}, {}
+            for n in cols:
+                fetch[n] = mean([v for _, v in fk[i:i + nc]])
+                write[n] = mean([v for _, v in wk[i:i + nc]])
+                i += nc
+            r["algorithmic_bytes"] = {str(n): gemv_bytes(synth.Q8_0, nrows, k, n) for n in cols}
+            r["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
+            r["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
+            r["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in cols}
+            r["source_sha256"] = source_digest()
+            store_traffic(f"gemv:{synth.Q8_0}:{nrows}x{k}", r)
+        if i != len(fk) or len(fk) != len(wk):
+            raise SystemExit(f"expected {i} GEMV dispatches, found {len(fk)} / {len(wk)}")
+        return
     if workload == "gemv":
         fetch = {n: mean([v for g, v in fk if int(g) == n]) for n in PROBE_COLS}
         write = {n: mean([v for g, v in wk if int(g) == n]) for n in PROBE_COLS}
@@ -596,6 +642,10 @@ def pmc_summary(workload, fetch_csv, write_csv):
     rec["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
     rec["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in fetch}
     rec["source_sha256"] = source_digest()
+    store_traffic(key, rec)
+
+
+def store_traffic(key, rec):
     try:
         with open(TRAFFIC_FILE) as fh:
             allrec = json.load(fh)
