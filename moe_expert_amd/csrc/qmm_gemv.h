@@ -450,8 +450,9 @@ __device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
 // One fp32 activation column quantized to q8_1 inside the workgroup, into the layout the
 // one-column ActStage writes (16 lanes per row, one staging slot: block b's int8 values at
 // q_at(b), q_at(b) + 16 LPR, its scale at d_at(b)).  Eight lanes per 32-value block, four
-// consecutive values per lane (one 16-byte load), 32 blocks a pass over the 256 threads;
-// blocks past the column (up to 96) read and stage zeros.  The arithmetic is the q8_1
+// consecutive values per lane (one 16-byte load), TH / 8 blocks a pass (64 with the 512
+// threads of the one-column kernel); blocks past the column (up to the passes' capacity)
+// read and stage zeros.  The arithmetic is the q8_1
 // quantizer's [DQ, Change]: amax over the block (exact in any order), d = amax / 127 and
 // q = x / d rounded half away from zero, IEEE binary32, clamped to +-127, so the staged bytes
 // equal the ones the standalone quantizer writes; only d (as fp16) is staged.
@@ -470,7 +471,7 @@ struct F32Stage {
     }
     template <int NS, int NC, int LPR>
     __device__ __forceinline__ void store(const ActLds& act) {
-        static_assert(NC == 1 && NS == 1 && LPR == 16 && TH == 256, "one column, 16 lanes per row, one slot");
+        static_assert(NC == 1 && NS == 1 && LPR == 16 && (TH == 256 || TH == 512), "one column, 16 lanes per row, one slot");
         const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
 #pragma unroll
         for (int p = 0; p < kPass; ++p) {

@@ -31,15 +31,15 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                    xqbytes, col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
 }
 
-// One fp32 column, quantized to q8_1 by every workgroup for itself (16 x 256 shape, one slot).
-template <int WT, int U>
-__global__ __launch_bounds__(256) void gemv_f32_kernel(const uint8_t* __restrict__ w, uint32_t wbytes, int nrows, int K,
+// One fp32 column, quantized to q8_1 by every workgroup for itself (16 lanes per row, one slot).
+template <int WT, int U, int TH>
+__global__ __launch_bounds__(TH) void gemv_f32_kernel(const uint8_t* __restrict__ w, uint32_t wbytes, int nrows, int K,
                                                        const uint8_t* __restrict__ grid, const float* __restrict__ x,
                                                        uint32_t xbytes, float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    gemv_tile<WT, false, 1, U, false, 1, 16, 256, false, 100, true>(make_rsrc_dw(w, wbytes), nrows, K, grid,
-                                                                    make_rsrc(x, xbytes), xbytes, 0, 1, y, nrows,
-                                                                    nullptr, blockIdx.x * 16, lds);
+    gemv_tile<WT, false, 1, U, false, 1, 16, TH, false, 100, true>(make_rsrc_dw(w, wbytes), nrows, K, grid,
+                                                                   make_rsrc(x, xbytes), xbytes, 0, 1, y, nrows,
+                                                                   nullptr, blockIdx.x * (TH / 16), lds);
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
@@ -152,23 +152,25 @@ static int check_gemv_args(int wtype, const void* w, const uint8_t* grid, int64_
 }
 
 // The fused one-column GEMV: rows of at most 96 blocks (16 lanes per row, chunks of 2, 5 or 6
-// blocks), in the 256-thread shape with one staging slot.
+// blocks), in 32-row workgroups of 512 threads with one staging slot: each workgroup quantizes
+// the column in two passes of 64 blocks (with 256 threads, three of 32) for twice the rows.
 template <int WT>
 static int launch_gemv_f32(const void* w, uint64_t wbytes, const uint8_t* grid, int64_t nrows, int64_t k,
                            const float* x, float* y, hipStream_t st) {
     const Chunk ch = pass_chunk(false, k);
     if (pass_lpr(false, k) != 16 || ch.multi || k / 32 > 96) return QMM_EUNSUPPORTED;
-    if (gemv_shape(WT, false, k, 1) != kNarrow || stage_slots(k, 1, 256, 16, ch.u) != 1) return QMM_EUNSUPPORTED;
-    const dim3 grid_dim((unsigned)((nrows + 15) / 16));
-    const size_t lds = gemv_lds_bytes(WT, k, 1, 16, ch.u, 256);
+    constexpr int TH = 512;
+    if (stage_slots(k, 1, TH, 16, ch.u) != 1 || gemv_lds_bytes(WT, k, 1, 16, ch.u, TH) > kLdsCap) return QMM_EUNSUPPORTED;
+    const dim3 grid_dim((unsigned)((nrows + TH / 16 - 1) / (TH / 16)));
+    const size_t lds = gemv_lds_bytes(WT, k, 1, 16, ch.u, TH);
     const uint32_t xbytes = (uint32_t)(k * 4);
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid_dim, dim3(256), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows, (int)k,
+        hipLaunchKernelGGL(kern, grid_dim, dim3(TH), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows, (int)k,
                            grid, x, xbytes, y);
     };
-    if (ch.u == 2) go(gemv_f32_kernel<WT, 2>);
-    else if (ch.u == 5) go(gemv_f32_kernel<WT, 5>);
-    else go(gemv_f32_kernel<WT, 6>);
+    if (ch.u == 2) go(gemv_f32_kernel<WT, 2, TH>);
+    else if (ch.u == 5) go(gemv_f32_kernel<WT, 5, TH>);
+    else go(gemv_f32_kernel<WT, 6, TH>);
     return launch_status();
 }
 
