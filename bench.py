@@ -135,11 +135,11 @@ def quant_bytes(k, n):
     return n * k * 4 + n * (k // 32) * 36
 
 
-def fused_bytes(wtype, nrows, k):
-    """Algorithmic bytes of the fused one-column call: every weight byte once, the fp32 column,
-    the fp32 outputs (the q8_1 column never leaves the workgroup)."""
+def fused_bytes(wtype, nrows, k, n):
+    """Algorithmic bytes of the fused n-column call: every weight byte once, the fp32 columns,
+    the fp32 outputs (the q8_1 columns never leave the workgroup)."""
     import synth
-    return nrows * synth.row_bytes(wtype, k) + k * 4 + nrows * 4
+    return nrows * synth.row_bytes(wtype, k) + n * k * 4 + n * nrows * 4
 
 
 def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
@@ -178,21 +178,21 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
         M.qmm_quantize_q8_1(xs[n], out=xqs[n])
     torch.cuda.synchronize()
     use_graph = not args.no_graph
-    # one column: the call that quantizes inside the GEMV (rows of at most 96 blocks)
-    fused = not args.unfused and 1 in cols and k <= 3072
+    # the calls that quantize inside the GEMV (rows of at most 96 blocks)
+    fused = set() if args.unfused or k > 3072 else {n for n in cols if n in FUSED_COLS}
 
     def step(slot):
         w = copies[slot % ncopies]
         for n in cols:
-            if fused and n == 1:
-                M.qgemv_dense_f32(wtype, w, nrows, k, xs[1][0], y=ys[1][0])
+            if n in fused:
+                M.qgemv_dense_f32(wtype, w, nrows, k, xs[n], n, y=ys[n])
                 continue
             M.qmm_quantize_q8_1(xs[n], out=xqs[n])
             M.qgemv_dense(wtype, w, nrows, k, xqs[n], n, y=ys[n])
 
     run_step = capture_slots(torch, step, ncopies) if use_graph else step
     ms = contract_steps(torch, run_step, args.steps, args.warmup)
-    step_bytes = sum(fused_bytes(wtype, nrows, k) if fused and n == 1 else gemv_bytes(wtype, nrows, k, n) +
+    step_bytes = sum(fused_bytes(wtype, nrows, k, n) if n in fused else gemv_bytes(wtype, nrows, k, n) +
                      quant_bytes(k, n) for n in cols)
 
     us, gbps, warm, literal = {}, {}, {}, {}
@@ -217,12 +217,12 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                 M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
         literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
-    fused_us = None
-    if fused:
-        def fused_batch():
+    fused_us = {}
+    for n in sorted(fused):
+        def fused_batch(n=n):
             for w in copies:
-                M.qgemv_dense_f32(wtype, w, nrows, k, xs[1][0], y=ys[1][0])
-        fused_us = round(timed_graph(torch, fused_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
+                M.qgemv_dense_f32(wtype, w, nrows, k, xs[n], n, y=ys[n])
+        fused_us[str(n)] = round(timed_graph(torch, fused_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
     floor = stream_read_reference(torch, M, copies, wbytes, use_graph, args.batch_reps)
     rec = recorded_traffic(f"gemv:{wtype}:{nrows}x{k}")
     traffic = None
@@ -232,9 +232,9 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                     {"workload": f"{name}, cold rotation of {ncopies} weight copies "
                                  f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
                      "weight_copies": ncopies, "hip_graph": use_graph,
-                     "one_column_call": "fp32 column, q8_1 inside the GEMV" if fused else "q8_1 quantizer + GEMV"})
+                     "fused_columns": sorted(fused)})
     if fused:
-        out["fused_1col_us_per_call"] = fused_us
+        out["fused_us_per_call"] = fused_us
     out.update({"us_per_call": us, "gbps_per_call": gbps, "warm_us_per_call": warm,
                 f"rotation_{ndistinct}_copies_us_per_call": literal, "hbm_read_reference": floor,
                 "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -484,6 +484,10 @@ def bench_prefill(args, torch, M):
 #   python bench.py --pmc-summary <F>/run_counter_collection.csv <W>/run_counter_collection.csv
 
 PROBE_COLS = (1, 4, 8)
+# column counts whose calls take fp32 columns and form q8_1 inside the GEMV (qgemv_dense_f32):
+# one column only; at 2 and 4 columns every workgroup's share of the quantization costs more
+# than the quantizer launch it saves
+FUSED_COLS = (1,)
 GROUPED_M = (1, 4, 8)
 # the Q8_0 workloads: (rows, k, columns, seed key)
 Q8_SPECS = ((12288, 2560, (1, 2, 3, 4), "q8_0_12288x2560"), (2560, 6144, (7, 8), "q8_0_2560x6144"))
@@ -665,7 +669,7 @@ def main() -> int:
     ap.add_argument("--workload", default="gemv", choices=["gemv", "q8_0", "grouped", "prefill"])
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--unfused", action="store_true", help="one-column GEMV calls as quantizer + q8_1 GEMV")
+    ap.add_argument("--unfused", action="store_true", help="every GEMV call as quantizer + q8_1 GEMV")
     ap.add_argument("--batch-reps", type=int, default=5)
     ap.add_argument("--pmc-probe", action="store_true", help="launch sequence for the counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

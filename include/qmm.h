@@ -105,17 +105,18 @@ int qmm_dequant_f16(int wtype, const void* w, const uint8_t* grid, int64_t nrows
 int qgemv_dense(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
                 const void* xq, int ncols, float* y, int64_t ldy, void* stream);
 
-/* One-column decode GEMV on fp32 activations, quantized to q8_1 inside the kernel [IQ, What it
- * does: decode GEMV on q8_1 activations; DQ, Change: the q8_1 quantizer]: y equals
- * qgemv_dense(wtype, w, grid, nrows, k, qmm_quantize_q8_1(x), 1, y, nrows) bit for bit, in one
- * launch instead of two (every workgroup quantizes the column for itself; the q8_1 bytes are
- * not written out).
- *   w, grid : as qgemv_dense.   x: float [k], 4-byte aligned.   y: float [nrows], 4-byte aligned.
+/* Decode GEMV on 1, 2 or 4 fp32 activation columns, quantized to q8_1 inside the kernel [IQ,
+ * What it does: decode GEMV on q8_1 activations; DQ, Change: the q8_1 quantizer]: y equals
+ * qgemv_dense(wtype, w, grid, nrows, k, qmm_quantize_q8_1(x), ncols, y, ldy) bit for bit, in
+ * one launch instead of two (every workgroup quantizes the columns for itself; the q8_1 bytes
+ * are not written out).
+ *   w, grid : as qgemv_dense.   x: float [ncols][k], 4-byte aligned.
+ *   y    : float, y[c*ldy + r], ldy >= nrows, 4-byte aligned.
  *   k    : multiple of 32 (of 256 for CB3), at most 3072 (rows of at most 96 blocks).
- * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (k above 3072, a weight buffer of 4 GiB or
- *         more). */
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (ncols other than 1, 2, 4; k above 3072; a
+ *         weight buffer of 4 GiB or more). */
 int qgemv_dense_f32(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
-                    const float* x, float* y, void* stream);
+                    const float* x, int ncols, float* y, int64_t ldy, void* stream);
 
 /* Test hook: the per-block integer sums isum(r, b, c) of qgemv_dense, computed by the same
  * device decode and dot code.  sums: int32 [ncols][nrows][k/32].  Same argument rules as

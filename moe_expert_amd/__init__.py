@@ -30,7 +30,7 @@ SIGNATURES = {
     "qmm_quantize_q8_1": (_I32, [_P, _I64, _I32, _I64, _P, _P]),
     "qmm_dequant_f16": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I64, _P]),
     "qgemv_dense": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
-    "qgemv_dense_f32": (_I32, [_I32, _P, _P, _I64, _I64, _P, _P, _P]),
+    "qgemv_dense_f32": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qmm_debug_block_sums": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "qmm_debug_stream_read": (_I32, [_P, _U64, _P, _I32, _P]),
     "qmm_debug_mfma_loop": (_I32, [_P, _I32, _I32, _P]),
@@ -135,15 +135,16 @@ def qgemv_dense(wtype, w, nrows, k, xq, ncols, grid=None, y=None, ldy=None, stre
     return y
 
 
-def qgemv_dense_f32(wtype, w, nrows, k, x, grid=None, y=None, stream=None):
-    """One fp32 column x [k] quantized to q8_1 inside the kernel: y float32 [nrows], bitwise
-    qgemv_dense of qmm_quantize_q8_1(x) (k at most 3072)."""
+def qgemv_dense_f32(wtype, w, nrows, k, x, ncols=1, grid=None, y=None, ldy=None, stream=None):
+    """1, 2 or 4 fp32 columns x [ncols, k] quantized to q8_1 inside the kernel: y float32
+    [ncols, ldy], bitwise qgemv_dense of qmm_quantize_q8_1(x) (k at most 3072)."""
     import torch
     _dev(w, "w"); _dev(x, "x")
+    ldy = nrows if ldy is None else ldy
     if y is None:
-        y = torch.empty(nrows, dtype=torch.float32, device=w.device)
-    _check("qgemv_dense_f32", lib().qgemv_dense_f32(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(x), _ptr(y),
-                                                   _stream(stream)))
+        y = torch.empty((ncols, ldy), dtype=torch.float32, device=w.device)
+    _check("qgemv_dense_f32", lib().qgemv_dense_f32(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(x), ncols, _ptr(y),
+                                                   ldy, _stream(stream)))
     return y
 
 

@@ -447,35 +447,40 @@ __device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
     return v;
 }
 
-// One fp32 activation column quantized to q8_1 inside the workgroup, into the layout the
-// one-column ActStage writes (16 lanes per row, one staging slot: block b's int8 values at
-// q_at(b), q_at(b) + 16 LPR, its scale at d_at(b)).  Eight lanes per 32-value block, four
-// consecutive values per lane (one 16-byte load), TH / 8 blocks a pass (64 with the 512
-// threads of the one-column kernel); blocks past the column (up to the passes' capacity)
-// read and stage zeros.  The arithmetic is the q8_1
-// quantizer's [DQ, Change]: amax over the block (exact in any order), d = amax / 127 and
-// q = x / d rounded half away from zero, IEEE binary32, clamped to +-127, so the staged bytes
-// equal the ones the standalone quantizer writes; only d (as fp16) is staged.
-template <int TH>
+// NC fp32 activation columns (column c at c K floats) quantized to q8_1 inside the workgroup,
+// into the layout the NC-column ActStage writes with 16 lanes per row and one staging slot
+// (block b of column c is the slot-0 block of staging thread ((b / 16) NC + c) 16 + b % 16:
+// its int8 values at q_at, q_at + 16 LPR, its scale at d_at).  Eight lanes per 32-value
+// block, four consecutive values per lane (one 16-byte load), TH / 8 block tasks a pass, task
+// i taking column i % NC, block i / NC; blocks past the row (up to 96) read and stage zeros.
+// The arithmetic is the q8_1 quantizer's [DQ, Change]: amax over the block (exact in any
+// order), d = amax / 127 and q = x / d rounded half away from zero, IEEE binary32, clamped to
+// +-127, so the staged bytes equal the ones the standalone quantizer writes; only d (as fp16)
+// is staged.
+template <int NC, int TH>
 struct F32Stage {
-    static constexpr int kBlocks = TH / 8;                       // per pass
-    static constexpr int kPass = (96 + kBlocks - 1) / kBlocks;  // rows of at most 96 blocks
+    static constexpr int kLogN = NC == 8 ? 3 : NC == 4 ? 2 : NC == 2 ? 1 : 0;
+    static constexpr int kBlocks = TH / 8;                            // block tasks per pass
+    static constexpr int kPass = (NC * 96 + kBlocks - 1) / kBlocks;  // rows of at most 96 blocks
     u32x4 v[kPass];
-    __device__ __forceinline__ void load(rsrc_t xr, int nb, uint32_t zero_off) {
+    __device__ __forceinline__ void load(rsrc_t xr, int nb, int K, uint32_t zero_off) {
         const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
 #pragma unroll
         for (int p = 0; p < kPass; ++p) {
-            const uint32_t b = (uint32_t)p * kBlocks + h;
-            v[p] = ld128(xr, b < (uint32_t)nb ? b * 128u + 16u * j : zero_off);
+            const uint32_t bt = (uint32_t)p * kBlocks + h;
+            const uint32_t c = bt & (NC - 1), b = bt >> kLogN;
+            v[p] = ld128(xr, b < (uint32_t)nb ? (c * (uint32_t)K + b * 32u) * 4u + 16u * j : zero_off);
         }
     }
-    template <int NS, int NC, int LPR>
+    template <int NS, int LPR>
     __device__ __forceinline__ void store(const ActLds& act) {
-        static_assert(NC == 1 && NS == 1 && LPR == 16 && (TH == 256 || TH == 512), "one column, 16 lanes per row, one slot");
+        static_assert(NS == 1 && LPR == 16 && NC <= 4 && TH / NC >= 96, "16 lanes per row, every block in slot 0");
         const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
 #pragma unroll
         for (int p = 0; p < kPass; ++p) {
-            const uint32_t b = (uint32_t)p * kBlocks + h;
+            const uint32_t bt = (uint32_t)p * kBlocks + h;
+            const uint32_t c = bt & (NC - 1), b = bt >> kLogN;
+            const uint32_t ts = ((b >> 4) << (4 + kLogN)) | (c << 4) | (b & 15u);
             // (each element copied out first: __builtin_bit_cast of a vector element in place
             // reads element 0 with this compiler)
             float x[4];
@@ -500,9 +505,9 @@ struct F32Stage {
                 q = q > 127 ? 127 : (q < -127 ? -127 : q);
                 w4 |= (uint32_t)(q & 0xFF) << (8 * i);
             }
-            uint8_t* dq = ActStage<NS, NC, LPR, TH>::q_at(act, b);
+            uint8_t* dq = ActStage<NS, NC, LPR, TH>::q_at(act, ts);
             *(uint32_t*)(dq + (j < 4 ? 4u * j : 16u * LPR + 4u * (j - 4))) = w4;
-            if (j == 0) *ActStage<NS, NC, LPR, TH>::d_at(act, b) = zero ? 0.0f : h2f(f2h(d));
+            if (j == 0) *ActStage<NS, NC, LPR, TH>::d_at(act, ts) = zero ? 0.0f : h2f(f2h(d));
         }
     }
 };
@@ -513,8 +518,8 @@ struct F32Stage {
 // results to y[(col0 + c) * ldy + row] (or the per-block integer sums, SUMS).  LPR lanes per
 // row (16 or 64).  Order of work: activation loads, then this lane's weight loads, then the
 // activation LDS writes (they wait only for the activation loads), barrier, decode + apply as
-// the weights arrive, cross-lane row sums.  F32: `xr` holds one fp32 column instead, which
-// the workgroup quantizes to q8_1 itself (F32Stage).
+// the weights arrive, cross-lane row sums.  F32: `xr` holds the pass's NC fp32 columns
+// instead, which the workgroup quantizes to q8_1 itself (F32Stage).
 template <int WT, bool SUMS, int NC, int U, bool MULTI, int NS, int LPR = kGemvLanesPerRow, int TH = kGemvThreads,
           bool VAR = false, int BUDGET = 100, bool F32 = false>
 __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t xr, uint32_t xbytes,
@@ -534,8 +539,8 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const uint32_t row_off = IQ4Consts::opaque_u((uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K));
 
     ActStage<NS, NC, LPR, TH> stage;
-    F32Stage<TH> fstage;
-    if constexpr (F32) fstage.load(xr, act.nb, xbytes);
+    F32Stage<NC, TH> fstage;
+    if constexpr (F32) fstage.load(xr, act.nb, K, xbytes);
     else stage.load(xr, act, col0, ncp, xbytes);
     GridStage<TH> gstage;
     if constexpr (WT == kCB3) gstage.load(grid);
@@ -543,7 +548,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR, BUDGET> eng(wr, row_off, K, l16);
     eng.load_first();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (F32) fstage.template store<NS, NC, LPR>(act);
+    if constexpr (F32) fstage.template store<NS, LPR>(act);
     else stage.store(act);
     if constexpr (WT == kCB3) gstage.store(lds_grid);
     __syncthreads();

@@ -31,15 +31,15 @@ __global__ __launch_bounds__(TH) void gemv_kernel(const uint8_t* __restrict__ w,
                                                    xqbytes, col0, ncp, y, ldy, sums, blockIdx.x * (TH / LPR), lds);
 }
 
-// One fp32 column, quantized to q8_1 by every workgroup for itself (16 lanes per row, one slot).
-template <int WT, int U, int TH>
+// NC fp32 columns, quantized to q8_1 by every workgroup for itself (16 lanes per row, one slot).
+template <int WT, int U, int NC, int TH>
 __global__ __launch_bounds__(TH) void gemv_f32_kernel(const uint8_t* __restrict__ w, uint32_t wbytes, int nrows, int K,
-                                                       const uint8_t* __restrict__ grid, const float* __restrict__ x,
-                                                       uint32_t xbytes, float* __restrict__ y) {
+                                                      const uint8_t* __restrict__ grid, const float* __restrict__ x,
+                                                      uint32_t xbytes, float* __restrict__ y, int64_t ldy) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    gemv_tile<WT, false, 1, U, false, 1, 16, TH, false, 100, true>(make_rsrc_dw(w, wbytes), nrows, K, grid,
-                                                                   make_rsrc(x, xbytes), xbytes, 0, 1, y, nrows,
-                                                                   nullptr, blockIdx.x * (TH / 16), lds);
+    gemv_tile<WT, false, NC, U, false, 1, 16, TH, false, 100, true>(make_rsrc_dw(w, wbytes), nrows, K, grid,
+                                                                    make_rsrc(x, xbytes), xbytes, 0, NC, y, ldy,
+                                                                    nullptr, blockIdx.x * (TH / 16), lds);
 }
 
 // Workgroup shapes: LPR lanes per row, TH threads (TH / LPR rows per workgroup).
@@ -151,26 +151,35 @@ static int check_gemv_args(int wtype, const void* w, const uint8_t* grid, int64_
     return QMM_OK;
 }
 
-// The fused one-column GEMV: rows of at most 96 blocks (16 lanes per row, chunks of 2, 5 or 6
-// blocks), in 32-row workgroups of 512 threads with one staging slot: each workgroup quantizes
-// the column in two passes of 64 blocks (with 256 threads, three of 32) for twice the rows.
+// The fused GEMV on 1, 2 or 4 fp32 columns: rows of at most 96 blocks (16 lanes per row,
+// chunks of 2, 5 or 6 blocks), in 32-row workgroups of 512 threads with one staging slot: each
+// workgroup quantizes the columns in NC * 96 / 64 passes of 64 blocks, for twice the rows of a
+// 256-thread workgroup.
 template <int WT>
 static int launch_gemv_f32(const void* w, uint64_t wbytes, const uint8_t* grid, int64_t nrows, int64_t k,
-                           const float* x, float* y, hipStream_t st) {
+                           const float* x, int ncols, float* y, int64_t ldy, hipStream_t st) {
+    constexpr int TH = 512;
     const Chunk ch = pass_chunk(false, k);
     if (pass_lpr(false, k) != 16 || ch.multi || k / 32 > 96) return QMM_EUNSUPPORTED;
-    constexpr int TH = 512;
-    if (stage_slots(k, 1, TH, 16, ch.u) != 1 || gemv_lds_bytes(WT, k, 1, 16, ch.u, TH) > kLdsCap) return QMM_EUNSUPPORTED;
+    if (ncols != 1 && ncols != 2 && ncols != 4) return QMM_EUNSUPPORTED;
+    if (stage_slots(k, ncols, TH, 16, ch.u) != 1 || gemv_lds_bytes(WT, k, ncols, 16, ch.u, TH) > kLdsCap)
+        return QMM_EUNSUPPORTED;
     const dim3 grid_dim((unsigned)((nrows + TH / 16 - 1) / (TH / 16)));
-    const size_t lds = gemv_lds_bytes(WT, k, 1, 16, ch.u, TH);
-    const uint32_t xbytes = (uint32_t)(k * 4);
+    const size_t lds = gemv_lds_bytes(WT, k, ncols, 16, ch.u, TH);
+    const uint32_t xbytes = (uint32_t)(ncols * k * 4);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid_dim, dim3(TH), lds, st, (const uint8_t*)w, (uint32_t)wbytes, (int)nrows, (int)k,
-                           grid, x, xbytes, y);
+                           grid, x, xbytes, y, ldy);
     };
-    if (ch.u == 2) go(gemv_f32_kernel<WT, 2, TH>);
-    else if (ch.u == 5) go(gemv_f32_kernel<WT, 5, TH>);
-    else go(gemv_f32_kernel<WT, 6, TH>);
+    auto by_u = [&](auto nc_c) {
+        constexpr int NC = decltype(nc_c)::value;
+        if (ch.u == 2) go(gemv_f32_kernel<WT, 2, NC, TH>);
+        else if (ch.u == 5) go(gemv_f32_kernel<WT, 5, NC, TH>);
+        else go(gemv_f32_kernel<WT, 6, NC, TH>);
+    };
+    if (ncols == 1) by_u(std::integral_constant<int, 1>{});
+    else if (ncols == 2) by_u(std::integral_constant<int, 2>{});
+    else by_u(std::integral_constant<int, 4>{});
     return launch_status();
 }
 
@@ -179,17 +188,17 @@ static int launch_gemv_f32(const void* w, uint64_t wbytes, const uint8_t* grid, 
 using namespace qmm;
 
 extern "C" int qgemv_dense_f32(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k, const float* x,
-                               float* y, void* stream) {
+                               int ncols, float* y, int64_t ldy, void* stream) {
     uint64_t wbytes, xqbytes;
-    // (the shape and weight checks of the q8_1 GEMV; the column is at most 3072 fp32 values)
-    const int rc = check_gemv_args(wtype, w, grid, nrows, k, x, 1, y, &wbytes, &xqbytes);
+    // (the shape and weight checks of the q8_1 GEMV; the columns are at most 4 x 3072 fp32 values)
+    const int rc = check_gemv_args(wtype, w, grid, nrows, k, x, ncols, y, &wbytes, &xqbytes);
     if (rc) return rc;
-    if (!aligned(x, 4)) return QMM_EALIGN;
+    if (ldy < nrows) return QMM_EINVAL;
     const hipStream_t st = as_stream(stream);
     switch (wtype) {
-        case QMM_Q8_0: return launch_gemv_f32<kQ8_0>(w, wbytes, grid, nrows, k, x, y, st);
-        case QMM_IQ4_NL: return launch_gemv_f32<kIQ4_NL>(w, wbytes, grid, nrows, k, x, y, st);
-        default: return launch_gemv_f32<kCB3>(w, wbytes, grid, nrows, k, x, y, st);
+        case QMM_Q8_0: return launch_gemv_f32<kQ8_0>(w, wbytes, grid, nrows, k, x, ncols, y, ldy, st);
+        case QMM_IQ4_NL: return launch_gemv_f32<kIQ4_NL>(w, wbytes, grid, nrows, k, x, ncols, y, ldy, st);
+        default: return launch_gemv_f32<kCB3>(w, wbytes, grid, nrows, k, x, ncols, y, ldy, st);
     }
 }
 

@@ -127,30 +127,34 @@ def test_gemv_full_sizes(wtype, nrows, k, cols, key):
 
 
 @pytest.mark.parametrize("wtype", FORMATS)
-@pytest.mark.parametrize("nrows,k", [(37, 512), (100, 2560), (300, 1536), (7, 96), (33, 3072), (8192, 2560)])
-def test_gemv_f32_fused(wtype, nrows, k):
-    """The one-column call on fp32 activations (q8_1 formed inside the kernel) equals the
-    quantizer followed by the q8_1 GEMV bitwise, and the oracle within the fp32 tolerance.  The
-    column holds an all-zero block, a block whose scale underflows to 0, a block of magnitude 1e6
-    and a block with d = 1 exactly whose other values are halves (ties, rounded away from 0)."""
+@pytest.mark.parametrize("nrows,k,ncols", [(37, 512, 1), (100, 2560, 1), (300, 1536, 2), (7, 96, 4), (33, 3072, 4),
+                                           (8192, 2560, 1), (8192, 2560, 4), (45, 2592, 2)])
+def test_gemv_f32_fused(wtype, nrows, k, ncols):
+    """The call on 1, 2 or 4 fp32 columns (q8_1 formed inside the kernel) equals the quantizer
+    followed by the q8_1 GEMV bitwise, and the oracle within the fp32 tolerance.  Each column
+    holds an all-zero block, a block whose scale underflows to 0, a block of magnitude 1e6 and a
+    block with d = 1 exactly whose other values are halves (ties, rounded away from 0), at
+    column-dependent positions."""
     if wtype == M.QMM_CB3 and k % 256:
         pytest.skip("CB3 rows are whole 256-value super-blocks")
-    print(f"fused f32 gemv wtype={wtype} nrows={nrows} k={k}", flush=True)
-    w, grid, x = case(wtype, nrows, k, 1, 800 + nrows + wtype)
+    print(f"fused f32 gemv wtype={wtype} nrows={nrows} k={k} ncols={ncols}", flush=True)
+    w, grid, x = case(wtype, nrows, k, ncols, 800 + nrows + wtype + ncols)
     x = x.copy()
     nb = k // 32
-    if nb >= 4:
-        x[0, 0:32] = 0.0
-        x[0, 32:64] = np.float32(1e-45)
-        x[0, 64:96] = np.float32(1e6) * x[0, 64:96]
-        x[0, 96:128] = np.arange(-15.5, 16.5, 1.0, dtype=np.float32)
-        x[0, 96] = 127.0
+    for c in range(ncols):
+        if nb >= 4 + c:
+            o = 32 * c
+            x[c, o:o + 32] = 0.0
+            x[c, o + 32:o + 64] = np.float32(1e-45)
+            x[c, o + 64:o + 96] = np.float32(1e6) * x[c, o + 64:o + 96]
+            x[c, o + 96:o + 128] = np.arange(-15.5, 16.5, 1.0, dtype=np.float32)
+            x[c, o + 96] = 127.0
     gd = None if grid is None else dev(grid)
-    y_two, xq = gpu_gemv(wtype, w, grid, x, nrows, k, 1)
-    y = host(M.qgemv_dense_f32(wtype, dev(w), nrows, k, dev(x[0].copy()), grid=gd))
-    assert np.array_equal(y.view(np.uint32), y_two[0].view(np.uint32)), np.abs(y - y_two[0]).max()
+    y_two, xq = gpu_gemv(wtype, w, grid, x, nrows, k, ncols)
+    y = host(M.qgemv_dense_f32(wtype, dev(w), nrows, k, dev(x), ncols, grid=gd))
+    assert np.array_equal(y.view(np.uint32), y_two.view(np.uint32)), np.abs(y - y_two).max()
     ref, a = oracle.gemv(wtype, w, k, oracle.quantize_q8_1(x), grid)
-    check_tol(y[None], ref, a, what=f"fused gemv {wtype}")
+    check_tol(y, ref, a, what=f"fused gemv {wtype}")
 
 
 def test_ldy_padding():

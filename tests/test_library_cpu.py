@@ -64,11 +64,14 @@ def test_qgemv_dense_rejects(args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((M.QMM_Q8_0, FAKE, None, 64, 2560, None, FAKE, None), -1),      # null activations
-    ((M.QMM_Q8_0, FAKE, None, 64, 2561, FAKE, FAKE, None), -1),      # k not a block multiple
-    ((M.QMM_CB3, FAKE, None, 64, 2560, FAKE, FAKE, None), -1),       # CB3 without a grid
-    ((M.QMM_Q8_0, FAKE, None, 64, 2560, ODD, FAKE, None), -3),       # misaligned activations
-    ((M.QMM_Q8_0, FAKE, None, 64, 3104, FAKE, FAKE, None), -2),      # rows of more than 96 blocks
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, None, 1, FAKE, 64, None), -1),      # null activations
+    ((M.QMM_Q8_0, FAKE, None, 64, 2561, FAKE, 1, FAKE, 64, None), -1),      # k not a block multiple
+    ((M.QMM_CB3, FAKE, None, 64, 2560, FAKE, 1, FAKE, 64, None), -1),       # CB3 without a grid
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, ODD, 1, FAKE, 64, None), -3),       # misaligned activations
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, FAKE, 2, FAKE, 63, None), -1),      # ldy < nrows
+    ((M.QMM_Q8_0, FAKE, None, 64, 3104, FAKE, 1, FAKE, 64, None), -2),      # rows of more than 96 blocks
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, FAKE, 3, FAKE, 64, None), -2),      # 3 columns
+    ((M.QMM_Q8_0, FAKE, None, 64, 2560, FAKE, 8, FAKE, 64, None), -2),      # 8 columns
 ])
 def test_qgemv_dense_f32_rejects(args, expect):
     assert M.lib().qgemv_dense_f32(*args) == expect
