@@ -157,6 +157,37 @@ def test_gemv_f32_fused(wtype, nrows, k, ncols):
     check_tol(y, ref, a, what=f"fused gemv {wtype}")
 
 
+@pytest.mark.parametrize("wtype,nrows,k,key", [(M.QMM_IQ4_NL, 8192, 2560, "iq4nl_8192x2560"),
+                                               (M.QMM_Q8_0, 12288, 2560, "q8_0_12288x2560")])
+def test_gemv_f32_full_sizes(wtype, nrows, k, key):
+    """The benchmark's one-column calls on fp32 activations at full size, with its first weight
+    copy and activations: every output within the fp32 tolerance of the oracle, and bitwise the
+    quantizer + q8_1 GEMV result."""
+    print(f"fused gemv full size {key}", flush=True)
+    seed = synth.SEEDS[key]
+    w = synth.weights(wtype, synth.rng_for(seed), nrows, k)
+    x = synth.activations(synth.rng_for(seed + 100), 1, k)
+    wd = dev(w)
+    y = host(M.qgemv_dense_f32(wtype, wd, nrows, k, dev(x), 1))
+    y_two = host(M.qgemv_dense(wtype, wd, nrows, k, M.qmm_quantize_q8_1(dev(x)), 1))
+    assert np.array_equal(y.view(np.uint32), y_two.view(np.uint32))
+    ref, a = oracle.gemv(wtype, w, k, oracle.quantize_q8_1(x))
+    check_tol(y, ref, a, what=f"fused gemv {key}")
+
+
+def test_gemv_f32_ldy_padding():
+    """Two fp32 columns into rows of ldy > nrows: the padding is not written."""
+    print("fused gemv ldy padding", flush=True)
+    import torch
+    w, grid, x = case(M.QMM_Q8_0, 50, 512, 2, 710)
+    y = torch.full((2, 64), 7.0, device="cuda")
+    M.qgemv_dense_f32(M.QMM_Q8_0, dev(w), 50, 512, dev(x), 2, y=y, ldy=64)
+    yh = host(y)
+    assert (yh[:, 50:] == 7.0).all()
+    ref, a = oracle.gemv(M.QMM_Q8_0, w, 512, oracle.quantize_q8_1(x))
+    check_tol(yh[:, :50], ref, a)
+
+
 def test_ldy_padding():
     print("ldy padding", flush=True)
     import torch
