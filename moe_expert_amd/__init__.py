@@ -7,7 +7,9 @@ passes their device pointers and the current HIP stream to the library and raise
 no CPU fallback, and a missing library raises at first use.
 
 Names follow the C ABI: ``qmm_quantize_q8_1``, ``qmm_dequant_f16``, ``qgemv_dense``,
-``qmm_debug_block_sums``, ``qgemv_grouped_experts``, ``qgemm_prefill_experts``.
+``qgemv_dense_f32``, ``qmm_debug_block_sums``, ``qgemv_grouped_experts``,
+``qgemm_prefill_experts`` (and the measurement hooks ``qmm_debug_stream_read``,
+``qmm_debug_mfma_loop``).
 """
 from __future__ import annotations
 
