@@ -1,21 +1,25 @@
 """Benchmark of the block-quantized hot path on one MI355X.
 
-Default workload (the headline): dense decode GEMV, IQ4_NL 8192 x 2560 weights x q8_1
-activations at 1, 4 and 8 columns, on cold weights.  One step = the hot path once per column
-count n in (1, 4, 8): q8_1 quantization of the n activation columns, then the n-column GEMV over
-the next weight copy of a rotation whose total (44 copies, 519 MB) exceeds twice the 256 MB
-Infinity Cache, so every GEMV reads its weights from HBM.  The launches of a step are replayed
-from a HIP graph (one per rotation slot); inputs are resident in HBM before the timed region.
+Headline workload: dense decode GEMV, IQ4_NL 8192 x 2560 weights at 1, 4 and 8 activation
+columns, on cold weights.  One step = the hot path once per column count n in (1, 4, 8): the
+one-column call takes its fp32 column and forms q8_1 inside the GEMV (one launch); the 4- and
+8-column calls quantize their columns to q8_1 and run the q8_1 GEMV.  Each step reads the next
+weight copy of a rotation whose total (47 copies, 554 MB) exceeds twice the 256 MB Infinity
+Cache, so every GEMV reads its weights from HBM.  The launches of a step are replayed from a HIP
+graph (one per rotation slot, each replayed once before timing); inputs are resident in HBM
+before the timed region.
 
-Other workloads (--workload): q8_0 (Q8_0 12288 x 2560 at 1-4 columns, and 2560 x 6144 at 7-8
-columns), grouped (grouped MoE decode, 128 experts, 16 groups x m entries, m = 1/4/8), prefill
-(prefill grouped expert GEMM, 8192 tokens x 2560, top-8 of 128 experts).  Each prints its own
-JSON line with the same fields.
+The default run (--workload all) prints ONE JSON line: the headline fields, and under
+"configs" every other workload timed the same way: Q8_0 512 x 2560 at 1 column, Q8_0
+12288 x 2560 at 1-4 columns, Q8_0 2560 x 6144 at 7-8 columns, the grouped MoE decode (128
+experts, 16 groups x m entries, m = 1/4/8) and the prefill grouped expert GEMM (8192 tokens x
+2560, top-8 of 128 experts).  --workload gemv|tiny|q8_0|grouped|prefill runs one of them alone.
 
 Fields: `value` = algorithmic bytes (GEMV, grouped) or FLOPs (prefill) of a step / step time;
-`roofline` = the dominant kernel's algorithmic bytes or FLOPs per launch over its average
-launch duration, timed with HIP events on the launch stream around graph-batched launches;
-`cpu_baseline` = the CPU oracle on the same workload (or a stated sample of it).
+`roofline` = algorithmic bytes or FLOPs per launch of the kernels the step runs over their
+average launch duration, timed with HIP events on the launch stream around graph-batched
+launches of the cold rotation; `cpu_baseline` = the CPU oracle on the same workload (or a stated
+sample of it), on all host threads and on one.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload W] [--no-graph] [--no-cpu]
 """
@@ -38,28 +42,41 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CALIB_BYTES = 64 << 20   # the plain copy that scales the counters
 
 
-def source_digest():
-    """sha256 of the library sources: recorded counter figures are only reported for the sources
-    they were taken on."""
+# Library sources each workload's kernels are built from: a recorded counter figure is reported
+# only while these hash as they did when the counters were taken.
+DIGEST_SOURCES = {
+    "gemv": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_gemv.hip"),
+    "grouped": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_grouped.hip"),
+    "prefill": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_prefill.hip"),
+}
+
+
+def source_digest(files=None):
+    """sha256 of the library sources `files` (names under moe_expert_amd/csrc; default: all of
+    them and the header)."""
     import hashlib
     h = hashlib.sha256()
-    for d in ("moe_expert_amd/csrc", "include"):
-        for f in sorted(os.listdir(os.path.join(ROOT, d))):
-            h.update(f.encode())
-            with open(os.path.join(ROOT, d, f), "rb") as fh:
-                h.update(fh.read())
+    if files is None:
+        paths = [os.path.join(d, f) for d in ("moe_expert_amd/csrc", "include")
+                 for f in sorted(os.listdir(os.path.join(ROOT, d)))]
+    else:
+        paths = [os.path.join("moe_expert_amd/csrc", f) for f in files]
+    for rel in paths:
+        h.update(os.path.basename(rel).encode())
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def recorded_traffic(key):
     """HBM bytes per launch recorded for `key` by --pmc-summary, or None when there is no record
-    or the sources have changed since it was taken."""
+    or the sources it was taken on have changed since."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256") != source_digest():
+    if not rec or rec.get("source_sha256") != source_digest(rec.get("sources")):
         return None
     return rec
 
@@ -105,7 +122,9 @@ def contract_steps(torch, run_step, steps, warmup):
 
 
 def capture_slots(torch, step, nslots):
-    """One HIP graph per rotation slot of `step`; returns run_step(i)."""
+    """One HIP graph per rotation slot of `step`, each replayed once here (its first replay
+    uploads it: set-up, not timed work); returns run_step(i).  The replays go in rotation order,
+    so the slots the timed steps start with were read longest ago."""
     graphs = []
     for slot in range(nslots):
         step(slot)
@@ -114,7 +133,49 @@ def capture_slots(torch, step, nslots):
         with torch.cuda.graph(g):
             step(slot)
         graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
     return lambda i: graphs[i % nslots].replay()
+
+
+def cpu_info():
+    """Host CPU model name, logical CPUs and sockets (from /proc/cpuinfo)."""
+    model, sockets, ncpu = "unknown", set(), 0
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "processor":
+                    ncpu += 1
+                elif key == "model name" and model == "unknown":
+                    model = val
+                elif key == "physical id":
+                    sockets.add(val)
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": ncpu or os.cpu_count(), "sockets": len(sockets) or 1}
+
+
+def cpu_rate(fn, work, min_s, threads=None):
+    """Rate (work per second) of fn() repeated until min_s seconds have run (at least once), with
+    the oracle's parallel loops on `threads` threads (default: all); returns (rate, reps, s)."""
+    import oracle
+    full = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                break
+    finally:
+        oracle.set_num_threads(full)
+    return work * reps / dt, reps, dt
 
 
 def base_line(metric, value, unit, args, ms, dtype, config, higher=True):
@@ -163,7 +224,7 @@ def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
             "grid": grid, "kernel": "qmm_debug_stream_read (16-byte loads, 8 in flight per thread)"}
 
 
-def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndistinct=6):
+def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndistinct=6, cpu=True, cpu_s=10.0):
     import synth
     wbytes = nrows * synth.row_bytes(wtype, k)
     ncopies = max(ndistinct, -(-2 * MALL_BYTES // wbytes) + 1)
@@ -196,7 +257,6 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                      quant_bytes(k, n) for n in cols)
 
     us, gbps, warm, literal = {}, {}, {}, {}
-    tot_b = tot_us = 0.0
     for n in cols:
         def batch(n=n):
             for w in copies:
@@ -204,8 +264,6 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
         t = timed_graph(torch, batch, args.batch_reps, use_graph) * 1e3 / ncopies
         us[str(n)] = round(t, 3)
         gbps[str(n)] = round(gemv_bytes(wtype, nrows, k, n) / (t * 1e-6) / 1e9, 1)
-        tot_b += gemv_bytes(wtype, nrows, k, n)
-        tot_us += t
 
         def warm_batch(n=n):
             for _ in range(ncopies):
@@ -216,18 +274,28 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
             for i in range(ncopies):
                 M.qgemv_dense(wtype, copies[i % ndistinct], nrows, k, xqs[n], n, y=ys[n])
         literal[str(n)] = round(timed_graph(torch, lit_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
-    achieved = tot_b / (tot_us * 1e-6) / 1e9
     fused_us = {}
     for n in sorted(fused):
         def fused_batch(n=n):
             for w in copies:
                 M.qgemv_dense_f32(wtype, w, nrows, k, xs[n], n, y=ys[n])
         fused_us[str(n)] = round(timed_graph(torch, fused_batch, args.batch_reps, use_graph) * 1e3 / ncopies, 3)
+    # the roofline of the GEMV launches the step runs: the fused call where the step fuses, the
+    # q8_1 GEMV elsewhere (each on the cold rotation)
+    tot_b = sum(fused_bytes(wtype, nrows, k, n) if n in fused else gemv_bytes(wtype, nrows, k, n) for n in cols)
+    tot_us = sum(fused_us[str(n)] if n in fused else us[str(n)] for n in cols)
+    achieved = tot_b / (tot_us * 1e-6) / 1e9
     floor = stream_read_reference(torch, M, copies, wbytes, use_graph, args.batch_reps)
     rec = recorded_traffic(f"gemv:{wtype}:{nrows}x{k}")
     traffic = None
-    if rec and all(str(n) in rec["bytes_per_launch"] for n in cols):
+    if rec and all(str(n) in rec["bytes_per_launch"] for n in cols) and \
+            sorted(rec.get("fused_columns", [])) == sorted(fused):
         traffic = round(sum(rec["bytes_per_launch"][str(n)] for n in cols) / len(cols))
+    parts = [f"gemv_f32_kernel at {sorted(fused)} column(s) (q8_1 formed in the kernel)"] if fused else []
+    rest = [n for n in cols if n not in fused]
+    if rest:
+        parts.append(f"gemv_kernel at {rest} columns")
+    kernels = " + ".join(parts)
     out = base_line(metric, step_bytes / (ms * 1e-3) / 1e9, "GB/s", args, ms, "int8",
                     {"workload": f"{name}, cold rotation of {ncopies} weight copies "
                                  f"({ncopies * wbytes / 1e6:.0f} MB)", "nrows": nrows, "k": k, "columns": list(cols),
@@ -240,30 +308,32 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
                 "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                              "algorithmic_bytes_per_launch": round(tot_b / len(cols)),
-                             "kernel": f"gemv_kernel ({name.split(',')[0]}), columns {list(cols)}"}})
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_gemv(wtype, host_copies[0], nrows, k, cols, seed, step_bytes)
+                             "us_per_launch": round(tot_us / len(cols), 3), "kernel": kernels}})
+    if cpu and not args.no_cpu:
+        out["cpu_baseline"] = cpu_gemv(wtype, host_copies[0], nrows, k, cols, seed, step_bytes, cpu_s)
     return out
 
 
 def cpu_gemv(wtype, w_host, nrows, k, cols, seed, step_bytes, min_s=10.0):
-    """The oracle on the same step, repeated until about min_s seconds of CPU work have run."""
+    """The oracle on the same step (q8_1 of the columns and the GEMV at each column count), on all
+    host threads for about min_s seconds and on one thread for about min_s / 2."""
     import oracle
     import synth
     rng = synth.rng_for(seed + 100)
     xs = {n: synth.activations(rng, n, k) for n in cols}
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def one_step():
         for n in cols:
             oracle.gemv(wtype, w_host, k, oracle.quantize_q8_1(xs[n]))
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_s:
-            break
-    per = dt / reps
-    return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    rate, reps, dt = cpu_rate(one_step, step_bytes, min_s)
+    rate1, reps1, dt1 = cpu_rate(one_step, step_bytes, min_s / 2, threads=1)
+    info = cpu_info()
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"the full step ({nrows} rows at {list(cols)} columns + q8_1 of the columns) x {reps} "
-                      f"repetitions, {dt:.1f} s, {per * 1e3:.1f} ms per step"}
+                      f"repetitions, {dt:.1f} s, {dt / reps * 1e3:.1f} ms per step",
+            "one_thread": {"value": round(rate1 / 1e9, 4), "unit": "GB/s",
+                           "sample": f"the same step x {reps1}, {dt1:.1f} s, {dt1 / reps1 * 1e3:.1f} ms per step"},
+            "host_cpu": info["model"], "logical_cpus": info["logical_cpus"], "sockets": info["sockets"]}
 
 
 # ------------------------------------------------------------------ grouped MoE decode
@@ -321,7 +391,7 @@ def grouped_setup(torch, M):
     return slots, calls, call, host, grid, sizes
 
 
-def bench_grouped(args, torch, M):
+def bench_grouped(args, torch, M, cpu_s=10.0):
     import synth
     ms_list = GROUPED_M
     slots, calls, call, host, grid, z = grouped_setup(torch, M)
@@ -367,20 +437,21 @@ def bench_grouped(args, torch, M):
                              "kernel": "gu_kernel + down_kernel (one call, m = 1/4/8)"}})
     if not args.no_cpu:
         import oracle
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            for m in ms_list:
-                ge, go, ec, x = calls[m]["host"]
-                oracle.grouped(synth.CB3, host["wg"], host["wu"], synth.IQ4_NL, host["wd"], hidden, inter,
-                               oracle.quantize_q8_1(x), ge, go, ec, grid)
-            reps += 1
-            dt = time.perf_counter() - t0
-            if dt >= 10.0:
-                break
-        out["cpu_baseline"] = {"value": round(step_bytes / (dt / reps) / 1e9, 4), "unit": "GB/s",
-                               "cores": oracle.num_threads(), "kind": "oracle",
-                               "sample": f"the full step (m = 1/4/8) x {reps}, {dt:.1f} s"}
+
+        def one_call(m):
+            ge, go, ec, x = calls[m]["host"]
+            oracle.grouped(synth.CB3, host["wg"], host["wu"], synth.IQ4_NL, host["wd"], hidden, inter,
+                           oracle.quantize_q8_1(x), ge, go, ec, grid)
+        rate, reps, dt = cpu_rate(lambda: [one_call(m) for m in ms_list], step_bytes, cpu_s)
+        b1 = grouped_bytes(hidden, inter, ngroups, 1, expert_bytes) + quant_bytes(hidden, 1)
+        rate1, reps1, dt1 = cpu_rate(lambda: one_call(1), b1, cpu_s / 2, threads=1)
+        info = cpu_info()
+        out["cpu_baseline"] = {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"the full step (m = 1/4/8) x {reps}, {dt:.1f} s",
+                               "one_thread": {"value": round(rate1 / 1e9, 4), "unit": "GB/s",
+                                              "sample": f"the m = 1 call x {reps1}, {dt1:.1f} s"},
+                               "host_cpu": info["model"], "logical_cpus": info["logical_cpus"],
+                               "sockets": info["sockets"]}
     return out
 
 
@@ -430,7 +501,7 @@ def mfma_reference(torch, M, reps):
             "kernel": "qmm_debug_mfma_loop (v_mfma_f32_32x32x16_f16, 8 accumulators per wave, registers only)"}
 
 
-def bench_prefill(args, torch, M):
+def bench_prefill(args, torch, M, cpu_s=10.0):
     import numpy as np
 
     import synth
@@ -445,7 +516,8 @@ def bench_prefill(args, torch, M):
     out = base_line("µs/call and MFMA TFLOP/s, prefill grouped expert GEMM (8192 tokens x 2560, top-8 of 128)",
                     tflops, "TFLOP/s", args, ms, "fp16",
                     {"workload": "prefill grouped expert GEMM: 8192 tokens x hidden 2560, top-8 of 128 experts, "
-                                 "IQ4_NL gate/up 2560->1024, Q8_0 down 1024->2560, FP16 dequant in LDS + fp16 MFMA",
+                                 "IQ4_NL gate/up 2560->1024, Q8_0 down 1024->2560, weights converted to FP16 in registers + "
+                                 "fp16 MFMA with fp32 sums",
                      "tokens": ntok, "entries": int(nent), "hip_graph": use_graph})
     rec = recorded_traffic("prefill")
     out["mfma_reference"] = mfma_reference(torch, M, args.batch_reps)
@@ -456,21 +528,27 @@ def bench_prefill(args, torch, M):
                              "kernel": "schedule + pf_gateup_kernel + pf_down_kernel (one call)"}})
     if not args.no_cpu:
         import oracle
-        # rows of the first experts, sized from a 32-row trial to about 10 s of CPU work
+
+        def rows(n):
+            oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off,
+                                np.arange(n, dtype=np.int64))
+        # rows of the first experts (their weights dequantized too), sized from a 32-row trial to
+        # about cpu_s seconds of work on all threads; 8 rows on one thread
         t0 = time.perf_counter()
-        oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off,
-                            np.arange(32, dtype=np.int64))
+        rows(32)
         trial = time.perf_counter() - t0
-        nrow = int(min(nent, max(32, 32 * 10.0 / max(trial, 1e-3))))
-        samples = np.arange(nrow, dtype=np.int64)
-        t0 = time.perf_counter()
-        oracle.prefill_rows(synth.IQ4_NL, wg, wu, synth.Q8_0, wd, nexp, hidden, inter, x16, st, off, samples)
-        dt = time.perf_counter() - t0
-        per_row = dt / samples.size
-        out["cpu_baseline"] = {"value": round(flops / nent / per_row / 1e12, 6), "unit": "TFLOP/s",
+        nrow = int(min(nent, max(32, 32 * cpu_s / max(trial, 1e-3))))
+        rate, _, dt = cpu_rate(lambda: rows(nrow), flops / nent * nrow, 0.0)
+        rate1, _, dt1 = cpu_rate(lambda: rows(8), flops / nent * 8, 0.0, threads=1)
+        info = cpu_info()
+        out["cpu_baseline"] = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.num_threads(), "kind": "oracle",
                                "sample": f"the first {nrow} sorted rows (experts 0..{int(np.searchsorted(off, nrow, 'right')) - 1}, "
-                                         f"incl. dequantizing their weights), {dt:.1f} s, scaled to {nent} rows"}
+                                         f"incl. dequantizing their weights), {dt:.1f} s, as a rate per row",
+                               "one_thread": {"value": round(rate1 / 1e12, 6), "unit": "TFLOP/s",
+                                              "sample": f"the first 8 sorted rows, {dt1:.1f} s"},
+                               "host_cpu": info["model"], "logical_cpus": info["logical_cpus"],
+                               "sockets": info["sockets"]}
     return out
 
 
@@ -512,13 +590,17 @@ def pmc_probe(torch, M, workload):
         host = [synth.weights(wt, synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + i), nrows, k) for i in range(6)]
         copies = [torch.from_numpy(host[i % 6]).to(dev) for i in range(ncopies)]
         rng = synth.rng_for(synth.SEEDS["iq4nl_8192x2560"] + 100)
-        xq = {n: M.qmm_quantize_q8_1(torch.from_numpy(synth.activations(rng, n, k)).to(dev)) for n in PROBE_COLS}
+        xs = {n: torch.from_numpy(synth.activations(rng, n, k)).to(dev) for n in PROBE_COLS}
+        xq = {n: M.qmm_quantize_q8_1(xs[n]) for n in PROBE_COLS}
         y = {n: torch.empty((n, nrows), dtype=torch.float32, device=dev) for n in PROBE_COLS}
 
-        def run():
+        def run():   # the GEMV launches of the benchmark step: fused where it fuses
             for n in PROBE_COLS:
                 for w in copies:
-                    M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
+                    if n in FUSED_COLS:
+                        M.qgemv_dense_f32(wt, w, nrows, k, xs[n], n, y=y[n])
+                    else:
+                        M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
     elif workload == "q8_0":
         wt = synth.Q8_0
         sets = []
@@ -570,9 +652,13 @@ def pmc_summary(workload, fetch_csv, write_csv):
     import re
 
     import synth
-    pattern = {"gemv": r"gemv_kernel<\d+, false, (\d+),", "q8_0": r"gemv_kernel<\d+, false, (\d+),",
+    pattern = {"gemv": r"gemv_f32_kernel<\d+, \d+, (\d+),|gemv_kernel<\d+, false, (\d+),",
+               "q8_0": r"gemv_kernel<\d+, false, (\d+),",
                "grouped": r"(gu_kernel|down_kernel)",
                "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)"}[workload]
+
+    def tag(name):   # the first group the pattern matched: column count or kernel name
+        return next(g for g in re.search(pattern, name).groups() if g is not None)
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -583,8 +669,7 @@ def pmc_summary(workload, fetch_csv, write_csv):
         cp = [float(r["Counter_Value"]) for r in rows
               if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first]
         calib = [v for v in cp if v >= 0.5 * max(cp)][-3:]
-        return sum(calib) / len(calib), [(re.search(pattern, r["Kernel_Name"]).group(1), float(r["Counter_Value"]))
-                                         for r in ours]
+        return sum(calib) / len(calib), [(tag(r["Kernel_Name"]), float(r["Counter_Value"])) for r in ours]
 
     fcal, fk = per_kernel(fetch_csv, "FETCH_SIZE")
     wcal, wk = per_kernel(write_csv, "WRITE_SIZE")
@@ -610,7 +695,8 @@ def pmc_summary(workload, fetch_csv, write_csv):
             r["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
             r["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
             r["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in cols}
-            r["source_sha256"] = source_digest()
+            r["sources"] = list(DIGEST_SOURCES["gemv"])
+            r["source_sha256"] = source_digest(r["sources"])
             store_traffic(f"gemv:{synth.Q8_0}:{nrows}x{k}", r)
         if i != len(fk) or len(fk) != len(wk):
             raise SystemExit(f"expected {i} GEMV dispatches, found {len(fk)} / {len(wk)}")
@@ -618,7 +704,9 @@ def pmc_summary(workload, fetch_csv, write_csv):
     if workload == "gemv":
         fetch = {n: mean([v for g, v in fk if int(g) == n]) for n in PROBE_COLS}
         write = {n: mean([v for g, v in wk if int(g) == n]) for n in PROBE_COLS}
-        rec["algorithmic_bytes"] = {str(n): gemv_bytes(synth.IQ4_NL, 8192, 2560, n) for n in PROBE_COLS}
+        rec["algorithmic_bytes"] = {str(n): fused_bytes(synth.IQ4_NL, 8192, 2560, n) if n in FUSED_COLS
+                                    else gemv_bytes(synth.IQ4_NL, 8192, 2560, n) for n in PROBE_COLS}
+        rec["fused_columns"] = list(FUSED_COLS)
         key = f"gemv:{synth.IQ4_NL}:8192x2560"
     elif workload == "grouped":
         # dispatch order: for each m, one gu_kernel and one down_kernel per expert set
@@ -645,7 +733,8 @@ def pmc_summary(workload, fetch_csv, write_csv):
     rec["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
     rec["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
     rec["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in fetch}
-    rec["source_sha256"] = source_digest()
+    rec["sources"] = list(DIGEST_SOURCES["gemv" if workload == "gemv" else workload])
+    rec["source_sha256"] = source_digest(rec["sources"])
     store_traffic(key, rec)
 
 
@@ -666,7 +755,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gemv", choices=["gemv", "q8_0", "grouped", "prefill"])
+    ap.add_argument("--workload", default="all", choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill"],
+                    help="all (default): the headline GEMV line with every other workload under 'configs'")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="every GEMV call as quantizer + q8_1 GEMV")
@@ -689,27 +779,73 @@ def main() -> int:
     import synth
 
     torch.cuda.set_device(0)
+    global TINY_SPEC, Q8_BENCH
+    TINY_SPEC, Q8_BENCH = _bench_specs()
     if args.pmc_probe:
         pmc_probe(torch, M, args.workload)
         return 0
-    if args.workload == "gemv":
+    if args.workload in ("gemv", "all"):
+        t0 = time.perf_counter()
         out = bench_gemv(args, torch, M, synth.IQ4_NL, 8192, 2560, (1, 4, 8), synth.SEEDS["iq4nl_8192x2560"],
                          "µs/call and achieved HBM GB/s, IQ4_NL 8192x2560 GEMV at 1/4/8 columns",
                          "IQ4_NL dense decode GEMV 8192x2560 x q8_1, 1/4/8 columns")
+        progress(f"headline IQ4_NL 8192x2560 GEMV done ({time.perf_counter() - t0:.0f} s)")
+        if args.workload == "all":
+            out["configs"] = other_configs(args, torch, M)
         print(json.dumps(out), flush=True)
+    elif args.workload == "tiny":
+        print(json.dumps(bench_gemv(args, torch, M, *TINY_SPEC)), flush=True)
     elif args.workload == "q8_0":
-        for nrows, k, cols, seed, name in ((12288, 2560, (1, 2, 3, 4), synth.SEEDS["q8_0_12288x2560"],
-                                            "Q8_0 dense decode GEMV 12288x2560 x q8_1, 1-4 columns"),
-                                           (2560, 6144, (7, 8), synth.SEEDS["q8_0_2560x6144"],
-                                            "Q8_0 dense decode GEMV 2560x6144 x q8_1, 7-8 columns")):
-            out = bench_gemv(args, torch, M, synth.Q8_0, nrows, k, cols, seed,
-                             f"µs/call and achieved HBM GB/s, {name}", name)
-            print(json.dumps(out), flush=True)
+        for spec in Q8_BENCH:
+            print(json.dumps(bench_gemv(args, torch, M, *spec)), flush=True)
     elif args.workload == "grouped":
         print(json.dumps(bench_grouped(args, torch, M)), flush=True)
     else:
         print(json.dumps(bench_prefill(args, torch, M)), flush=True)
     return 0
+
+
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _bench_specs():
+    import synth
+    tiny = (synth.Q8_0, 512, 2560, (1,), synth.SEEDS["q8_0_tiny"],
+            "µs/call and achieved HBM GB/s, Q8_0 512x2560 GEMV at 1 column",
+            "Q8_0 dense decode GEMV 512x2560 x q8_1, 1 column")
+    q8 = [(synth.Q8_0, nrows, k, cols, synth.SEEDS[key], f"µs/call and achieved HBM GB/s, {name}", name)
+          for nrows, k, cols, key, name in ((12288, 2560, (1, 2, 3, 4), "q8_0_12288x2560",
+                                             "Q8_0 dense decode GEMV 12288x2560 x q8_1, 1-4 columns"),
+                                            (2560, 6144, (7, 8), "q8_0_2560x6144",
+                                             "Q8_0 dense decode GEMV 2560x6144 x q8_1, 7-8 columns"))]
+    return tiny, q8
+
+
+# keys of a workload's own line that the headline line already states
+_BOILERPLATE = ("n_gpus", "higher_is_better", "scaling", "vs_baseline", "data")
+
+
+def other_configs(args, torch, M):
+    """The other workloads of the contract, each timed like the headline (same steps and warm-up,
+    cold rotations, graphs), with a shorter oracle sample: returned as one dict per workload."""
+    tiny, q8 = _bench_specs()
+    runs = [("q8_0_512x2560_1col", lambda: bench_gemv(args, torch, M, *tiny, cpu_s=3.0)),
+            ("q8_0_12288x2560_1to4col", lambda: bench_gemv(args, torch, M, *q8[0], cpu_s=3.0)),
+            ("q8_0_2560x6144_7to8col", lambda: bench_gemv(args, torch, M, *q8[1], cpu_s=3.0)),
+            ("grouped_moe_decode_128x2560x1024", lambda: bench_grouped(args, torch, M, cpu_s=4.0)),
+            ("prefill_experts_8192x2560_top8", lambda: bench_prefill(args, torch, M, cpu_s=4.0))]
+    out = {}
+    for name, fn in runs:
+        t0 = time.perf_counter()
+        r = fn()
+        out[name] = {k: v for k, v in r.items() if k not in _BOILERPLATE}
+        torch.cuda.empty_cache()
+        progress(f"{name} done ({time.perf_counter() - t0:.0f} s)")
+    return out
+
+
+TINY_SPEC, Q8_BENCH = None, None
 
 
 if __name__ == "__main__":

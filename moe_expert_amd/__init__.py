@@ -2,9 +2,11 @@
 
 A thin ctypes binding over ``libqmm.so`` (the C ABI declared in include/qmm.h).  Every entry
 point below only marshals arguments: it takes torch tensors that already live on the GPU,
-passes their device pointers and the current HIP stream to the library and raises
-``QmmError`` on a non-zero status.  All arithmetic runs in the library's HIP kernels; there is
-no CPU fallback, and a missing library raises at first use.
+checks that each one is a contiguous tensor of the expected dtype on the same GPU and holds at
+least the bytes the call reads or writes (``ValueError`` otherwise, before anything is launched:
+the library trusts the sizes it is given), passes the device pointers and the current HIP stream
+to the library and raises ``QmmError`` on a non-zero status.  All arithmetic runs in the
+library's HIP kernels; there is no CPU fallback, and a missing library raises at first use.
 
 Names follow the C ABI: ``qmm_quantize_q8_1``, ``qmm_dequant_f16``, ``qgemv_dense``,
 ``qgemv_dense_f32``, ``qmm_debug_block_sums``, ``qgemv_grouped_experts``,
@@ -23,6 +25,8 @@ QMM_Q8_0, QMM_IQ4_NL, QMM_CB3 = 1, 2, 3
 QMM_FLAG_DEBUG_INTERMEDIATES = 1
 BLOCK_VALUES = {QMM_Q8_0: 32, QMM_IQ4_NL: 32, QMM_CB3: 256}
 BLOCK_BYTES = {QMM_Q8_0: 34, QMM_IQ4_NL: 18, QMM_CB3: 110}
+Q8_1_BYTES = 36
+GRID_BYTES = 2048
 
 _P, _I64, _I32, _U32, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_uint, C.c_uint64, C.c_size_t
 SIGNATURES = {
@@ -80,11 +84,11 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, device=None):
     if stream is not None:
         return C.c_void_p(stream)
     import torch
-    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _check(fn, rc):
@@ -92,48 +96,115 @@ def _check(fn, rc):
         raise QmmError(fn, rc)
 
 
-def _dev(t, name):
-    if not t.is_cuda:
+# ------------------------------------------------------------------ argument checks
+#
+# The C library takes plain pointers and sizes and cannot see the allocations behind them, so
+# every tensor is checked here against what the call will touch.
+
+def _dtypes(kind):
+    import torch
+    return {"u8": (torch.uint8,), "f32": (torch.float32,), "i32": (torch.int32,),
+            "f16": tuple(d for d in (torch.float16, torch.int16, getattr(torch, "uint16", None)) if d is not None)}[kind]
+
+
+def _nbytes(t) -> int:
+    return int(t.numel()) * int(t.element_size())
+
+
+def _need(t, name, kind, nbytes, device=None):
+    """t must be a contiguous GPU tensor of dtype `kind` (u8, f32, i32, f16: any 2-byte type), on
+    `device` when given, holding at least `nbytes` bytes."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not getattr(t, "is_cuda", False):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in _dtypes(kind):
+        raise ValueError(f"{name} must have dtype {kind}, not {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes; the call touches {nbytes}")
     return t
 
+
+def _block_multiple(wtype, k, name="k"):
+    if wtype not in BLOCK_VALUES:
+        raise ValueError(f"unknown weight format {wtype}")
+    if k < 1 or k % BLOCK_VALUES[wtype]:
+        raise ValueError(f"{name}={k} is not a positive multiple of {BLOCK_VALUES[wtype]}")
+    return (k // BLOCK_VALUES[wtype]) * BLOCK_BYTES[wtype]
+
+
+def _grid_arg(wtype, grid, device, name="grid"):
+    if wtype == QMM_CB3 or grid is not None:
+        _need(grid, name, "u8", GRID_BYTES, device)
+    return grid
+
+
+def _out(t, name, kind, nbytes, device, shape, dtype):
+    """A caller-supplied output (checked) or a new one of `shape`."""
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, name, kind, nbytes, device)
+
+
+# ------------------------------------------------------------------ entry points
 
 def qmm_quantize_q8_1(x, out=None, stream=None):
     """x: float32 [ncols, k] (GPU) -> uint8 [ncols, k/32*36] q8_1 blocks."""
     import torch
-    _dev(x, "x")
-    if x.dim() == 1:
+    if getattr(x, "dim", lambda: 0)() == 1:
         x = x.view(1, -1)
+    if getattr(x, "dim", lambda: 0)() != 2:
+        raise ValueError("x must be [ncols, k]")
     ncols, k = x.shape
-    if out is None:
-        out = torch.empty((ncols, (k // 32) * 36), dtype=torch.uint8, device=x.device)
-    _check("qmm_quantize_q8_1", lib().qmm_quantize_q8_1(_ptr(x), k, ncols, k, _ptr(out), _stream(stream)))
+    if k < 32 or k % 32:
+        raise ValueError(f"k={k} is not a positive multiple of 32")
+    _need(x, "x", "f32", ncols * k * 4)
+    out = _out(out, "out", "u8", ncols * (k // 32) * Q8_1_BYTES, x.device, (ncols, (k // 32) * Q8_1_BYTES),
+               torch.uint8)
+    _check("qmm_quantize_q8_1", lib().qmm_quantize_q8_1(_ptr(x), k, ncols, k, _ptr(out), _stream(stream, x.device)))
     return out
 
 
 def qmm_dequant_f16(wtype, w, nrows, k, grid=None, out=None, ld=None, stream=None):
     """Weight blocks -> binary16 [nrows, ld] (returned as torch.float16)."""
     import torch
-    _dev(w, "w")
+    rb = _block_multiple(wtype, k)
     ld = k if ld is None else ld
-    if out is None:
-        out = torch.empty((nrows, ld), dtype=torch.float16, device=w.device)
+    if nrows < 1 or ld < k:
+        raise ValueError("nrows >= 1 and ld >= k")
+    _need(w, "w", "u8", nrows * rb)
+    _grid_arg(wtype, grid, w.device)
+    out = _out(out, "out", "f16", ((nrows - 1) * ld + k) * 2, w.device, (nrows, ld), torch.float16)
     _check("qmm_dequant_f16", lib().qmm_dequant_f16(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(out), ld,
-                                                   _stream(stream)))
+                                                   _stream(stream, w.device)))
     return out
+
+
+def _gemv_common(wtype, w, nrows, k, ncols, grid, ldy):
+    rb = _block_multiple(wtype, k)
+    if nrows < 1 or ncols < 1:
+        raise ValueError("nrows and ncols must be positive")
+    ldy = nrows if ldy is None else ldy
+    if ldy < nrows:
+        raise ValueError("ldy < nrows")
+    _need(w, "w", "u8", nrows * rb)
+    _grid_arg(wtype, grid, w.device)
+    return ldy
 
 
 def qgemv_dense(wtype, w, nrows, k, xq, ncols, grid=None, y=None, ldy=None, stream=None):
     """y[c, r] for c < ncols: float32 [ncols, ldy] (ldy defaults to nrows)."""
     import torch
-    _dev(w, "w"); _dev(xq, "xq")
-    ldy = nrows if ldy is None else ldy
-    if y is None:
-        y = torch.empty((ncols, ldy), dtype=torch.float32, device=w.device)
+    ldy = _gemv_common(wtype, w, nrows, k, ncols, grid, ldy)
+    _need(xq, "xq", "u8", ncols * (k // 32) * Q8_1_BYTES, w.device)
+    y = _out(y, "y", "f32", ((ncols - 1) * ldy + nrows) * 4, w.device, (ncols, ldy), torch.float32)
     _check("qgemv_dense", lib().qgemv_dense(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(xq), ncols, _ptr(y), ldy,
-                                           _stream(stream)))
+                                           _stream(stream, w.device)))
     return y
 
 
@@ -141,23 +212,22 @@ def qgemv_dense_f32(wtype, w, nrows, k, x, ncols=1, grid=None, y=None, ldy=None,
     """1, 2 or 4 fp32 columns x [ncols, k] quantized to q8_1 inside the kernel: y float32
     [ncols, ldy], bitwise qgemv_dense of qmm_quantize_q8_1(x) (k at most 3072)."""
     import torch
-    _dev(w, "w"); _dev(x, "x")
-    ldy = nrows if ldy is None else ldy
-    if y is None:
-        y = torch.empty((ncols, ldy), dtype=torch.float32, device=w.device)
+    ldy = _gemv_common(wtype, w, nrows, k, ncols, grid, ldy)
+    _need(x, "x", "f32", ncols * k * 4, w.device)
+    y = _out(y, "y", "f32", ((ncols - 1) * ldy + nrows) * 4, w.device, (ncols, ldy), torch.float32)
     _check("qgemv_dense_f32", lib().qgemv_dense_f32(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(x), ncols, _ptr(y),
-                                                   ldy, _stream(stream)))
+                                                   ldy, _stream(stream, w.device)))
     return y
 
 
 def qmm_debug_block_sums(wtype, w, nrows, k, xq, ncols, grid=None, out=None, stream=None):
     """Per-block integer sums int32 [ncols, nrows, k/32]."""
     import torch
-    _dev(w, "w"); _dev(xq, "xq")
-    if out is None:
-        out = torch.empty((ncols, nrows, k // 32), dtype=torch.int32, device=w.device)
+    _gemv_common(wtype, w, nrows, k, ncols, grid, None)
+    _need(xq, "xq", "u8", ncols * (k // 32) * Q8_1_BYTES, w.device)
+    out = _out(out, "out", "i32", ncols * nrows * (k // 32) * 4, w.device, (ncols, nrows, k // 32), torch.int32)
     _check("qmm_debug_block_sums", lib().qmm_debug_block_sums(wtype, _ptr(w), _ptr(grid), nrows, k, _ptr(xq), ncols,
-                                                             _ptr(out), _stream(stream)))
+                                                             _ptr(out), _stream(stream, w.device)))
     return out
 
 
@@ -165,10 +235,12 @@ def qmm_debug_stream_read(p, nbytes, grid, out=None, stream=None):
     """Plain streaming read of the first nbytes of device tensor p in one launch of `grid`
     256-thread workgroups (the HBM reference); returns out (uint32 [grid * 256])."""
     import torch
-    _dev(p, "p")
-    if out is None:
-        out = torch.empty(grid * 256, dtype=torch.int32, device=p.device)
-    _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid, _stream(stream)))
+    if grid < 1:
+        raise ValueError("grid must be positive")
+    _need(p, "p", "u8", nbytes)
+    out = _out(out, "out", "i32", grid * 256 * 4, p.device, (grid * 256,), torch.int32)
+    _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid,
+                                                               _stream(stream, p.device)))
     return out
 
 
@@ -176,14 +248,29 @@ def qmm_debug_mfma_loop(grid, iters, out=None, device="cuda", stream=None):
     """Register-only fp16 MFMA loop (grid * 4 * 8 * iters * 32768 FLOP); returns out (float
     [grid * 256])."""
     import torch
+    if grid < 1 or iters < 1:
+        raise ValueError("grid and iters must be positive")
     if out is None:
         out = torch.empty(grid * 256, dtype=torch.float32, device=device)
-    _check("qmm_debug_mfma_loop", lib().qmm_debug_mfma_loop(_ptr(out), grid, iters, _stream(stream)))
+    _need(out, "out", "f32", grid * 256 * 4)
+    _check("qmm_debug_mfma_loop", lib().qmm_debug_mfma_loop(_ptr(out), grid, iters, _stream(stream, out.device)))
     return out
 
 
 def qgemv_grouped_experts_workspace(inter, nentries, flags=0):
     return int(lib().qgemv_grouped_experts_workspace(inter, nentries, flags))
+
+
+def _expert_weights(t, name, nexperts, matrix_bytes, device):
+    """[nexperts, ...] uint8 expert matrices of at least matrix_bytes each; returns the
+    per-expert stride in bytes."""
+    if getattr(t, "dim", lambda: 0)() < 1 or t.shape[0] != nexperts:
+        raise ValueError(f"{name} must be [{nexperts} experts, ...]")
+    _need(t, name, "u8", nexperts * matrix_bytes, device)
+    stride = _nbytes(t) // nexperts
+    if stride < matrix_bytes:
+        raise ValueError(f"{name}: {stride} bytes per expert, one matrix is {matrix_bytes}")
+    return stride
 
 
 def qgemv_grouped_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, hidden, inter, xq, group_expert,
@@ -192,24 +279,32 @@ def qgemv_grouped_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, hidden, in
     w_down: [nexperts, hidden * row_bytes(down, inter)] bytes, xq: [xq_cols, hidden/32*36] q8_1;
     returns (y [nentries, hidden] float32, ws)."""
     import torch
-    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (xq, "xq"), (group_expert, "group_expert"),
-                 (group_entry_off, "group_entry_off"), (entry_col, "entry_col")):
-        _dev(t, n)
-    nentries = entry_col.numel()
-    ngroups = group_expert.numel()
-    nexperts = w_gate.shape[0]
-    xq_cols = xq.numel() // ((hidden // 32) * 36)
-    gu_stride = w_gate[0].numel()
-    d_stride = w_down[0].numel()
-    if y is None:
-        y = torch.empty((nentries, hidden), dtype=torch.float32, device=w_gate.device)
+    if getattr(w_gate, "dim", lambda: 0)() < 1:
+        raise ValueError("w_gate must be [nexperts, ...]")
+    dev = w_gate.device
+    nexperts = int(w_gate.shape[0])
+    gu_stride = _expert_weights(w_gate, "w_gate", nexperts, inter * _block_multiple(wtype_gu, hidden, "hidden"), dev)
+    if _expert_weights(w_up, "w_up", nexperts, gu_stride, dev) != gu_stride:
+        raise ValueError("w_up must have w_gate's shape")
+    d_stride = _expert_weights(w_down, "w_down", nexperts, hidden * _block_multiple(wtype_down, inter, "inter"), dev)
+    _grid_arg(wtype_gu if wtype_gu == QMM_CB3 else wtype_down, grid, dev)
+    col_bytes = (hidden // 32) * Q8_1_BYTES
+    _need(xq, "xq", "u8", col_bytes, dev)
+    if _nbytes(xq) % col_bytes:
+        raise ValueError("xq must hold whole q8_1 columns of width hidden")
+    xq_cols = _nbytes(xq) // col_bytes
+    ngroups = int(group_expert.numel())
+    nentries = int(entry_col.numel())
+    _need(group_expert, "group_expert", "i32", 0, dev)
+    _need(group_entry_off, "group_entry_off", "i32", (ngroups + 1) * 4, dev)
+    _need(entry_col, "entry_col", "i32", 0, dev)
+    y = _out(y, "y", "f32", nentries * hidden * 4, dev, (nentries, hidden), torch.float32)
     need = qgemv_grouped_experts_workspace(inter, nentries, flags)
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=w_gate.device)
+    ws = _out(ws, "ws", "u8", need, dev, (max(need, 16),), torch.uint8)
     _check("qgemv_grouped_experts", lib().qgemv_grouped_experts(
         wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, nexperts, _ptr(grid),
         hidden, inter, _ptr(xq), xq_cols, _ptr(group_expert), _ptr(group_entry_off), ngroups, _ptr(entry_col),
-        nentries, _ptr(y), _ptr(ws), ws.numel(), flags, _stream(stream)))
+        nentries, _ptr(y), _ptr(ws), _nbytes(ws), flags, _stream(stream, dev)))
     return y, ws
 
 
@@ -221,20 +316,25 @@ def qgemm_prefill_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, nexperts, 
                           expert_off, y=None, ws=None, flags=0, stream=None):
     """Prefill grouped expert GEMM; returns (y [nentries, hidden] float32, ws)."""
     import torch
-    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (x_f16, "x_f16"),
-                 (sorted_tok, "sorted_tok"), (expert_off, "expert_off")):
-        _dev(t, n)
-    nentries = sorted_tok.numel()
-    ntok = x_f16.shape[0]
-    gu_stride = inter * row_bytes(wtype_gu, hidden)
-    d_stride = hidden * row_bytes(wtype_down, inter)
-    if y is None:
-        y = torch.empty((nentries, hidden), dtype=torch.float32, device=w_gate.device)
+    if getattr(x_f16, "dim", lambda: 0)() != 2 or x_f16.shape[1] != hidden:
+        raise ValueError("x_f16 must be [ntok, hidden]")
+    dev = x_f16.device
+    ntok = int(x_f16.shape[0])
+    _need(x_f16, "x_f16", "f16", ntok * hidden * 2, dev)
+    gu_stride = inter * _block_multiple(wtype_gu, hidden, "hidden")
+    d_stride = hidden * _block_multiple(wtype_down, inter, "inter")
+    for t, n, s in ((w_gate, "w_gate", gu_stride), (w_up, "w_up", gu_stride), (w_down, "w_down", d_stride)):
+        if t is None or int(t.numel()) * int(t.element_size()) != nexperts * s:
+            raise ValueError(f"{n} must hold {nexperts} expert matrices of {s} bytes")
+        _need(t, n, "u8", nexperts * s, dev)
+    nentries = int(sorted_tok.numel())
+    _need(sorted_tok, "sorted_tok", "i32", 0, dev)
+    _need(expert_off, "expert_off", "i32", (nexperts + 1) * 4, dev)
+    y = _out(y, "y", "f32", nentries * hidden * 4, dev, (nentries, hidden), torch.float32)
     need = qgemm_prefill_experts_workspace(nexperts, inter, nentries, flags)
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=w_gate.device)
+    ws = _out(ws, "ws", "u8", need, dev, (max(need, 16),), torch.uint8)
     _check("qgemm_prefill_experts", lib().qgemm_prefill_experts(
         wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, nexperts, hidden, inter,
-        _ptr(x_f16), ntok, _ptr(sorted_tok), _ptr(expert_off), nentries, _ptr(y), _ptr(ws), ws.numel(), flags,
-        _stream(stream)))
+        _ptr(x_f16), ntok, _ptr(sorted_tok), _ptr(expert_off), nentries, _ptr(y), _ptr(ws), _nbytes(ws), flags,
+        _stream(stream, dev)))
     return y, ws

@@ -268,9 +268,10 @@ __device__ __forceinline__ uint32_t sign_bits_to_bytes(uint32_t nib) {
     return __umul24(nib, 0x00204081u) & 0x01010101u;
 }
 
-// Apply per-byte signs to four codebook magnitudes: (g ^ mask) + (mask & 0x01010101) negates
-// each selected byte [GP, What changed: sign masks].  No magnitude is 0, so a negated byte
-// never carries into its neighbour.
+// Apply per-byte signs to four codebook magnitudes [GP, What changed: sign masks]: each byte
+// whose sign bit is set is replaced by its two's-complement negation (all ones XOR the byte,
+// plus one), the other bytes pass unchanged.  No magnitude is 0, so the added one never carries
+// into the neighbouring byte.
 __device__ __forceinline__ uint32_t cb3_signed(uint32_t g, uint32_t nib) {
     const uint32_t x = sign_bits_to_bytes(nib);
     // (x << 8) - x = x * 255; kept as a shift and a subtract (the compiler would otherwise emit

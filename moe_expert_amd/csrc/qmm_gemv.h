@@ -130,12 +130,13 @@ struct ActStage {
         return (((int)threadIdx.x >> (kLogL + kLogN)) << kLogL) | ((int)threadIdx.x & (LPR - 1));
     }
     // q8_1 block `base` of the buffer and the blocks kStep, 2 kStep, ... after it (pair j is
-    // block b0 + j kStep of its column, read when ok and b0 + j kStep < nb)
+    // block b0 + j kStep of its column, read when ok and b0 + j kStep < nb).  A full 32-bit
+    // multiply: buffers of up to kMaxActBytes hold more than 2^24 blocks.
     __device__ __forceinline__ void load_blocks(rsrc_t xr, const ActLds& act, uint32_t base, int b0, bool ok,
                                                 uint32_t zero_off) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const uint32_t off = (ok && b0 + j * kStep < act.nb) ? __umul24(base, 36u) + 36u * kStep * j : zero_off;
+            const uint32_t off = (ok && b0 + j * kStep < act.nb) ? base * 36u + 36u * kStep * j : zero_off;
             h[j] = ld32(xr, off);
             q0[j] = ld128(xr, off + 4);
             q1[j] = ld128(xr, off + 20);

@@ -629,7 +629,10 @@ extern "C" int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const voi
     if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(x_f16, 16) || !aligned(y, 16) ||
         !aligned(ws, 16))
         return QMM_EALIGN;
-    if ((uint64_t)ntok * hidden * 2 > kMaxBufferBytes || (uint64_t)nentries * inter * 2 > kMaxBufferBytes ||
+    // A row outside the tile (or an invalid token) is read at the buffer's end plus up to 2 k + 112
+    // bytes (chunk and step offsets), which must not wrap the 32-bit offset back into the buffer.
+    if ((uint64_t)ntok * hidden * 2 + 2 * (uint64_t)hidden + 128 > kMaxBufferBytes ||
+        (uint64_t)nentries * inter * 2 + 2 * (uint64_t)inter + 128 > kMaxBufferBytes ||
         gu_bytes > (int64_t)kMaxBufferBytes || d_bytes > (int64_t)kMaxBufferBytes || nentries > 0x7FFFFFFF ||
         hidden > kMaxK || inter > kMaxK)
         return QMM_EUNSUPPORTED;

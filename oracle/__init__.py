@@ -26,6 +26,7 @@ def _signatures():
     i64, i32 = C.c_int64, C.c_int
     return {
         "or_num_threads": (C.c_int, []),
+        "or_set_num_threads": (None, [C.c_int]),
         "or_f16_to_f32": (C.c_float, [C.c_uint16]),
         "or_f32_to_f16": (C.c_uint16, [C.c_float]),
         "or_f64_to_f16": (C.c_uint16, [C.c_double]),
@@ -77,6 +78,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.L.or_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the oracle's parallel loops (timing only; results do not depend on it)."""
+        self.L.or_set_num_threads(int(n))
 
     def row_bytes(self, wtype: int, k: int) -> int:
         return int(self.L.or_row_bytes(wtype, k))
@@ -237,4 +242,4 @@ def __getattr__(name):
     raise AttributeError(name)
 
 
-_API = set(['num_threads', 'row_bytes', 'f16_to_f32', 'f32_to_f16', 'f64_to_f16', 'dequant_f64', 'dequant_f16', 'quantize_q8_1', 'block_sums', 'gemv', 'silu_mul', 'grouped', 'prefill_rows'])
+_API = set(['num_threads', 'set_num_threads', 'row_bytes', 'f16_to_f32', 'f32_to_f16', 'f64_to_f16', 'dequant_f64', 'dequant_f16', 'quantize_q8_1', 'block_sums', 'gemv', 'silu_mul', 'grouped', 'prefill_rows'])

@@ -53,6 +53,16 @@ int or_num_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops below use from now on (n >= 1); timing only, no effect on any
+ * result (every loop writes disjoint outputs). */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------- IEEE half <-> float */
 
 /* Exact value of an IEEE-754 binary16 bit pattern. */

@@ -10,7 +10,9 @@ than one code is correct.  The check therefore
   2. propagates that bound through silu and the quantizer to an interval of valid d and q per
      value, using the oracle's g, u only;
   3. requires every GPU H byte to equal the oracle's where the interval holds a single value,
-     and to lie in the interval elsewhere;
+     and to lie in the interval elsewhere; the sum field s = fp16(d * sum q) equals the oracle's
+     where the whole block is unique, and elsewhere is what a valid binary32 d gives with the
+     GPU's own codes;
   4. requires |y_gpu - y_oracle| <= 1e-4 * sum|terms| + sum_j |W_down[r, j]| * |H_gpu_j - H_or_j|,
      the second term covering only the validated differences of step 3.
 Every expected value comes from the oracle; the GPU's outputs are only tested.
@@ -70,7 +72,17 @@ def q8_1_intervals(h_lo, h_hi):
     dh_lo = np.float32(d_lo).astype(np.float16).astype(np.float64)
     dh_hi = np.float32(d_hi).astype(np.float16).astype(np.float64)
     dh_lo = np.where(zero_possible, 0.0, dh_lo)
-    return dh_lo, dh_hi, q_lo, q_hi
+    return dh_lo, dh_hi, q_lo, q_hi, d_lo32, d_hi32, zero_possible
+
+
+def s_interval(d_lo32, d_hi32, sum_q):
+    """Bounds of the q8_1 sum field s = fp16(d * sum_q) (binary32 product) over binary32 scales d
+    in [d_lo32, d_hi32]: the product and both roundings are monotone in d for a fixed sum."""
+    sq = np.float32(sum_q)
+    with np.errstate(over="ignore"):
+        a = (d_lo32 * sq).astype(np.float16).astype(np.float64)
+        b = (d_hi32 * sq).astype(np.float16).astype(np.float64)
+    return np.minimum(a, b), np.maximum(a, b)
 
 
 def decode_q8_1(hq, n):
@@ -98,7 +110,8 @@ def check_grouped(orc_out, y_gpu, hq_gpu, g_gpu, u_gpu, wd_exact_by_entry, inter
     h_lo, h_hi = silu_mul_interval(g32 - dg, g32 + dg, u32 - du, u32 + du)
     pad = 8 * U32 * np.maximum(np.abs(h_lo), np.abs(h_hi)) + 1e-38
     h_lo, h_hi = h_lo - pad, h_hi + pad
-    dh_lo, dh_hi, q_lo, q_hi = q8_1_intervals(h_lo.reshape(ne, -1, 32), h_hi.reshape(ne, -1, 32))
+    dh_lo, dh_hi, q_lo, q_hi, d_lo32, d_hi32, zero_ok = q8_1_intervals(h_lo.reshape(ne, -1, 32),
+                                                                        h_hi.reshape(ne, -1, 32))
     # 3. H bytes
     d_gpu, q_gpu = decode_q8_1(hq_gpu, inter)
     d_or, q_or = decode_q8_1(orc_out["hq"], inter)
@@ -109,6 +122,17 @@ def check_grouped(orc_out, y_gpu, hq_gpu, g_gpu, u_gpu, wd_exact_by_entry, inter
     stats["ambiguous_values"] = int((~unique).sum())
     hb_gpu = np.asarray(hq_gpu, np.uint8).reshape(ne, -1, 36)
     hb_or = np.asarray(orc_out["hq"], np.uint8).reshape(ne, -1, 36)
+    # the sum field s = fp16(d * sum q): equal to the oracle's where the block's d and codes are
+    # all unique; elsewhere s is what a valid binary32 d gives with the GPU's own codes (0 for a
+    # block that may be all zero)
+    s_gpu = hb_gpu[:, :, 2:4].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    blk_unique = unique.all(axis=-1) & (d_lo32 == d_hi32)
+    assert np.array_equal(hb_gpu[:, :, 2:4][blk_unique], hb_or[:, :, 2:4][blk_unique]), \
+        "H sum field differs where the block is unique"
+    s_lo, s_hi = s_interval(d_lo32, d_hi32, q_gpu.sum(axis=-1))
+    s_ok = ((s_gpu >= s_lo) & (s_gpu <= s_hi)) | (zero_ok & (s_gpu == 0) & (d_gpu == 0))
+    assert s_ok.all(), f"H sum field outside its valid interval in {(~s_ok).sum()} blocks"
+    stats["s_blocks_checked"] = int(s_ok.size)
     diff_blocks = np.any(hb_gpu != hb_or, axis=-1)
     stats["h_blocks_differ"] = int(diff_blocks.sum())
     stats["h_values_differ"] = int((q_gpu != q_or).sum())

@@ -54,15 +54,16 @@ def test_q8_0_summary_groups_dispatches_in_order(tmp_path, traffic_file):
     for (nrows, k, n), b in expect.items():
         r = rec[f"gemv:{synth.Q8_0}:{nrows}x{k}"]
         assert r["bytes_per_launch"][str(n)] == b
-        assert r["source_sha256"] == bench.source_digest()
+        assert r["source_sha256"] == bench.source_digest(r["sources"])
 
 
 def test_gemv_summary_and_lookup(tmp_path, traffic_file):
-    """The headline GEMV summary keys launches by pass width; the lookup returns the record only
-    while the sources hash the same."""
+    """The headline GEMV summary keys launches by pass width (fused one-column kernel included);
+    the lookup returns the record only while the sources hash the same."""
     rows_f, rows_w = _copies(32768.0), _copies(65536.0)
-    for n in bench.PROBE_COLS:
-        name = f"void qmm::gemv_kernel<2, false, {n}, 5, false, 1, 16, 256>(x)"
+    for n in bench.PROBE_COLS:   # the fused kernel where the step fuses, the q8_1 GEMV elsewhere
+        name = (f"void qmm::gemv_f32_kernel<2, 5, {n}, 512>(x)" if n in bench.FUSED_COLS else
+                f"void qmm::gemv_kernel<2, false, {n}, 5, false, 1, 16, 256>(x)")
         rows_f += [(name, 5800.0 + n)] * 4
         rows_w += [(name, 32.0 * n)] * 4
     _write(tmp_path / "f.csv", "FETCH_SIZE", rows_f)

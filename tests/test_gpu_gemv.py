@@ -14,10 +14,13 @@ pytestmark = pytest.mark.gpu
 FORMATS = [M.QMM_Q8_0, M.QMM_IQ4_NL, M.QMM_CB3]
 
 
-def case(wtype, nrows, k, ncols, seed):
+def case(wtype, nrows, k, ncols, seed, full_range=False):
+    """Seeded weights, codebook and activations; full_range: Q8_0 factors over all of
+    [-128, 127]."""
     rng = synth.rng_for(seed)
     grid = synth.cb3_grid(rng) if wtype == M.QMM_CB3 else None
-    w = synth.weights(wtype, rng, nrows, k)
+    kw = dict(qlo=-128) if full_range and wtype == M.QMM_Q8_0 else {}
+    w = synth.weights(wtype, rng, nrows, k, **kw)
     x = synth.activations(rng, ncols, k)
     return w, grid, x
 
@@ -242,3 +245,51 @@ def test_mfma_loop_reference():
             ref[w0 + li] = 8 * iters * D[rows, li % 32].sum()
     ref[256:] = ref[:256]
     assert np.array_equal(out, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("nrows,k,ncols", [(64, 2560, 1), (37, 6144, 8), (100, 1024, 5)])
+def test_q8_0_minus_128(nrows, k, ncols):
+    """Q8_0 factors over all of [-128, 127], plus rows whose every factor is -128: block sums
+    bit-exact, one-hot rows bit-exact, outputs within the fp32 tolerance."""
+    print(f"Q8_0 factor -128: nrows={nrows} k={k} ncols={ncols}", flush=True)
+    wt = M.QMM_Q8_0
+    w, grid, x = case(wt, nrows, k, ncols, 1300 + nrows, full_range=True)
+    w = w.reshape(nrows, k // 32, 34).copy()
+    w[:3, :, 2:] = np.uint8(0x80)                       # three rows of -128 only
+    w = w.reshape(nrows, -1)
+    assert (w.reshape(nrows, -1, 34)[3:, :, 2:].view(np.int8) == -128).any()
+    xq = oracle.quantize_q8_1(x)
+    got = host(M.qmm_debug_block_sums(wt, dev(w), nrows, k, dev(xq), ncols))
+    assert np.array_equal(got, oracle.block_sums(wt, w, k, xq))
+    y, _ = gpu_gemv(wt, w, grid, x, nrows, k, ncols)
+    ref, a = oracle.gemv(wt, w, k, xq)
+    check_tol(y, ref, a, what="Q8_0 -128")
+    # one-hot rows: only block r of row r keeps its scale
+    nb = k // 32
+    w1 = w[:min(nrows, nb)].reshape(-1, nb, 34).copy()
+    for r in range(w1.shape[0]):
+        w1[r, np.arange(nb) != r, 0:2] = 0
+    w1 = w1.reshape(w1.shape[0], -1)
+    y1, _ = gpu_gemv(wt, w1, grid, x, w1.shape[0], k, ncols)
+    ref1, _ = oracle.gemv(wt, w1, k, xq)
+    assert np.array_equal(y1, ref1.astype(np.float32))
+
+
+def test_gemv_activation_blocks_beyond_2_24():
+    """A q8_1 buffer of more than 2^24 blocks (k = 32768, 16392 columns, 604 MB): the blocks of
+    the last 8 columns lie at and past block 2^24, and their outputs equal an 8-column call on a
+    copy of those columns, bitwise (the staging offset is a full 32-bit product; out-of-range
+    reads return zeros, so a wrong offset shows as a wrong value, not a fault)."""
+    import torch
+    k, ncols, nrows = 32768, 16392, 16
+    print(f"gemv with {ncols * k // 32} q8_1 blocks (k={k}, {ncols} columns)", flush=True)
+    w, grid, x = case(M.QMM_Q8_0, nrows, k, 8, 1400)
+    xq8 = M.qmm_quantize_q8_1(dev(x))
+    xq = torch.zeros((ncols, (k // 32) * 36), dtype=torch.uint8, device="cuda")
+    xq[ncols - 8:] = xq8
+    wd = dev(w)
+    y = host(M.qgemv_dense(M.QMM_Q8_0, wd, nrows, k, xq, ncols))
+    y8 = host(M.qgemv_dense(M.QMM_Q8_0, wd, nrows, k, xq8, 8))
+    assert np.array_equal(y[ncols - 8:].view(np.uint32), y8.view(np.uint32))
+    ref, a = oracle.gemv(M.QMM_Q8_0, w, k, host(xq8))
+    check_tol(y8, ref, a)

@@ -13,14 +13,17 @@ pytestmark = pytest.mark.gpu
 
 
 class Experts:
-    def __init__(self, seed, nexp, hidden, inter, wt_gu=M.QMM_CB3, wt_down=M.QMM_IQ4_NL):
+    def __init__(self, seed, nexp, hidden, inter, wt_gu=M.QMM_CB3, wt_down=M.QMM_IQ4_NL, full_range=False):
         rng = synth.rng_for(seed)
         self.grid = synth.cb3_grid(synth.rng_for(synth.SEEDS["cb3_grid"]))
         self.wt_gu, self.wt_down = wt_gu, wt_down
         self.hidden, self.inter, self.nexp = hidden, inter, nexp
-        self.wg = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
-        self.wu = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
-        self.wd = np.stack([synth.weights(wt_down, rng, hidden, inter) for _ in range(nexp)])
+
+        def wts(wt, nrows, k):   # full_range: Q8_0 factors over all of [-128, 127]
+            return synth.weights(wt, rng, nrows, k, **(dict(qlo=-128) if full_range and wt == M.QMM_Q8_0 else {}))
+        self.wg = np.stack([wts(wt_gu, inter, hidden) for _ in range(nexp)])
+        self.wu = np.stack([wts(wt_gu, inter, hidden) for _ in range(nexp)])
+        self.wd = np.stack([wts(wt_down, hidden, inter) for _ in range(nexp)])
         self.d = dict(wg=dev(self.wg), wu=dev(self.wu), wd=dev(self.wd), grid=dev(self.grid))
         self._wd_exact = {}
 
@@ -89,8 +92,11 @@ def test_grouped_ragged_passes():
 
 @pytest.mark.parametrize("wt_gu,wt_down", [(M.QMM_IQ4_NL, M.QMM_Q8_0), (M.QMM_Q8_0, M.QMM_IQ4_NL)])
 def test_grouped_other_formats(wt_gu, wt_down):
+    """Q8_0 matrices (down, or gate/up) with factors over all of [-128, 127]."""
     print(f"grouped formats gu={wt_gu} down={wt_down}", flush=True)
-    ex = Experts(820 + wt_gu, 4, 1024, 128, wt_gu=wt_gu, wt_down=wt_down)
+    ex = Experts(820 + wt_gu, 4, 1024, 128, wt_gu=wt_gu, wt_down=wt_down, full_range=True)
+    q8 = ex.wd if wt_down == M.QMM_Q8_0 else ex.wg
+    assert (q8.reshape(-1, 34)[:, 2:].view(np.int8) == -128).any()
     ge, go, ec = synth.decode_routing(synth.rng_for(821), 4, 4, 2)
     run_case(ex, ge, go, ec, 2, 822)
 

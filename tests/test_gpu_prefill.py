@@ -7,8 +7,9 @@ interval the bound allows; the interval is widened by 8 binary32 ulp for the dev
 silu (expf within 1 ulp, v_rcp_f32 of 1 + e within 1 ulp, two products) against the
 oracle's binary64 exp.  Y: within 1e-4 * sum|w h| plus the effect of the validated H16
 differences.  Full size (8192
-tokens x 2560, 128 experts, top-8) is checked on sampled entries, including every entry of
-an expert split into several tiles."""
+tokens x 2560, 128 experts, top-8) is checked on every row of 8 whole experts (each split into
+several tiles) plus sampled rows.  The FP16 weights the MFMAs consume are pinned bit for bit
+through one-hot tokens (G = W16 exactly) and one-hot H16 (Y = Wd16 exactly)."""
 import numpy as np
 import pytest
 
@@ -22,14 +23,22 @@ pytestmark = pytest.mark.gpu
 U32 = 2.0 ** -24
 
 
+def weights(wt, rng, nrows, k, full_range):
+    """Seeded blocks; full_range: Q8_0 factors drawn from all of [-128, 127] (the generator's
+    default stops at -127)."""
+    kw = dict(qlo=-128) if full_range and wt == M.QMM_Q8_0 else {}
+    return synth.weights(wt, rng, nrows, k, **kw)
+
+
 class Prefill:
-    def __init__(self, seed, nexp, ntok, topk, hidden, inter, wt_gu=M.QMM_IQ4_NL, wt_down=M.QMM_Q8_0):
+    def __init__(self, seed, nexp, ntok, topk, hidden, inter, wt_gu=M.QMM_IQ4_NL, wt_down=M.QMM_Q8_0,
+                 full_range=False):
         rng = synth.rng_for(seed)
         self.nexp, self.hidden, self.inter = nexp, hidden, inter
         self.wt_gu, self.wt_down = wt_gu, wt_down
-        self.wg = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
-        self.wu = np.stack([synth.weights(wt_gu, rng, inter, hidden) for _ in range(nexp)])
-        self.wd = np.stack([synth.weights(wt_down, rng, hidden, inter) for _ in range(nexp)])
+        self.wg = np.stack([weights(wt_gu, rng, inter, hidden, full_range) for _ in range(nexp)])
+        self.wu = np.stack([weights(wt_gu, rng, inter, hidden, full_range) for _ in range(nexp)])
+        self.wd = np.stack([weights(wt_down, rng, hidden, inter, full_range) for _ in range(nexp)])
         self.x16 = synth.prefill_tokens(rng, ntok, hidden)
         self.st, self.off = synth.prefill_routing(rng, ntok, nexp, topk)
         self.d = dict(wg=dev(self.wg), wu=dev(self.wu), wd=dev(self.wd), x=dev(self.x16.view(np.uint16)),
@@ -126,18 +135,114 @@ def test_prefill_formats_swapped():
     print(pf.check(np.arange(pf.st.size), y, ws), flush=True)
 
 
-def test_prefill_full_size_sampled():
-    """8192 tokens x 2560, 128 experts, top-8, gate/up IQ4_NL 2560->1024, down Q8_0 1024->2560."""
+@pytest.mark.parametrize("wt_gu,wt_down", [(M.QMM_Q8_0, M.QMM_Q8_0), (M.QMM_IQ4_NL, M.QMM_Q8_0)])
+def test_prefill_q8_0_full_range(wt_gu, wt_down):
+    """Q8_0 factors over all of [-128, 127] (-128 is the biased byte 0x00 of the conversion)."""
+    print(f"prefill Q8_0 factors -128..127: gu={wt_gu} down={wt_down}", flush=True)
+    pf = Prefill(925 + wt_gu, 4, 80, 2, 320, 128, wt_gu=wt_gu, wt_down=wt_down, full_range=True)
+    assert (pf.wd.reshape(-1, 34)[:, 2:].view(np.int8) == -128).any()
+    y, ws = pf.run_gpu()
+    print(pf.check(np.arange(pf.st.size), y, ws), flush=True)
+
+
+def identity_tokens(hidden):
+    """Token t is the unit row e_t (binary16 1.0 at column t): X16 = I."""
+    return np.eye(hidden, dtype=np.float16)
+
+
+def every_token_routing(nexp, ntok):
+    """Every token to every expert; rows sorted by expert, then token."""
+    st = np.tile(np.arange(ntok, dtype=np.int32), nexp)
+    off = (np.arange(nexp + 1, dtype=np.int32) * ntok).astype(np.int32)
+    return st, off
+
+
+@pytest.mark.parametrize("wt_gu", [M.QMM_IQ4_NL, M.QMM_Q8_0])
+def test_prefill_gate_up_weights_bitexact(wt_gu):
+    """The FP16 weights the gate/up MFMA consumes equal the dequantized values bit for bit:
+    with token t = e_t every product but one is a zero, so G[row of (e, t)][i] = Wg16[e][i][t]
+    exactly (likewise U), and the debug G, U of two experts x 2560 tokens are compared with the
+    oracle's FP16 dequantization of every (i, t) of both matrices."""
+    hidden, inter, nexp = 2560, 1024, 2
+    print(f"prefill one-hot tokens: gate/up weights bit-exact, gu={wt_gu}", flush=True)
+    pf = Prefill(950 + wt_gu, nexp, 1, 1, hidden, inter, wt_gu=wt_gu, wt_down=M.QMM_Q8_0, full_range=True)
+    pf.x16 = identity_tokens(hidden)
+    pf.st, pf.off = every_token_routing(nexp, hidden)
+    pf.d["x"], pf.d["st"], pf.d["off"] = dev(pf.x16.view(np.uint16)), dev(pf.st), dev(pf.off)
+    y, ws = pf.run_gpu()
+    _, g, u = pf.split_ws(ws)
+    for e in range(nexp):
+        rows = slice(int(pf.off[e]), int(pf.off[e + 1]))
+        for got, wq, what in ((g, pf.wg, "gate"), (u, pf.wu, "up")):
+            w16 = oracle.dequant_f16(wt_gu, wq[e], hidden).view(np.float16).astype(np.float32)  # [inter, hidden]
+            ok = got[rows] == w16.T
+            assert ok.all(), f"expert {e} {what}: {(~ok).sum()} weights differ"
+
+
+def unit_gate_up(nexp, hidden, inter):
+    """Q8_0 gate/up matrices for which token e_t gives h = 1.0 at intermediate index t mod inter
+    and 0 elsewhere: gate value 32 (d = 1/2, q = 64) and up value 1/32 (d = 2^-10, q = 32) at
+    the columns k with k mod inter = row, zero factors elsewhere; silu(32) * (1/32) = 1 in
+    binary32 (e^-32 vanishes beside 1)."""
+    def mat(d, q):
+        m = np.zeros((inter, hidden // 32, 34), np.uint8)
+        m[:, :, 0:2] = np.array([d], np.float16).view(np.uint8)
+        vals = np.zeros((inter, hidden), np.int8)
+        k = np.arange(hidden)
+        vals[k % inter, k] = q
+        m[:, :, 2:] = vals.reshape(inter, hidden // 32, 32).view(np.uint8)
+        return m.reshape(inter, -1)
+    g = mat(0.5, 64)
+    u = mat(2.0 ** -10, 32)
+    return np.stack([g] * nexp), np.stack([u] * nexp)
+
+
+@pytest.mark.parametrize("wt_down", [M.QMM_Q8_0, M.QMM_IQ4_NL])
+def test_prefill_down_weights_bitexact(wt_down):
+    """The FP16 weights of the down MFMA equal the dequantized values bit for bit: token e_t
+    through unit_gate_up gives H16 = e_(t mod inter), so Y[row of (e, t)][j] = Wd16[e][j][t mod
+    inter] exactly; every (j, i) of two experts' down matrices is compared with the oracle."""
+    hidden, inter, nexp = 2560, 1024, 2
+    print(f"prefill one-hot H: down weights bit-exact, down={wt_down}", flush=True)
+    pf = Prefill(960 + wt_down, nexp, 1, 1, hidden, inter, wt_gu=M.QMM_Q8_0, wt_down=wt_down, full_range=True)
+    pf.wg, pf.wu = unit_gate_up(nexp, hidden, inter)
+    pf.x16 = identity_tokens(hidden)
+    pf.st, pf.off = every_token_routing(nexp, hidden)
+    pf.d.update(wg=dev(pf.wg), wu=dev(pf.wu), x=dev(pf.x16.view(np.uint16)), st=dev(pf.st), off=dev(pf.off))
+    y, ws = pf.run_gpu()
+    h16, _, _ = pf.split_ws(ws)
+    t = np.arange(hidden)
+    one_hot = np.zeros((hidden, inter), np.float16)
+    one_hot[t, t % inter] = 1.0
+    yh = host(y)
+    for e in range(nexp):
+        rows = slice(int(pf.off[e]), int(pf.off[e + 1]))
+        assert np.array_equal(h16[rows], one_hot.view(np.uint16)), f"expert {e}: H16 is not one-hot"
+        wd16 = oracle.dequant_f16(wt_down, pf.wd[e], inter).view(np.float16).astype(np.float32)  # [hidden, inter]
+        ok = yh[rows] == wd16[:, t % inter].T
+        assert ok.all(), f"expert {e}: {(~ok).sum()} down weights differ"
+    # and the tolerance check of the general path agrees on a few rows
+    print(pf.check(np.array([0, 1, 1023, 1024, 2559, 2560, 5119]), y, ws), flush=True)
+
+
+def test_prefill_full_size_whole_experts():
+    """8192 tokens x 2560, 128 experts, top-8, gate/up IQ4_NL 2560->1024, down Q8_0 1024->2560:
+    every row of 8 whole experts (the largest and the smallest, both split into several tiles,
+    and 6 drawn at random), plus 64 random rows of the others, against the oracle."""
     print("prefill full size: 8192 x 2560, 128 experts, top-8", flush=True)
     pf = Prefill(synth.SEEDS["prefill"], 128, 8192, 8, 2560, 1024)
     y, ws = pf.run_gpu()
-    rng = synth.rng_for(930)
-    samples = set(rng.choice(pf.st.size, size=160, replace=False).tolist())
     counts = np.diff(pf.off)
-    split = [e for e in range(128) if counts[e] > 256 and counts[e] % 32][:1]
-    for e in split:                        # every row of one expert split into several tiles
-        samples.update(range(pf.off[e], pf.off[e + 1]))
+    rng = synth.rng_for(930)
+    exps = {int(np.argmax(counts)), int(np.argmin(counts))}
+    exps.update(int(e) for e in rng.choice(128, size=12, replace=False) if len(exps) < 8)
+    exps = sorted(exps)[:8]
+    samples = set()
+    for e in exps:
+        samples.update(range(int(pf.off[e]), int(pf.off[e + 1])))
+    samples.update(rng.choice(pf.st.size, size=64, replace=False).tolist())
     samples.update([0, pf.st.size - 1])
+    print(f"experts {exps} ({counts[exps].tolist()} rows), {len(samples)} rows in all", flush=True)
     print(pf.check(sorted(samples), y, ws), flush=True)
     # rows of all other experts are finite (no unwritten output)
     assert np.isfinite(host(y)).all()

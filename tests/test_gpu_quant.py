@@ -44,7 +44,7 @@ def test_quantize_rejects_ldx():
 
 @pytest.mark.parametrize("wtype", [M.QMM_Q8_0, M.QMM_IQ4_NL, M.QMM_CB3])
 def test_dequant_every_scale(wtype):
-    """Every finite fp16 scale, random factors: bit-exact FP16."""
+    """Every finite fp16 scale, random factors (Q8_0: over all of [-128, 127]): bit-exact FP16."""
     print(f"dequant every scale wtype={wtype}", flush=True)
     rng = synth.rng_for(100 + wtype)
     d = finite_f16_patterns()
@@ -53,8 +53,11 @@ def test_dequant_every_scale(wtype):
     nblk = d.size
     k = bv * 8
     grid = synth.cb3_grid(rng) if wtype == M.QMM_CB3 else None
-    w = synth.weights(wtype, rng, nblk // 8 + 1, k).reshape(-1, bb)[:nblk].copy()
+    kw = dict(qlo=-128) if wtype == M.QMM_Q8_0 else {}     # every int8 factor, -128 included
+    w = synth.weights(wtype, rng, nblk // 8 + 1, k, **kw).reshape(-1, bb)[:nblk].copy()
     w[:, 0:2] = d.view(np.uint8).reshape(-1, 2)
+    if wtype == M.QMM_Q8_0:
+        assert (w[:, 2:].view(np.int8) == -128).any() and (w[:, 2:].view(np.int8) == 127).any()
     w = w[: (nblk // 8) * 8].reshape(-1, 8 * bb)
     ref = oracle.dequant_f16(wtype, w, k, grid)
     got = host(M.qmm_dequant_f16(wtype, dev(w), w.shape[0], k, grid=None if grid is None else dev(grid)))

@@ -140,3 +140,99 @@ def _pf_args(**kw):
 def test_prefill_rejects(kw, expect):
     assert M.lib().qgemm_prefill_experts(*_pf_args(**kw)) == expect
     assert M.lib().qgemm_prefill_experts_workspace(4, 1024, 128, 0) >= 128 * 1024 * 2
+
+
+def test_prefill_rejects_offsets_that_would_wrap():
+    """x_f16 whose size plus the zero-read headroom (2 hidden + 128 bytes) passes 4 GiB."""
+    assert M.lib().qgemm_prefill_experts(*_pf_args(ntok=838860)) == -2
+    assert M.lib().qgemm_prefill_experts(*_pf_args(ntok=838859, ws_bytes=64)) == -5   # passes that check
+
+
+# ------------------------------------------------------------------ binding checks (no GPU)
+
+class FakeGpuTensor:
+    """Duck-typed stand-in for a contiguous GPU tensor: the binding's checks read only these
+    attributes, and every case below is refused before its pointer would be used."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = self.device.type == "cuda"
+        self._contiguous = contiguous
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        import torch
+        return torch.empty((), dtype=self.dtype).element_size()
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return self._contiguous
+
+    def data_ptr(self):
+        raise AssertionError("the binding must refuse this call before reading a pointer")
+
+    def __getitem__(self, i):
+        return FakeGpuTensor(self.shape[1:], self.dtype, str(self.device))
+
+    def view(self, *shape):
+        return FakeGpuTensor(shape, self.dtype, str(self.device))
+
+
+def _gemv_tensors(**kw):
+    import torch
+    t = dict(w=FakeGpuTensor((64, 1440), torch.uint8), xq=FakeGpuTensor((2, 2880), torch.uint8),
+             y=FakeGpuTensor((2, 64), torch.float32))
+    t.update(kw)
+    return t
+
+
+@pytest.mark.parametrize("change", [
+    "y_short", "y_dtype", "xq_short", "xq_dtype", "w_short", "w_cpu", "w_strided", "xq_other_gpu", "k_ragged"])
+def test_binding_refuses_bad_gemv_tensors(change):
+    import torch
+    F = FakeGpuTensor
+    kw = {"y_short": dict(y=F((2, 63), torch.float32)), "y_dtype": dict(y=F((2, 64), torch.float16)),
+          "xq_short": dict(xq=F((1, 2880), torch.uint8)), "xq_dtype": dict(xq=F((2, 720), torch.float32)),
+          "w_short": dict(w=F((63, 1440), torch.uint8)), "w_cpu": dict(w=F((64, 1440), torch.uint8, "cpu")),
+          "w_strided": dict(w=F((64, 1440), torch.uint8, contiguous=False)),
+          "xq_other_gpu": dict(xq=F((2, 2880), torch.uint8, "cuda:1")), "k_ragged": {}}[change]
+    t = _gemv_tensors(**kw)
+    k = 2576 if change == "k_ragged" else 2560
+    with pytest.raises(ValueError):
+        M.qgemv_dense(M.QMM_IQ4_NL, t["w"], 64, k, t["xq"], 2, y=t["y"])
+
+
+def test_binding_refuses_bad_grouped_and_prefill_tensors():
+    import torch
+    F = FakeGpuTensor
+    u8, i32 = torch.uint8, torch.int32
+    wg, wd = F((4, 1024 * 1440), u8), F((4, 2560 * 1088), u8)
+    xq, ge, go, ec = F((2, 2880), u8), F((2,), i32), F((3,), i32), F((4,), i32)
+    # w_up with fewer experts than w_gate
+    with pytest.raises(ValueError):
+        M.qgemv_grouped_experts(M.QMM_IQ4_NL, wg, F((3, 1024 * 1440), u8), M.QMM_Q8_0, wd, 2560, 1024, xq, ge, go, ec)
+    # a short entry-offset array
+    with pytest.raises(ValueError):
+        M.qgemv_grouped_experts(M.QMM_IQ4_NL, wg, wg, M.QMM_Q8_0, wd, 2560, 1024, xq, ge, F((2,), i32), ec)
+    # a float16 x for the prefill is fine, a half-width one is not; int64 token ids are not
+    x16 = F((64, 1280), torch.float16)
+    st, off = F((128,), i32), F((5,), i32)
+    with pytest.raises(ValueError):
+        M.qgemm_prefill_experts(M.QMM_IQ4_NL, wg, wg, M.QMM_Q8_0, wd, 4, 2560, 1024, x16, st, off)
+    with pytest.raises(ValueError):
+        M.qgemm_prefill_experts(M.QMM_IQ4_NL, wg, wg, M.QMM_Q8_0, wd, 4, 2560, 1024, F((64, 2560), torch.float16),
+                                F((128,), torch.int64), off)
+    # a caller workspace below the query
+    with pytest.raises(ValueError):
+        M.qgemm_prefill_experts(M.QMM_IQ4_NL, wg, wg, M.QMM_Q8_0, wd, 4, 2560, 1024, F((64, 2560), torch.float16),
+                                st, off, y=F((128, 2560), torch.float32), ws=F((64,), u8))
