@@ -45,6 +45,9 @@ def _signatures():
                              P, P, P, P, P, P, P, P]),
         "or_prefill_rows": (i32, [i32, P, P, i64, i32, P, i64, P, i32, i64, i64, P, i64, P, P,
                                   P, i64, P, P, P, P, P, P, P]),
+        "or_moe_combine": (i32, [P, i64, i64, P, P, i64, i32, P]),
+        "or_dense_rows": (i32, [i32, P, P, i64, i64, P, i64, P, i64, P, P]),
+        "or_pack_planes": (i32, [i32, P, i64, i64, P]),
     }
 
 
@@ -223,6 +226,41 @@ class Oracle:
         return out
 
 
+    def moe_combine(self, y, row_idx, w) -> np.ndarray:
+        """out [ntok, hidden] float32: the router-weighted sum of each token's expert rows of y
+        [nrows, hidden] in k order (row_idx, w: [ntok, topk])."""
+        y = _c(y, np.float32)
+        ri = _c(row_idx, np.int32)
+        ww = _c(w, np.float32)
+        ntok, topk = ri.shape
+        out = np.empty((ntok, y.shape[1]), np.float32)
+        if self.L.or_moe_combine(_p(y), y.shape[0], y.shape[1], _p(ri), _p(ww), ntok, topk, _p(out)):
+            raise ValueError("bad combine arguments")
+        return out
+
+    def dense_rows(self, wtype: int, w, nrows: int, k: int, x16, samples, grid=None):
+        """Dense projection of the sampled prompt tokens on FP16 weights: returns (Y, Yabs), each
+        [ns, nrows] float64.  wtype 0: w is binary16 [nrows, k] already."""
+        w = np.ascontiguousarray(w)
+        x16 = np.ascontiguousarray(x16).view(np.uint16)
+        sm = _c(samples, np.int64)
+        Y = np.empty((sm.size, nrows))
+        A = np.empty((sm.size, nrows))
+        g = _grid(grid)
+        if self.L.or_dense_rows(wtype, _p(w), _p(g), nrows, k, _p(x16), x16.shape[0], _p(sm), sm.size, _p(Y), _p(A)):
+            raise ValueError("bad dense_rows arguments")
+        return Y, A
+
+    def pack_planes(self, wtype: int, w, k: int) -> np.ndarray:
+        """Planes of Q8_0 / IQ4_NL rows (same shape and size as the blocks)."""
+        w = _c(w, np.uint8)
+        nrows = w.size // self.row_bytes(wtype, k)
+        out = np.empty_like(w)
+        if self.L.or_pack_planes(wtype, _p(w), nrows, k, _p(out)):
+            raise ValueError("bad pack_planes arguments")
+        return out
+
+
 _default = None
 
 
@@ -242,4 +280,4 @@ def __getattr__(name):
     raise AttributeError(name)
 
 
-_API = set(['num_threads', 'set_num_threads', 'row_bytes', 'f16_to_f32', 'f32_to_f16', 'f64_to_f16', 'dequant_f64', 'dequant_f16', 'quantize_q8_1', 'block_sums', 'gemv', 'silu_mul', 'grouped', 'prefill_rows'])
+_API = set(['num_threads', 'set_num_threads', 'row_bytes', 'f16_to_f32', 'f32_to_f16', 'f64_to_f16', 'dequant_f64', 'dequant_f16', 'quantize_q8_1', 'block_sums', 'gemv', 'silu_mul', 'grouped', 'prefill_rows', 'moe_combine', 'dense_rows', 'pack_planes'])

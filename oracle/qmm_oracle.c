@@ -455,3 +455,100 @@ int or_prefill_rows(int wtype_gu, const uint8_t* w_gate, const uint8_t* w_up, in
     free(wg); free(wu); free(wd); free(t16);
     return rc;
 }
+
+/* ---------------------------------------------------------------- MoE combine */
+
+/* MoE combine [DQ, Change: the combine sums a token's expert rows in a fixed k order; profile
+ * block: moe_combine4 reads the rows at bandwidth].  The pages fix the k order but not the
+ * expression; the reading used: out[t][j] = sum over k = 0 .. topk-1 of w[t][k] * y[r][j] with
+ * r = row_idx[t][k], starting from +0 and adding in k order, every product and every sum one
+ * binary32 rounding (no fused multiply-add); a row index outside [0, nrows) adds nothing.
+ *   y: [nrows][hidden]; row_idx, w: [ntok][topk]; out: [ntok][hidden]. */
+int or_moe_combine(const float* y, int64_t nrows, int64_t hidden, const int32_t* row_idx,
+                   const float* w, int64_t ntok, int topk, float* out) {
+    if (hidden < 1 || topk < 1 || ntok < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t)
+        for (int64_t j = 0; j < hidden; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < topk; ++k) {
+                int32_t r = row_idx[t * topk + k];
+                if (r < 0 || r >= nrows) continue;
+                float prod = w[t * topk + k] * y[r * hidden + j];
+                acc = acc + prod;
+            }
+            out[t * hidden + j] = acc;
+        }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- dense prompt projections */
+
+/* Dense projection of prompt tokens on FP16-dequantized weights [DQ, Change: the dense weights
+ * dequantized to FP16 for a matrix product over the prompt; PF, Summary: FP16 products, FP32
+ * sums].  For each sampled token t: Y[s][r] = sum over k of W16[r][k] * X16[t][k], with W16 the
+ * FP16 dequantization (or_dequant_f16), products exact in double, double sums; Yabs the sum of
+ * |W16 X16| (the scale of the tolerance).  wtype 0 takes w as binary16 bits [nrows][k] already.
+ *   x16: [ntok][k] binary16 bits; samples: token indices; Y, Yabs: [ns][nrows] (either may be
+ *   NULL). */
+int or_dense_rows(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
+                  const uint16_t* x16, int64_t ntok, const int64_t* samples, int64_t ns,
+                  double* Y, double* Yabs) {
+    if (nrows < 1 || k < 1) return -1;
+    if (wtype != 0 && !or_row_bytes(wtype, k)) return -1;
+    uint16_t* w16 = (uint16_t*)malloc(sizeof(uint16_t) * nrows * k);
+    if (!w16) return -2;
+    if (wtype == 0)
+        memcpy(w16, w, sizeof(uint16_t) * nrows * k);
+    else
+        or_dequant_f16(wtype, (const uint8_t*)w, grid, nrows, k, w16, k);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t s = 0; s < ns; ++s) {
+        int64_t t = samples[s];
+        for (int64_t r = 0; r < nrows; ++r) {
+            double acc = 0.0, aabs = 0.0;
+            if (t >= 0 && t < ntok)
+                for (int64_t kk = 0; kk < k; ++kk) {
+                    double p = (double)or_f16_to_f32(w16[r * k + kk]) * (double)or_f16_to_f32(x16[t * k + kk]);
+                    acc += p;
+                    aabs += fabs(p);
+                }
+            if (Y) Y[s * nrows + r] = acc;
+            if (Yabs) Yabs[s * nrows + r] = aabs;
+        }
+    }
+    free(w16);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- weight planes */
+
+/* Repack of Q8_0 / IQ4_NL rows into planes [GP, What changed: a device-side repack of the
+ * GGUF blocks into planes, an int8 plane plus scales, owned by explicit pack / release calls].
+ * The pages name the planes but not their layout; the reading used: a row is cut into tiles of
+ * 16 consecutive blocks (the last tile of a row may hold fewer, n = the blocks left); a tile is
+ * the factor bytes of its n blocks back to back in block order (Q8_0: the 32 int8 q; IQ4_NL: the
+ * 16 index bytes), then the n fp16 scales in block order.  A row keeps its size and position,
+ * so the planes of a matrix take exactly the bytes of its blocks. */
+int or_pack_planes(int wtype, const uint8_t* w, int64_t nrows, int64_t k, uint8_t* out) {
+    if (wtype != OR_Q8_0 && wtype != OR_IQ4_NL) return -1;
+    int64_t rb = or_row_bytes(wtype, k);
+    if (!rb) return -1;
+    int64_t nb = k / 32;
+    int bb = block_bytes(wtype);      /* 34 or 18 */
+    int fb = bb - 2;                  /* factor bytes per block: 32 or 16 */
+    for (int64_t r = 0; r < nrows; ++r) {
+        const uint8_t* row = w + r * rb;
+        uint8_t* dst = out + r * rb;
+        for (int64_t b0 = 0; b0 < nb; b0 += 16) {
+            int64_t n = nb - b0 < 16 ? nb - b0 : 16;
+            uint8_t* tile = dst + b0 * bb;
+            for (int64_t i = 0; i < n; ++i) {
+                const uint8_t* blk = row + (b0 + i) * bb;
+                memcpy(tile + i * fb, blk + 2, (size_t)fb);       /* factors */
+                memcpy(tile + n * fb + 2 * i, blk, 2);            /* scale */
+            }
+        }
+    }
+    return 0;
+}

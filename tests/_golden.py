@@ -76,3 +76,40 @@ def q8_1_cases():
                         q=np.array([int(v) for v in c["q"]], np.int8),
                         d=int(c["d"][0], 16), s=int(c["s"][0], 16)))
     return out
+
+
+def _cases(name):
+    cases, cur = [], None
+    for line in _lines(name):
+        if line.startswith("case"):
+            cur = {"name": line.split()[1]}
+            cases.append(cur)
+            continue
+        key, val = line.split(":", 1)
+        cur[key.strip()] = val.split()
+    return cases
+
+
+def _hexf(v):
+    return float.fromhex(v)
+
+
+def moe_combine_cases():
+    """(name, y [nrows, 1] float32, idx [1, topk], w [1, topk], out float) per case."""
+    out = []
+    for c in _cases("moe_combine.txt"):
+        y = np.array([_hexf(v) for v in c["y"]], np.float32)[:, None]
+        idx = np.array([[int(v) for v in c["idx"]]], np.int32)
+        w = np.array([[_hexf(v) for v in c["w"]]], np.float32)
+        out.append((c["name"], y, idx, w, _hexf(c["out"][0])))
+    return out
+
+
+def planes_cases():
+    """(name, wtype, k, blocks uint8 [1, row bytes], planes uint8 [1, row bytes]) per case."""
+    out = []
+    for c in _cases("planes.txt"):
+        blk = np.array([int(b, 16) for b in c["blocks"]], np.uint8)[None, :]
+        pl = np.array([int(b, 16) for b in c["planes"]], np.uint8)[None, :]
+        out.append((c["name"], int(c["wtype"][0]), int(c["k"][0]), blk, pl))
+    return out

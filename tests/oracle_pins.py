@@ -410,9 +410,106 @@ def pin_prefill_entry_independence(orc):
     assert np.array_equal(part["H16"], full["H16"][pick])
 
 
+# ------------------------------------------------------------------ MoE combine
+
+def pin_moe_combine_golden(orc):
+    """Hand-worked cases: k order, the product rounded before the sum, +0, skipped rows."""
+    for name, y, idx, w, out in _golden.moe_combine_cases():
+        got = orc.moe_combine(y, idx, w)[0, 0]
+        assert got == out and np.signbit(got) == np.signbit(out), (name, float(got).hex(), out)
+
+
+def pin_moe_combine_properties(orc):
+    """Within the binary32 bound of the exact weighted sum (float64 brute force: every product
+    of two binary32 values is exact in float64); one row with weight 1 copies it; moving the
+    rows of y (and the indices with them) changes no bit; k order matters only by rounding."""
+    rng = np.random.default_rng(90)
+    nrows, hidden, ntok, topk = 64, 40, 12, 6
+    y = (rng.standard_normal((nrows, hidden)) * np.exp2(rng.integers(-8, 8, (nrows, 1)))).astype(np.float32)
+    idx = rng.integers(0, nrows, (ntok, topk)).astype(np.int32)
+    w = rng.random((ntok, topk)).astype(np.float32)
+    out = orc.moe_combine(y, idx, w).astype(np.float64)
+    terms = w.astype(np.float64)[:, :, None] * y.astype(np.float64)[idx]      # [ntok, topk, hidden]
+    exact = terms.sum(axis=1)
+    bound = 2 * topk * 2.0 ** -24 * np.abs(terms).sum(axis=1)
+    assert np.all(np.abs(out - exact) <= bound)
+    one = orc.moe_combine(y, idx[:, :1], np.ones((ntok, 1), np.float32))
+    assert np.array_equal(one, y[idx[:, 0]])
+    perm = rng.permutation(nrows)
+    inv = np.argsort(perm)
+    moved = orc.moe_combine(y[perm], inv[idx].astype(np.int32), w)
+    assert np.array_equal(moved.view(np.uint32), out.astype(np.float32).view(np.uint32))
+    rev = orc.moe_combine(y, idx[:, ::-1].copy(), w[:, ::-1].copy()).astype(np.float64)
+    assert np.all(np.abs(rev - exact) <= bound)
+
+
+# ------------------------------------------------------------------ dense prompt projections
+
+def np_dequant_f16(wtype, w, k):
+    """FP16 dequantization of Q8_0 / IQ4_NL rows with numpy alone: the exact product d * factor in
+    float64, rounded by numpy's binary16 conversion.  [nrows, k] float64 of the binary16 values."""
+    bb = 34 if wtype == Q8_0 else 18
+    blk = np.asarray(w, np.uint8).reshape(-1, k // 32, bb)
+    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    if wtype == Q8_0:
+        f = blk[:, :, 2:].view(np.int8).astype(np.float64)
+    else:
+        qs = blk[:, :, 2:].astype(np.int64)
+        f = KV_IQ4NL[np.concatenate([qs & 15, qs >> 4], axis=2)].astype(np.float64)
+    return (d[:, :, None] * f).astype(np.float16).astype(np.float64).reshape(blk.shape[0], k)
+
+
+def pin_dense_rows(orc):
+    """Y equals the float64 numpy matmul of numpy's FP16 dequantization with the tokens
+    (library routines), for Q8_0 and IQ4_NL and for weights given as binary16 already; one-hot
+    tokens give the weight columns exactly."""
+    rng = synth.rng_for(95)
+    nrows, k, ntok = 48, 192, 20
+    x16 = synth.prefill_tokens(rng, ntok, k)
+    samples = np.array([0, 3, 7, 19, 11], np.int64)
+    for wt in (Q8_0, IQ4_NL):
+        w = synth.weights(wt, rng, nrows, k, **(dict(qlo=-128) if wt == Q8_0 else {}))
+        W = np_dequant_f16(wt, w, k)
+        Y, A = orc.dense_rows(wt, w, nrows, k, x16, samples)
+        ref = x16.astype(np.float64)[samples] @ W.T
+        assert np.allclose(Y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+        assert np.allclose(A, np.abs(x16.astype(np.float64)[samples]) @ np.abs(W.T), rtol=1e-12)
+        Y16, _ = orc.dense_rows(0, W.astype(np.float16).view(np.uint16), nrows, k, x16, samples)
+        assert np.array_equal(Y16, Y)
+        eye = np.eye(k, dtype=np.float16)
+        Yi, _ = orc.dense_rows(wt, w, nrows, k, eye, np.arange(k, dtype=np.int64))
+        assert np.array_equal(Yi, W.T)
+
+
+# ------------------------------------------------------------------ weight planes
+
+def pin_planes_golden(orc):
+    for name, wt, k, blk, planes in _golden.planes_cases():
+        assert np.array_equal(orc.pack_planes(wt, blk, k), planes), name
+
+
+def pin_planes_layout(orc):
+    """Rows of 1, 16, 17 and 80 blocks: each tile of n blocks holds the n blocks' factor bytes
+    in order and then their n scales (numpy slicing of the blocks), rows keep their place."""
+    rng = synth.rng_for(96)
+    for wt in (Q8_0, IQ4_NL):
+        bb, fb = (34, 32) if wt == Q8_0 else (18, 16)
+        for nb in (1, 16, 17, 80):
+            w = synth.weights(wt, rng, 3, 32 * nb)
+            got = orc.pack_planes(wt, w, 32 * nb)
+            blk = w.reshape(3, nb, bb)
+            for t0 in range(0, nb, 16):
+                n = min(16, nb - t0)
+                tile = got[:, t0 * bb:(t0 + n) * bb]
+                assert np.array_equal(tile[:, :n * fb], blk[:, t0:t0 + n, 2:].reshape(3, n * fb))
+                assert np.array_equal(tile[:, n * fb:], blk[:, t0:t0 + n, 0:2].reshape(3, 2 * n))
+
+
 CHEAP_PINS = [pin_fp16_golden, pin_formats_golden, pin_q8_1_golden, pin_q8_1_ties,
               pin_silu, pin_dequant_ld, pin_block_sums, pin_gemv_bruteforce, pin_gemv_onehot,
               pin_cross_format, pin_q8_1_properties, pin_grouped,
-              pin_grouped_entry_independence, pin_prefill, pin_prefill_entry_independence]
+              pin_grouped_entry_independence, pin_prefill, pin_prefill_entry_independence,
+              pin_moe_combine_golden, pin_moe_combine_properties, pin_dense_rows, pin_planes_golden,
+              pin_planes_layout]
 EXPENSIVE_PINS = [pin_fp16_exhaustive, pin_dequant_f16_exhaustive]
 ALL_PINS = CHEAP_PINS + EXPENSIVE_PINS

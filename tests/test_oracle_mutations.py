@@ -48,6 +48,22 @@ MUTATIONS = {
     "prefill_down_transposed": ("ya += wd[j * inter + i] * hrow[i];", "ya += wd[i * hidden + j] * hrow[i];"),
     "prefill_h_not_rounded": ("hrow[i] = or_f16_to_f32(hb);",
                               "hrow[i] = or_silu_mul((float)ga, (float)ua);"),
+    "combine_fused_multiply_add": ("acc = acc + prod;", "acc = fmaf(w[t * topk + k], y[r * hidden + j], acc);"),
+    "combine_reverse_k_order": ("int32_t r = row_idx[t * topk + k];\n                if (r < 0",
+                                "int32_t r = row_idx[t * topk + (topk - 1 - k)];\n                if (r < 0"),
+    "combine_drops_last_k": ("for (int k = 0; k < topk; ++k) {\n                int32_t r",
+                             "for (int k = 0; k + 1 < topk; ++k) {\n                int32_t r"),
+    "combine_weight_of_other_k": ("float prod = w[t * topk + k] * y[r * hidden + j];",
+                                  "float prod = w[t * topk + (k + 1) % topk] * y[r * hidden + j];"),
+    "combine_keeps_bad_rows": ("if (r < 0 || r >= nrows) continue;", "if (r < 0 || r >= nrows) r = 0;"),
+    "dense_rows_transposed": ("or_f16_to_f32(w16[r * k + kk]) * (double)or_f16_to_f32(x16[t * k + kk])",
+                              "or_f16_to_f32(w16[kk * nrows + r]) * (double)or_f16_to_f32(x16[t * k + kk])"),
+    "dense_rows_unrounded": ("or_dequant_f16(wtype, (const uint8_t*)w, grid, nrows, k, w16, k);",
+                             "{ or_dequant_f16(wtype, (const uint8_t*)w, grid, nrows, k, w16, k); "
+                             "for (int64_t i = 0; i < nrows * k; ++i) w16[i] &= 0xFFFE; }"),
+    "planes_scales_first": ("memcpy(tile + i * fb, blk + 2, (size_t)fb);       /* factors */",
+                            "memcpy(tile + 2 * n + i * fb, blk + 2, (size_t)fb);       /* factors */"),
+    "planes_whole_row_tile": ("int64_t n = nb - b0 < 16 ? nb - b0 : 16;", "int64_t n = nb - b0 < 32 ? nb - b0 : 32;"),
     "prefill_wrong_token": ("const uint16_t* xr = x16 + (int64_t)t * hidden;",
                             "const uint16_t* xr = x16 + (int64_t)(p % ntok) * hidden;"),
 }
