@@ -10,7 +10,9 @@
  *
  * General rules for every entry point:
  *   - All pointers are DEVICE pointers unless a comment says "host".  The caller owns every
- *     buffer; the library allocates nothing and keeps no state between calls (reentrant).
+ *     buffer; the library allocates nothing and keeps no state between calls (reentrant),
+ *     except where an entry point says otherwise (qgemv_grouped_experts_noalloc's fixed device
+ *     array).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
  *     asynchronous on that stream; outputs are ready when the stream reaches the call.
  *   - Argument errors are reported synchronously by the return value, before anything is
@@ -175,6 +177,26 @@ int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up,
                           const int32_t* group_expert, const int32_t* group_entry_off, int ngroups,
                           const int32_t* entry_col, int nentries, float* y, void* ws,
                           size_t ws_bytes, unsigned flags, void* stream);
+
+/* Allocation-free grouped decode, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Computes exactly
+ * what qgemv_grouped_experts computes with flags = 0 (same kernels: y is bitwise the same), but
+ * keeps H in a fixed device array of the library instead of a caller workspace, and calls no
+ * allocating routine.  Limit: H of nentries * (inter/32) * 36 bytes must fit the array's
+ * qgemv_grouped_experts_noalloc_max_bytes() bytes (4 MiB: 3640 entries at inter 1024), else
+ * QMM_ESPACE.  Every call on a GPU uses that GPU's one array, so calls that overlap on one GPU
+ * (two streams, two threads) race; the array keeps the last call's H.  Each GPU the library runs
+ * on holds its own array until the process ends.  Arguments otherwise as qgemv_grouped_experts.
+ * Errors: as qgemv_grouped_experts; QMM_ESPACE (H beyond the array), QMM_EHIP (the array's
+ * device address could not be obtained). */
+size_t qgemv_grouped_experts_noalloc_max_bytes(void);
+int qgemv_grouped_experts_noalloc(int wtype_gu, const void* w_gate, const void* w_up,
+                                  int64_t gu_expert_stride, int wtype_down, const void* w_down,
+                                  int64_t down_expert_stride, int nexperts, const uint8_t* grid,
+                                  int64_t hidden, int64_t inter, const void* xq, int xq_cols,
+                                  const int32_t* group_expert, const int32_t* group_entry_off,
+                                  int ngroups, const int32_t* entry_col, int nentries, float* y,
+                                  void* stream);
 
 /* Workspace bytes qgemm_prefill_experts needs (host). */
 size_t qgemm_prefill_experts_workspace(int nexperts, int64_t inter, int64_t nentries,

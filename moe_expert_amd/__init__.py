@@ -43,6 +43,9 @@ SIGNATURES = {
     "qgemv_grouped_experts_workspace": (_SZ, [_I64, _I32, _U32]),
     "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
                                      _P, _P, _I32, _P, _I32, _P, _P, _SZ, _U32, _P]),
+    "qgemv_grouped_experts_noalloc_max_bytes": (_SZ, []),
+    "qgemv_grouped_experts_noalloc": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
+                                             _P, _P, _I32, _P, _I32, _P, _P]),
     "qgemm_prefill_experts_workspace": (_SZ, [_I32, _I64, _I64, _U32]),
     "qgemm_prefill_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _I64, _I64, _P, _I64,
                                      _P, _P, _I64, _P, _P, _SZ, _U32, _P]),
@@ -306,6 +309,38 @@ def qgemv_grouped_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, hidden, in
         hidden, inter, _ptr(xq), xq_cols, _ptr(group_expert), _ptr(group_entry_off), ngroups, _ptr(entry_col),
         nentries, _ptr(y), _ptr(ws), _nbytes(ws), flags, _stream(stream, dev)))
     return y, ws
+
+
+def qgemv_grouped_experts_noalloc(wtype_gu, w_gate, w_up, wtype_down, w_down, hidden, inter, xq, group_expert,
+                                  group_entry_off, entry_col, grid=None, y=None, stream=None):
+    """The grouped MoE decode without a workspace: H lives in the library's fixed device array
+    (qgemv_grouped_experts_noalloc_max_bytes() bytes per GPU; calls that overlap on one GPU race).
+    Arguments as qgemv_grouped_experts; returns y [nentries, hidden] float32."""
+    import torch
+    if getattr(w_gate, "dim", lambda: 0)() < 1:
+        raise ValueError("w_gate must be [nexperts, ...]")
+    dev = w_gate.device
+    nexperts = int(w_gate.shape[0])
+    gu_stride = _expert_weights(w_gate, "w_gate", nexperts, inter * _block_multiple(wtype_gu, hidden, "hidden"), dev)
+    if _expert_weights(w_up, "w_up", nexperts, gu_stride, dev) != gu_stride:
+        raise ValueError("w_up must have w_gate's shape")
+    d_stride = _expert_weights(w_down, "w_down", nexperts, hidden * _block_multiple(wtype_down, inter, "inter"), dev)
+    _grid_arg(wtype_gu if wtype_gu == QMM_CB3 else wtype_down, grid, dev)
+    col_bytes = (hidden // 32) * Q8_1_BYTES
+    _need(xq, "xq", "u8", col_bytes, dev)
+    if _nbytes(xq) % col_bytes:
+        raise ValueError("xq must hold whole q8_1 columns of width hidden")
+    ngroups = int(group_expert.numel())
+    nentries = int(entry_col.numel())
+    _need(group_expert, "group_expert", "i32", 0, dev)
+    _need(group_entry_off, "group_entry_off", "i32", (ngroups + 1) * 4, dev)
+    _need(entry_col, "entry_col", "i32", 0, dev)
+    y = _out(y, "y", "f32", nentries * hidden * 4, dev, (nentries, hidden), torch.float32)
+    _check("qgemv_grouped_experts_noalloc", lib().qgemv_grouped_experts_noalloc(
+        wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, nexperts, _ptr(grid),
+        hidden, inter, _ptr(xq), _nbytes(xq) // col_bytes, _ptr(group_expert), _ptr(group_entry_off), ngroups,
+        _ptr(entry_col), nentries, _ptr(y), _stream(stream, dev)))
+    return y
 
 
 def qgemm_prefill_experts_workspace(nexperts, inter, nentries, flags=0):

@@ -15,6 +15,8 @@
 // silu(z) = z / (1 + e^-z) in binary32 (expf within 1 ulp, IEEE division).
 #include "qmm_gemv.h"
 
+#include <mutex>
+
 namespace qmm {
 
 constexpr int kGroupPass = 8;  // entries per pass
@@ -347,6 +349,33 @@ static int launch_grouped(const GroupedArgs& a) {
     }
 }
 
+// ------------------------------------------------------------------ allocation-free variant
+//
+// For callers that cannot allocate (code under graph capture, serving loops): H lives in a
+// file-scope device array.  In host code `scratch` names a host-side stand-in, not the device
+// array, so host code never passes it to a kernel: the device address is taken once per device
+// with hipGetSymbolAddress (with that device current) and used from then on.  Every call on a
+// device shares its array; calls that overlap on one device race.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;  // H of 3640 entries at inter 1024
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (nullptr if it cannot be had).
+static void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace qmm
 
 using namespace qmm;
@@ -358,12 +387,12 @@ extern "C" size_t qgemv_grouped_experts_workspace(int64_t inter, int nentries, u
     return b;
 }
 
-extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up, int64_t gu_expert_stride,
-                                     int wtype_down, const void* w_down, int64_t down_expert_stride, int nexperts,
-                                     const uint8_t* grid, int64_t hidden, int64_t inter, const void* xq, int xq_cols,
-                                     const int32_t* group_expert, const int32_t* group_entry_off, int ngroups,
-                                     const int32_t* entry_col, int nentries, float* y, void* ws, size_t ws_bytes,
-                                     unsigned flags, void* stream) {
+// Argument checks shared by both entry points (everything but the workspace), then the call.
+static int grouped_call(int wtype_gu, const void* w_gate, const void* w_up, int64_t gu_expert_stride, int wtype_down,
+                        const void* w_down, int64_t down_expert_stride, int nexperts, const uint8_t* grid, int64_t hidden,
+                        int64_t inter, const void* xq, int xq_cols, const int32_t* group_expert,
+                        const int32_t* group_entry_off, int ngroups, const int32_t* entry_col, int nentries, float* y,
+                        void* ws, size_t ws_bytes, unsigned flags, void* stream) {
     if (!valid_wtype(wtype_gu) || !valid_wtype(wtype_down)) return QMM_EINVAL;
     if (!w_gate || !w_up || !w_down || !xq || !group_expert || !group_entry_off || !entry_col || !y || !ws)
         return QMM_EINVAL;
@@ -410,4 +439,33 @@ extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const voi
     a.flags = flags;
     a.st = as_stream(stream);
     return launch_grouped(a);
+}
+
+extern "C" int qgemv_grouped_experts(int wtype_gu, const void* w_gate, const void* w_up, int64_t gu_expert_stride,
+                                     int wtype_down, const void* w_down, int64_t down_expert_stride, int nexperts,
+                                     const uint8_t* grid, int64_t hidden, int64_t inter, const void* xq, int xq_cols,
+                                     const int32_t* group_expert, const int32_t* group_entry_off, int ngroups,
+                                     const int32_t* entry_col, int nentries, float* y, void* ws, size_t ws_bytes,
+                                     unsigned flags, void* stream) {
+    return grouped_call(wtype_gu, w_gate, w_up, gu_expert_stride, wtype_down, w_down, down_expert_stride, nexperts,
+                        grid, hidden, inter, xq, xq_cols, group_expert, group_entry_off, ngroups, entry_col, nentries,
+                        y, ws, ws_bytes, flags, stream);
+}
+
+extern "C" size_t qgemv_grouped_experts_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int qgemv_grouped_experts_noalloc(int wtype_gu, const void* w_gate, const void* w_up,
+                                             int64_t gu_expert_stride, int wtype_down, const void* w_down,
+                                             int64_t down_expert_stride, int nexperts, const uint8_t* grid,
+                                             int64_t hidden, int64_t inter, const void* xq, int xq_cols,
+                                             const int32_t* group_expert, const int32_t* group_entry_off,
+                                             int ngroups, const int32_t* entry_col, int nentries, float* y,
+                                             void* stream) {
+    if (inter < 32 || nentries < 0) return QMM_EINVAL;
+    if (qgemv_grouped_experts_workspace(inter, nentries, 0) > kNoAllocScratchBytes) return QMM_ESPACE;
+    void* ws = scratch_ptr();
+    if (!ws) return QMM_EHIP;
+    return grouped_call(wtype_gu, w_gate, w_up, gu_expert_stride, wtype_down, w_down, down_expert_stride, nexperts,
+                        grid, hidden, inter, xq, xq_cols, group_expert, group_entry_off, ngroups, entry_col, nentries,
+                        y, ws, kNoAllocScratchBytes, 0u, stream);
 }
