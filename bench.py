@@ -31,6 +31,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -552,6 +554,152 @@ def bench_prefill(args, torch, M, cpu_s=10.0):
     return out
 
 
+# ------------------------------------------------------------------ the next rows: combine, dense projections, planes
+
+def combine_bytes(ntok, topk, hidden):
+    """Algorithmic bytes of one combine: every routed row read once, the indices and weights, the
+    output written once."""
+    return ntok * topk * hidden * 4 + ntok * topk * 8 + ntok * hidden * 4
+
+
+def bench_combine(args, torch, M, cpu_s=3.0):
+    """MoE combine on the prefill workload (8192 tokens, top-8 of 128, hidden 2560: the sorted
+    entry rows are 671 MB, over twice the memory-side cache, so every call reads them from HBM)
+    and on the decode shape (8 tokens x 16 experts)."""
+    import oracle
+    import synth
+    dev = torch.device("cuda", 0)
+    rng = synth.rng_for(synth.SEEDS["prefill"] + 10)
+    res = {}
+    for name, ntok, topk, nrows in (("prefill_8192tok_top8", 8192, 8, None), ("decode_8tok_top16", 8, 16, 128)):
+        hidden = 2560
+        if nrows is None:
+            st, _ = synth.prefill_routing(rng, ntok, 128, topk)
+            idx = synth.token_positions(st, ntok, topk)
+            nrows = st.size
+        else:
+            idx = (np.arange(topk)[None, :] * ntok + np.arange(ntok)[:, None]).astype(np.int32)
+        y = torch.randn((nrows, hidden), dtype=torch.float32, device=dev)
+        w = synth.router_weights(rng, ntok, topk)
+        di, dw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+        out = torch.empty((ntok, hidden), dtype=torch.float32, device=dev)
+        reps = 10 if ntok > 64 else 200
+        ms = timed_graph(torch, lambda: M.qmm_moe_combine(y, di, dw, out=out), reps, not args.no_graph)
+        b = combine_bytes(ntok, topk, hidden)
+        gbps = b / (ms * 1e-3) / 1e9
+        r = {"us_per_call": round(ms * 1e3, 3), "gbps": round(gbps, 1),
+             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": b,
+                          "kernel": "combine_kernel"},
+             "workload": f"{ntok} tokens x top-{topk}, hidden {hidden}, {nrows} rows of y ({nrows * hidden * 4 / 1e6:.0f} MB)"}
+        if not args.no_cpu:
+            yh = y.cpu().numpy()
+            rate, reps_c, dt = cpu_rate(lambda: oracle.moe_combine(yh, idx, w), b, cpu_s)
+            r["cpu_baseline"] = {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                                 "kind": "oracle", "sample": f"the same call x {reps_c}, {dt:.1f} s"}
+        res[name] = r
+        del y
+    return res
+
+
+def bench_dense(args, torch, M, cpu_s=3.0):
+    """Dense prompt projections: 8192 prompt tokens through the decode workloads' matrices
+    (IQ4_NL 8192 x 2560 and Q8_0 12288 x 2560), fused (weights converted to FP16 inside the
+    GEMM) and in two steps (qmm_dequant_f16 with 16-byte stores, then the GEMM on FP16 weights)."""
+    import oracle
+    import synth
+    dev = torch.device("cuda", 0)
+    ntok, k = 8192, 2560
+    x16 = synth.prefill_tokens(synth.rng_for(synth.SEEDS["prefill"] + 20), ntok, k)
+    xd = torch.from_numpy(x16.view(np.uint16)).to(dev)
+    res = {}
+    for wt, nrows, key in ((synth.IQ4_NL, 8192, "iq4nl_8192x2560"), (synth.Q8_0, 12288, "q8_0_12288x2560")):
+        w = synth.weights(wt, synth.rng_for(synth.SEEDS[key]), nrows, k)
+        wd = torch.from_numpy(w).to(dev)
+        w16 = torch.empty((nrows, k), dtype=torch.float16, device=dev)
+        y = torch.empty((ntok, nrows), dtype=torch.float32, device=dev)
+        g = not args.no_graph
+        fused = timed_graph(torch, lambda: M.qgemm_dense(wt, wd, nrows, k, xd, y=y), 10, g)
+        deq = timed_graph(torch, lambda: M.qmm_dequant_f16(wt, wd, nrows, k, out=w16), 50, g)
+        f16 = timed_graph(torch, lambda: M.qgemm_dense(M.QMM_F16, w16, nrows, k, xd, y=y), 10, g)
+        flops = 2.0 * ntok * nrows * k
+        tf = flops / (fused * 1e-3) / 1e12
+        deq_bytes = nrows * synth.row_bytes(wt, k) + nrows * k * 2
+        name = f"{'iq4_nl' if wt == synth.IQ4_NL else 'q8_0'}_{nrows}x{k}_8192tok"
+        r = {"us_per_call": round(fused * 1e3, 2), "tflops": round(tf, 1),
+             "two_step": {"dequant_us": round(deq * 1e3, 2), "dequant_gbps": round(deq_bytes / (deq * 1e-3) / 1e9, 1),
+                          "f16_gemm_us": round(f16 * 1e3, 2),
+                          "f16_gemm_tflops": round(flops / (f16 * 1e-3) / 1e12, 1),
+                          "total_us": round((deq + f16) * 1e3, 2)},
+             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                          "kernel": "dense_kernel (weights converted to FP16 in registers, fp16 MFMA 32x32x16)"},
+             "workload": f"8192 tokens x {nrows}x{k} {'IQ4_NL' if wt == synth.IQ4_NL else 'Q8_0'}"}
+        if not args.no_cpu:
+            rows = np.arange(8, dtype=np.int64)
+            rate, reps_c, dt = cpu_rate(lambda: oracle.dense_rows(wt, w, nrows, k, x16, rows),
+                                        2.0 * 8 * nrows * k, cpu_s)
+            r["cpu_baseline"] = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                                 "kind": "oracle", "sample": f"8 tokens (weights dequantized too) x {reps_c}, {dt:.1f} s"}
+        res[name] = r
+        del wd, w16, y
+    return res
+
+
+def bench_planes(args, torch, M):
+    """The decode GEMVs on weight planes against the same GEMVs on the GGUF blocks, each over a
+    cold rotation of copies, in the same run; plus the time of one repack."""
+    import synth
+    dev = torch.device("cuda", 0)
+    res = {}
+    g = not args.no_graph
+    for wt, nrows, k, cols, key in ((synth.IQ4_NL, 8192, 2560, (1, 4, 8), "iq4nl_8192x2560"),
+                                    (synth.Q8_0, 12288, 2560, (1, 2, 4), "q8_0_12288x2560"),
+                                    (synth.Q8_0, 2560, 6144, (7, 8), "q8_0_2560x6144")):
+        wbytes = nrows * synth.row_bytes(wt, k)
+        host_w = [synth.weights(wt, synth.rng_for(synth.SEEDS[key] + i), nrows, k) for i in range(6)]
+        nc = cold_copies(wbytes)
+        blocks = [torch.from_numpy(host_w[i % 6]).to(dev) for i in range(nc)]
+        planes = [M.qmm_pack_planes(wt, b, nrows, k) for b in blocks]
+        pack_ms = timed_graph(torch, lambda: M.qmm_pack_planes(wt, blocks[0], nrows, k, out=planes[0]), 5, g)
+        xq = M.qmm_quantize_q8_1(torch.from_numpy(synth.activations(synth.rng_for(7), max(cols), k)).to(dev))
+        y = torch.empty((max(cols), nrows), dtype=torch.float32, device=dev)
+        r = {"planes_us_per_call": {}, "blocks_us_per_call": {}, "planes_gbps": {},
+             "pack_us": round(pack_ms * 1e3, 2), "weight_copies": nc}
+        tot_b = tot_t = 0.0
+        for n in cols:
+            xn = xq[:n].contiguous()
+            tp = timed_graph(torch, lambda: [M.qgemv_planes(wt, p, nrows, k, xn, n, y=y) for p in planes],
+                             args.batch_reps, g) * 1e3 / nc
+            tb = timed_graph(torch, lambda: [M.qgemv_dense(wt, b, nrows, k, xn, n, y=y) for b in blocks],
+                             args.batch_reps, g) * 1e3 / nc
+            b = gemv_bytes(wt, nrows, k, n)
+            r["planes_us_per_call"][str(n)] = round(tp, 3)
+            r["blocks_us_per_call"][str(n)] = round(tb, 3)
+            r["planes_gbps"][str(n)] = round(b / (tp * 1e-6) / 1e9, 1)
+            tot_b += b
+            tot_t += tp
+        ach = tot_b / (tot_t * 1e-6) / 1e9
+        r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": f"gemv_kernel on planes, columns {list(cols)}"}
+        res[f"{'iq4_nl' if wt == synth.IQ4_NL else 'q8_0'}_{nrows}x{k}"] = r
+        del blocks, planes
+        torch.cuda.empty_cache()
+    return res
+
+
+def next_rows(args, torch, M):
+    """The rows after the contract's workloads: MoE combine, dense prompt projections, planes."""
+    out = {}
+    for name, fn in (("moe_combine", bench_combine), ("dense_prompt_projection", bench_dense),
+                     ("weight_planes_gemv", bench_planes)):
+        t0 = time.perf_counter()
+        out[name] = fn(args, torch, M)
+        torch.cuda.empty_cache()
+        progress(f"{name} done ({time.perf_counter() - t0:.0f} s)")
+    return out
+
+
 # ------------------------------------------------------------------ HBM traffic counters
 #
 # The traffic figure comes from two rocprofv3 counter runs of `--pmc-probe` (FETCH_SIZE, then
@@ -755,7 +903,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill"],
+    ap.add_argument("--workload", default="all", choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill", "next"],
                     help="all (default): the headline GEMV line with every other workload under 'configs'")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -792,6 +940,7 @@ def main() -> int:
         progress(f"headline IQ4_NL 8192x2560 GEMV done ({time.perf_counter() - t0:.0f} s)")
         if args.workload == "all":
             out["configs"] = other_configs(args, torch, M)
+            out["next"] = next_rows(args, torch, M)
         print(json.dumps(out), flush=True)
     elif args.workload == "tiny":
         print(json.dumps(bench_gemv(args, torch, M, *TINY_SPEC)), flush=True)
@@ -800,6 +949,8 @@ def main() -> int:
             print(json.dumps(bench_gemv(args, torch, M, *spec)), flush=True)
     elif args.workload == "grouped":
         print(json.dumps(bench_grouped(args, torch, M)), flush=True)
+    elif args.workload == "next":
+        print(json.dumps(next_rows(args, torch, M)), flush=True)
     else:
         print(json.dumps(bench_prefill(args, torch, M)), flush=True)
     return 0

@@ -11,8 +11,8 @@
  * General rules for every entry point:
  *   - All pointers are DEVICE pointers unless a comment says "host".  The caller owns every
  *     buffer; the library allocates nothing and keeps no state between calls (reentrant),
- *     except where an entry point says otherwise (qgemv_grouped_experts_noalloc's fixed device
- *     array).
+ *     except where an entry point says otherwise (qmm_planes_alloc owns a packed copy until
+ *     qmm_planes_release).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
  *     asynchronous on that stream; outputs are ready when the stream reaches the call.
  *   - Argument errors are reported synchronously by the return value, before anything is
@@ -47,6 +47,7 @@ extern "C" {
 #define QMM_Q8_0 1
 #define QMM_IQ4_NL 2
 #define QMM_CB3 3
+#define QMM_F16 4 /* binary16 weights [rows][k] (qgemm_dense only): 2 bytes per value */
 
 /* status codes */
 #define QMM_OK 0
@@ -66,7 +67,7 @@ int qmm_version(void);
 const char* qmm_status_str(int status);
 
 /* Host-only.  Bytes of one weight row of k values, or 0 when k is not a positive multiple of
- * the format's block (32 values; 256 for CB3) or wtype is unknown. */
+ * the format's block (32 values; 256 for CB3; 1 for QMM_F16) or wtype is unknown. */
 int64_t qmm_row_bytes(int wtype, int64_t k);
 
 /* q8_1 quantization of activations [DQ, Change: the q8_1 quantizer's 32-value blocks; GP, What
@@ -230,6 +231,65 @@ int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const void* w_up,
                           const uint16_t* x_f16, int64_t ntok, const int32_t* sorted_tok,
                           const int32_t* expert_off, int64_t nentries, float* y, void* ws,
                           size_t ws_bytes, unsigned flags, void* stream);
+
+/* Dense prompt projection [DQ, Change: dense Q8_0 / IQ4_XS weights dequantized to FP16 with
+ * 16-byte stores for a matrix product over the prompt's tokens; PF, Summary: the FP16 weights the
+ * matrix cores get, FP32 sums]:
+ *   y[t*ldy + r] = sum over k of W16[r][k] * X16[t][k]      (FP16 products, FP32 sums)
+ * with W16 the qmm_dequant_f16 values of w (wtype Q8_0 or IQ4_NL: converted in registers inside
+ * the GEMM, bitwise those values) or w itself (wtype QMM_F16: binary16 [nrows][k], e.g. the
+ * output of qmm_dequant_f16).  fp16 MFMA (32x32x16) with FP32 accumulation.
+ *   w     : nrows x qmm_row_bytes(wtype, k) bytes (QMM_F16: 2k bytes per row, 16-byte aligned;
+ *           the others 4-byte aligned).   x_f16: binary16 [ntok][k], 16-byte aligned.
+ *   y     : float [ntok][ldy], ldy >= nrows, 4-byte aligned.
+ *   k     : a multiple of 64, at most 32768.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (k not a multiple of 64, buffers of 4 GiB or
+ *         more). */
+int qgemm_dense(int wtype, const void* w, int64_t nrows, int64_t k, const uint16_t* x_f16,
+                int64_t ntok, float* y, int64_t ldy, void* stream);
+
+/* Weight planes [GP, What changed: a device-side repack of the GGUF blocks into planes (an int8
+ * plane plus scales) for the decode GEMV, the packed copy owned through pack / release calls].
+ * Layout (Q8_0 and IQ4_NL): each row is cut into tiles of 16 consecutive blocks (the last tile
+ * of a row holds the blocks left); a tile is its n blocks' factor bytes back to back in block
+ * order (Q8_0: 32 int8; IQ4_NL: 16 index bytes), then their n fp16 scales in block order.  A row
+ * keeps its size and place, so the planes of a matrix take exactly its blocks' bytes and every
+ * factor run of a lane starts 16-byte aligned.
+ *
+ * qmm_pack_planes: writes the planes of the nrows x k matrix w into `planes` (caller-owned,
+ *   nrows * qmm_row_bytes(wtype, k) bytes, must not overlap w).  Byte copies only.
+ * qmm_planes_alloc: allocates the planes buffer (hipMalloc; the one allocating entry point of the
+ *   library), packs w into it on `stream` and returns it in *planes; the caller owns it until
+ *   qmm_planes_release (hipFree; synchronizes the device).  *planes is NULL on error.
+ * qgemv_planes: qgemv_dense on a planes buffer: the same kernels with the realignment of each
+ *   block left out, so y is bitwise qgemv_dense's on the original blocks.  planes 16-byte
+ *   aligned, k a multiple of 512 (rows of whole tiles); other arguments as qgemv_dense.
+ * Errors: QMM_EINVAL (format other than Q8_0 / IQ4_NL, null, sizes), QMM_EALIGN,
+ *         QMM_EUNSUPPORTED (qgemv_planes: k not a multiple of 512, or as qgemv_dense),
+ *         QMM_EHIP (allocation or launch). */
+int qmm_pack_planes(int wtype, const void* w, int64_t nrows, int64_t k, void* planes, void* stream);
+int qmm_planes_alloc(int wtype, const void* w, int64_t nrows, int64_t k, void** planes, void* stream);
+int qmm_planes_release(void* planes);
+int qgemv_planes(int wtype, const void* planes, int64_t nrows, int64_t k, const void* xq, int ncols,
+                 float* y, int64_t ldy, void* stream);
+
+/* MoE combine [DQ, Change: the combine sums a token's expert rows with one fixed
+ * thread-to-element mapping and k order; profile block: moe_combine4 reads them at bandwidth].
+ *   out[t*ldo + j] = sum over k = 0 .. topk-1 of  weights[t*topk + k] * y[r*hidden + j],
+ *                    r = row_idx[t*topk + k]
+ * in binary32, from +0, adding in k order, each product and each sum rounded once (no fused
+ * multiply-add); an index outside [0, nrows) adds nothing.  Decode: y is a grouped call's
+ * [nentries][hidden] output and row_idx the entries of each token; prefill: y is the sorted-
+ * entry output and row_idx each token's positions in the sorted order.
+ *   y       : float [nrows][hidden], 16-byte aligned.   out: float [ntok][ldo], 16-byte aligned.
+ *   row_idx : int32 [ntok][topk];  weights: float [ntok][topk] (both 4-byte aligned).
+ *   hidden, ldo: multiples of 4, ldo >= hidden (columns hidden..ldo-1 are not written).
+ *   topk    : 1 .. 64.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (hidden or ldo not a multiple of 4, topk
+ *         above 64, sizes of 2^31 or more). */
+int qmm_moe_combine(const float* y, int64_t nrows, int64_t hidden, const int32_t* row_idx,
+                    const float* weights, int64_t ntok, int topk, float* out, int64_t ldo,
+                    void* stream);
 
 #ifdef __cplusplus
 }

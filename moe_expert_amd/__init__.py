@@ -21,10 +21,10 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmm.so")
 
-QMM_Q8_0, QMM_IQ4_NL, QMM_CB3 = 1, 2, 3
+QMM_Q8_0, QMM_IQ4_NL, QMM_CB3, QMM_F16 = 1, 2, 3, 4
 QMM_FLAG_DEBUG_INTERMEDIATES = 1
-BLOCK_VALUES = {QMM_Q8_0: 32, QMM_IQ4_NL: 32, QMM_CB3: 256}
-BLOCK_BYTES = {QMM_Q8_0: 34, QMM_IQ4_NL: 18, QMM_CB3: 110}
+BLOCK_VALUES = {QMM_Q8_0: 32, QMM_IQ4_NL: 32, QMM_CB3: 256, QMM_F16: 1}
+BLOCK_BYTES = {QMM_Q8_0: 34, QMM_IQ4_NL: 18, QMM_CB3: 110, QMM_F16: 2}
 Q8_1_BYTES = 36
 GRID_BYTES = 2048
 
@@ -46,6 +46,12 @@ SIGNATURES = {
     "qgemv_grouped_experts_noalloc_max_bytes": (_SZ, []),
     "qgemv_grouped_experts_noalloc": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
                                              _P, _P, _I32, _P, _I32, _P, _P]),
+    "qmm_moe_combine": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _I64, _P]),
+    "qmm_pack_planes": (_I32, [_I32, _P, _I64, _I64, _P, _P]),
+    "qmm_planes_alloc": (_I32, [_I32, _P, _I64, _I64, C.POINTER(C.c_void_p), _P]),
+    "qmm_planes_release": (_I32, [_P]),
+    "qgemv_planes": (_I32, [_I32, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
+    "qgemm_dense": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "qgemm_prefill_experts_workspace": (_SZ, [_I32, _I64, _I64, _U32]),
     "qgemm_prefill_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _I64, _I64, _P, _I64,
                                      _P, _P, _I64, _P, _P, _SZ, _U32, _P]),
@@ -188,15 +194,16 @@ def qmm_dequant_f16(wtype, w, nrows, k, grid=None, out=None, ld=None, stream=Non
     return out
 
 
-def _gemv_common(wtype, w, nrows, k, ncols, grid, ldy):
+def _gemv_common(wtype, w, nrows, k, ncols, grid, ldy, check_w=True):
     rb = _block_multiple(wtype, k)
     if nrows < 1 or ncols < 1:
         raise ValueError("nrows and ncols must be positive")
     ldy = nrows if ldy is None else ldy
     if ldy < nrows:
         raise ValueError("ldy < nrows")
-    _need(w, "w", "u8", nrows * rb)
-    _grid_arg(wtype, grid, w.device)
+    if check_w:
+        _need(w, "w", "u8", nrows * rb)
+        _grid_arg(wtype, grid, w.device)
     return ldy
 
 
@@ -373,3 +380,103 @@ def qgemm_prefill_experts(wtype_gu, w_gate, w_up, wtype_down, w_down, nexperts, 
         _ptr(x_f16), ntok, _ptr(sorted_tok), _ptr(expert_off), nentries, _ptr(y), _ptr(ws), _nbytes(ws), flags,
         _stream(stream, dev)))
     return y, ws
+
+
+def qmm_moe_combine(y, row_idx, weights, out=None, ldo=None, stream=None):
+    """Router-weighted sum of each token's expert rows in k order: y float32 [nrows, hidden],
+    row_idx int32 [ntok, topk], weights float32 [ntok, topk] -> out float32 [ntok, ldo]."""
+    import torch
+    if getattr(y, "dim", lambda: 0)() != 2 or getattr(row_idx, "dim", lambda: 0)() != 2:
+        raise ValueError("y must be [nrows, hidden] and row_idx [ntok, topk]")
+    nrows, hidden = int(y.shape[0]), int(y.shape[1])
+    ntok, topk = int(row_idx.shape[0]), int(row_idx.shape[1])
+    dev = y.device
+    _need(y, "y", "f32", nrows * hidden * 4, dev)
+    _need(row_idx, "row_idx", "i32", ntok * topk * 4, dev)
+    _need(weights, "weights", "f32", ntok * topk * 4, dev)
+    ldo = hidden if ldo is None else ldo
+    if ldo < hidden:
+        raise ValueError("ldo < hidden")
+    out = _out(out, "out", "f32", (max(ntok, 1) - 1) * ldo * 4 + hidden * 4, dev, (ntok, ldo), torch.float32)
+    _check("qmm_moe_combine", lib().qmm_moe_combine(_ptr(y), nrows, hidden, _ptr(row_idx), _ptr(weights), ntok, topk,
+                                                   _ptr(out), ldo, _stream(stream, dev)))
+    return out
+
+
+def qmm_pack_planes(wtype, w, nrows, k, out=None, stream=None):
+    """Q8_0 / IQ4_NL rows repacked into planes (16-block tiles: factor bytes, then scales) in a
+    caller-owned uint8 buffer of the blocks' size; returns it."""
+    import torch
+    if wtype not in (QMM_Q8_0, QMM_IQ4_NL):
+        raise ValueError("planes are Q8_0 or IQ4_NL")
+    rb = _block_multiple(wtype, k)
+    _need(w, "w", "u8", nrows * rb)
+    out = _out(out, "out", "u8", nrows * rb, w.device, (nrows, rb), torch.uint8)
+    _check("qmm_pack_planes", lib().qmm_pack_planes(wtype, _ptr(w), nrows, k, _ptr(out), _stream(stream, w.device)))
+    return out
+
+
+class Planes:
+    """A packed copy owned by the library's allocation (qmm_planes_alloc), freed by release()
+    (qmm_planes_release) or when the object is collected."""
+
+    def __init__(self, wtype, w, nrows, k, stream=None):
+        if wtype not in (QMM_Q8_0, QMM_IQ4_NL):
+            raise ValueError("planes are Q8_0 or IQ4_NL")
+        rb = _block_multiple(wtype, k)
+        _need(w, "w", "u8", nrows * rb)
+        self.wtype, self.nrows, self.k, self.device, self.nbytes = wtype, nrows, k, w.device, nrows * rb
+        self.ptr = C.c_void_p()
+        _check("qmm_planes_alloc", lib().qmm_planes_alloc(wtype, _ptr(w), nrows, k, C.byref(self.ptr),
+                                                          _stream(stream, w.device)))
+
+    def release(self):
+        if self.ptr:
+            _check("qmm_planes_release", lib().qmm_planes_release(self.ptr))
+            self.ptr = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+def qgemv_planes(wtype, planes, nrows, k, xq, ncols, y=None, ldy=None, stream=None):
+    """qgemv_dense on planes (a uint8 tensor from qmm_pack_planes, or a Planes object): y
+    float32 [ncols, ldy], bitwise qgemv_dense on the original blocks."""
+    import torch
+    if isinstance(planes, Planes):
+        if (planes.wtype, planes.nrows, planes.k) != (wtype, nrows, k) or not planes.ptr:
+            raise ValueError("the packed copy holds another matrix (or was released)")
+        dev, ptr = planes.device, planes.ptr
+        ldy = _gemv_common(wtype, None, nrows, k, ncols, None, ldy, check_w=False)
+    else:
+        ldy = _gemv_common(wtype, planes, nrows, k, ncols, None, ldy)
+        dev, ptr = planes.device, _ptr(planes)
+    _need(xq, "xq", "u8", ncols * (k // 32) * Q8_1_BYTES, dev)
+    y = _out(y, "y", "f32", ((ncols - 1) * ldy + nrows) * 4, dev, (ncols, ldy), torch.float32)
+    _check("qgemv_planes", lib().qgemv_planes(wtype, ptr, nrows, k, _ptr(xq), ncols, _ptr(y), ldy,
+                                             _stream(stream, dev)))
+    return y
+
+
+def qgemm_dense(wtype, w, nrows, k, x_f16, y=None, ldy=None, stream=None):
+    """Dense prompt projection y [ntok, ldy] float32 = X16 . W16^T: w Q8_0 / IQ4_NL blocks
+    (converted to FP16 in the GEMM) or binary16 [nrows, k] (QMM_F16); x_f16 [ntok, k]."""
+    import torch
+    if wtype not in (QMM_Q8_0, QMM_IQ4_NL, QMM_F16):
+        raise ValueError("dense projections take Q8_0, IQ4_NL or F16 weights")
+    rb = _block_multiple(wtype, k)
+    if getattr(x_f16, "dim", lambda: 0)() != 2 or x_f16.shape[1] != k:
+        raise ValueError("x_f16 must be [ntok, k]")
+    ntok = int(x_f16.shape[0])
+    ldy = nrows if ldy is None else ldy
+    if nrows < 1 or ldy < nrows:
+        raise ValueError("nrows >= 1 and ldy >= nrows")
+    _need(w, "w", "f16" if wtype == QMM_F16 else "u8", nrows * rb)
+    _need(x_f16, "x_f16", "f16", ntok * k * 2, w.device)
+    y = _out(y, "y", "f32", (max(ntok, 1) - 1) * ldy * 4 + nrows * 4, w.device, (ntok, ldy), torch.float32)
+    _check("qgemm_dense", lib().qgemm_dense(wtype, _ptr(w), nrows, k, _ptr(x_f16), ntok, _ptr(y), ldy,
+                                           _stream(stream, w.device)))
+    return y

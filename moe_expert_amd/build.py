@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmm.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["qmm_api.hip", "qmm_quant.hip", "qmm_gemv.hip", "qmm_grouped.hip", "qmm_prefill.hip", "qmm_probe.hip"]
+SOURCES = ["qmm_api.hip", "qmm_quant.hip", "qmm_gemv.hip", "qmm_grouped.hip", "qmm_prefill.hip", "qmm_probe.hip",
+           "qmm_combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -21,6 +21,7 @@ extern "C" int64_t qmm_row_bytes(int wtype, int64_t k) {
         case QMM_Q8_0: return k % 32 ? 0 : (k / 32) * 34;
         case QMM_IQ4_NL: return k % 32 ? 0 : (k / 32) * 18;
         case QMM_CB3: return k % 256 ? 0 : (k / 256) * 110;
+        case QMM_F16: return 2 * k;
         default: return 0;
     }
 }

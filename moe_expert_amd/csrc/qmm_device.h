@@ -16,7 +16,11 @@
 
 namespace qmm {
 
-enum : int { kQ8_0 = 1, kIQ4_NL = 2, kCB3 = 3 };
+// Q8_0P, IQ4_NLP: the same blocks repacked into planes (tiles of 16 blocks: their factor bytes,
+// then their scales; see Unit<kQ8_0P>).
+// F16: binary16 weights [rows][k] (the FP16 dequantization's output), read by the prefill-style
+// MFMA GEMM as they are.
+enum : int { kQ8_0 = 1, kIQ4_NL = 2, kCB3 = 3, kQ8_0P = 4, kIQ4_NLP = 5, kF16 = 6 };
 
 // ------------------------------------------------------------------ buffer loads
 
@@ -244,6 +248,68 @@ struct Unit<kIQ4_NL> {
         dw = realign_scale(raw[0], f.hi);
 #pragma unroll
         for (int i = 0; i < 4; ++i) iq4nl_decode_word(perm(raw[i + 1], raw[i], sel), W[i], W[i + 4], k);
+        mult = 1;
+    }
+};
+
+// Planes [GP, What changed: GGUF blocks repacked into an int8 plane plus scales]: a row of
+// Q8_0 / IQ4_NL blocks is cut into tiles of 16 blocks, each the 16 blocks' factor bytes back to
+// back (32 or 16 per block) followed by their 16 fp16 scales, so a tile takes the bytes of its 16
+// blocks and a row keeps its size.  The kernels take rows of whole tiles (k a multiple of 512).
+// The lanes of a row take blocks l, l + L, ... with L a multiple of 16, so lane l always sits at
+// position p = l mod 16 of its tiles: its factor bytes start 16-byte aligned at the tile start
+// plus FB p, its scale at the tile start plus 16 FB + 2 p.  The frame holds both addresses of
+// the lane's first block (computed from the block-layout offset the row engine passes, tile
+// start + BYTES p); block j of the lane lies j times the lane stride (whole tiles) further.
+struct PlaneFrame {
+    uint32_t q, d;
+};
+
+template <>
+struct Unit<kQ8_0P> {
+    using Consts = NoConsts;
+    static constexpr int RAW = 9;
+    static constexpr int BYTES = 34;
+    using Frame = PlaneFrame;
+    __device__ static __forceinline__ Frame frame(uint32_t off, int l) {
+        const uint32_t p = (uint32_t)l & 15u;
+        return {off - 2u * p, off + 512u - 32u * p};
+    }
+    __device__ static __forceinline__ void load(rsrc_t r, const Frame& f, uint32_t jb, uint32_t* raw) {
+        const u32x4 x = ld128(r, f.q + jb), y = ld128(r, f.q + jb + 16);
+        raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
+        raw[4] = y.x; raw[5] = y.y; raw[6] = y.z; raw[7] = y.w;
+        raw[8] = ld16(r, f.d + jb);
+    }
+    __device__ static __forceinline__ void decode(const uint32_t* raw, const Frame&, uint32_t* W, uint32_t& dw, int& mult,
+                                                  const NoConsts&) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) W[i] = raw[i];
+        dw = raw[8];
+        mult = 1;
+    }
+};
+
+template <>
+struct Unit<kIQ4_NLP> {
+    using Consts = IQ4Levels;
+    static constexpr int RAW = 5;
+    static constexpr int BYTES = 18;
+    using Frame = PlaneFrame;
+    __device__ static __forceinline__ Frame frame(uint32_t off, int l) {
+        const uint32_t p = (uint32_t)l & 15u;
+        return {off - 2u * p, off + 256u - 16u * p};
+    }
+    __device__ static __forceinline__ void load(rsrc_t r, const Frame& f, uint32_t jb, uint32_t* raw) {
+        const u32x4 x = ld128(r, f.q + jb);
+        raw[0] = x.x; raw[1] = x.y; raw[2] = x.z; raw[3] = x.w;
+        raw[4] = ld16(r, f.d + jb);
+    }
+    __device__ static __forceinline__ void decode(const uint32_t* raw, const Frame&, uint32_t* W, uint32_t& dw, int& mult,
+                                                  const IQ4Levels& k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) iq4nl_decode_word(raw[i], W[i], W[i + 4], k);
+        dw = raw[4];
         mult = 1;
     }
 };

@@ -18,7 +18,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int WT>
 __host__ __device__ constexpr int row_bytes_dev(int K) {
-    return WT == kQ8_0 ? (K / 32) * 34 : WT == kIQ4_NL ? (K / 32) * 18 : (K / 256) * kCB3Bytes;
+    return (WT == kQ8_0 || WT == kQ8_0P)     ? (K / 32) * 34
+           : (WT == kIQ4_NL || WT == kIQ4_NLP) ? (K / 32) * 18
+           : WT == kF16                        ? K * 2
+                                               : (K / 256) * kCB3Bytes;
 }
 
 // ------------------------------------------------------------------ activations in LDS
@@ -275,7 +278,8 @@ struct RowEngine {
 
     __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l_)
         : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + LPR - 1) / LPR), l16(l_) {
-        fr = Unit<WT>::frame(unit_off(l16), l16 & 7);
+        // (CB3: the sub-block of the lane's first block; planes: the lane's position in its tiles)
+        fr = Unit<WT>::frame(unit_off(l16), WT == kCB3 ? (l16 & 7) : l16);
     }
 
     // byte offset of block s of the row (CB3: of its super-block)

@@ -183,9 +183,89 @@ static int launch_gemv_f32(const void* w, uint64_t wbytes, const uint8_t* grid, 
     return launch_status();
 }
 
+// Repack into planes: one thread per block of a row copies the block's factor bytes to its
+// place in the tile's factor area and its scale to the tile's scale area (a one-time layout
+// change: byte copies, no arithmetic).
+template <int BB>
+__global__ __launch_bounds__(256) void pack_planes_kernel(const uint8_t* __restrict__ w, uint8_t* __restrict__ out,
+                                                          int64_t nrows, int nb) {
+    constexpr int FB = BB - 2;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= nrows * nb) return;
+    const int64_t r = g / nb;
+    const int b = (int)(g - r * nb);
+    const int t0 = b & ~15, n = nb - t0 < 16 ? nb - t0 : 16, i = b - t0;
+    const uint8_t* blk = w + (r * nb + b) * BB;
+    uint8_t* tile = out + (r * nb + t0) * BB;
+#pragma unroll
+    for (int j = 0; j < FB; ++j) tile[i * FB + j] = blk[2 + j];
+    tile[n * FB + 2 * i] = blk[0];
+    tile[n * FB + 2 * i + 1] = blk[1];
+}
+
+static int check_planes_args(int wtype, const void* src, const void* dst, int64_t nrows, int64_t k) {
+    if ((wtype != QMM_Q8_0 && wtype != QMM_IQ4_NL) || !src || !dst || nrows < 1 || k < 32 || k % 32)
+        return QMM_EINVAL;
+    if ((uint64_t)nrows * (uint64_t)qmm_row_bytes(wtype, k) > ((uint64_t)1 << 40)) return QMM_EUNSUPPORTED;
+    return QMM_OK;
+}
+
+static int launch_pack(int wtype, const void* w, void* out, int64_t nrows, int64_t k, hipStream_t st) {
+    const int nb = (int)(k / 32);
+    const dim3 g((unsigned)((nrows * nb + 255) / 256));
+    if (wtype == QMM_Q8_0)
+        hipLaunchKernelGGL(pack_planes_kernel<34>, g, dim3(256), 0, st, (const uint8_t*)w, (uint8_t*)out, nrows, nb);
+    else
+        hipLaunchKernelGGL(pack_planes_kernel<18>, g, dim3(256), 0, st, (const uint8_t*)w, (uint8_t*)out, nrows, nb);
+    return launch_status();
+}
+
 }  // namespace qmm
 
 using namespace qmm;
+
+extern "C" int qmm_pack_planes(int wtype, const void* w, int64_t nrows, int64_t k, void* planes, void* stream) {
+    const int rc = check_planes_args(wtype, w, planes, nrows, k);
+    if (rc) return rc;
+    if (k > ((int64_t)1 << 24) || nrows * (k / 32) > ((int64_t)1 << 40)) return QMM_EUNSUPPORTED;
+    return launch_pack(wtype, w, planes, nrows, k, as_stream(stream));
+}
+
+extern "C" int qmm_planes_alloc(int wtype, const void* w, int64_t nrows, int64_t k, void** planes, void* stream) {
+    if (!planes) return QMM_EINVAL;
+    *planes = nullptr;
+    const int rc = check_planes_args(wtype, w, w, nrows, k);
+    if (rc) return rc;
+    void* p = nullptr;
+    if (hipMalloc(&p, (size_t)nrows * (size_t)qmm_row_bytes(wtype, k)) != hipSuccess) return QMM_EHIP;
+    const int prc = qmm_pack_planes(wtype, w, nrows, k, p, stream);
+    if (prc) {
+        (void)hipFree(p);
+        return prc;
+    }
+    *planes = p;
+    return QMM_OK;
+}
+
+extern "C" int qmm_planes_release(void* planes) {
+    if (!planes) return QMM_OK;
+    return hipFree(planes) == hipSuccess ? QMM_OK : QMM_EHIP;
+}
+
+extern "C" int qgemv_planes(int wtype, const void* planes, int64_t nrows, int64_t k, const void* xq, int ncols, float* y,
+                            int64_t ldy, void* stream) {
+    if (wtype != QMM_Q8_0 && wtype != QMM_IQ4_NL) return QMM_EINVAL;
+    uint64_t wbytes, xqbytes;
+    const int rc = check_gemv_args(wtype, planes, nullptr, nrows, k, xq, ncols, y, &wbytes, &xqbytes);
+    if (rc) return rc;
+    if (ldy < nrows) return QMM_EINVAL;
+    if (k % 512) return QMM_EUNSUPPORTED;       // rows of whole 16-block tiles
+    if (!aligned(planes, 16)) return QMM_EALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (wtype == QMM_Q8_0)
+        return launch_gemv<kQ8_0P, false>(planes, wbytes, nullptr, nrows, k, xq, xqbytes, ncols, y, ldy, nullptr, st);
+    return launch_gemv<kIQ4_NLP, false>(planes, wbytes, nullptr, nrows, k, xq, xqbytes, ncols, y, ldy, nullptr, st);
+}
 
 extern "C" int qgemv_dense_f32(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k, const float* x,
                                int ncols, float* y, int64_t ldy, void* stream) {

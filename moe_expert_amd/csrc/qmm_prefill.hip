@@ -222,6 +222,32 @@ struct BRow<kIQ4_NL> {
     }
 };
 
+// F16: binary16 weights as they are (the FP16 dequantization's output).  Per step a lane reads,
+// for each of the step's four k16 fragments j = 2 bi + jj, its row's 8 values k = 32 bi + 16 jj +
+// 8 h .. + 7: one 16-byte load each (4 per lane and step), nothing to convert.
+template <>
+struct BPrep<kF16> {
+    u32x4 f[4];
+    __device__ __forceinline__ void convert(int j, int i, const IQ4Consts&, u32x4& F) const {
+        if (i) { F.z = f[j].z; F.w = f[j].w; } else { F.x = f[j].x; F.y = f[j].y; }
+    }
+};
+template <>
+struct BRow<kF16> {
+    static constexpr uint32_t kBytes = 64;  // bytes per 32 values
+    static constexpr int kLoads = 4;
+    u32x4 f[4];
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t row, int blk0, uint32_t hh) {
+        const uint32_t base = row + (uint32_t)blk0 * kBytes + 16u * hh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = ld128(r, base + 32u * j);
+    }
+    __device__ __forceinline__ void prepare(uint32_t, int, uint32_t, BPrep<kF16>& P) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P.f[j] = f[j];
+    }
+};
+
 // ---------------------------------------------------------------- activations -> LDS
 //
 // Stage layout: row r (0..255) at 128 r bytes, its 16-byte chunk c (k 8c .. 8c + 7) at slot
@@ -582,6 +608,74 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(DownArgs p) {
     }
 }
 
+// ---------------------------------------------------------------- dense prompt projections
+//
+// Y = X16 . W16^T over the prompt's tokens [DQ, Change: the dense weights as FP16 for a matrix
+// product over the prompt; PF, Summary: FP16 products with FP32 sums]: the K loop above with the
+// token rows in order (no routing) and one weight matrix.  Workgroup (token tile of 256 rows,
+// column tile of 256 weight rows); the tiles go to the 8 XCDs in contiguous runs (XCD c takes
+// token tiles in order with all their column tiles), so a token tile and the weight slices are
+// reused from that XCD's L2.  Y is stored straight from the accumulators as in the down GEMM.
+
+struct DenseArgs {
+    const uint8_t* w;
+    uint32_t wbytes;
+    int nrows, k, ntok, ntt, nct;
+    const uint16_t* x;
+    uint32_t xbytes;
+    float* y;
+    int64_t ldy;
+};
+
+template <int WT, int MB>
+__device__ __forceinline__ void dense_tile(const DenseArgs& p, int tt, int ct, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row0 = tt * kPfRows;
+    const int rows = p.ntok - row0 < kPfRows ? p.ntok - row0 : kPfRows;
+    uint32_t a_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = pf_arow(i);
+        a_off[i] = r < rows ? (uint32_t)(row0 + r) * (uint32_t)p.k * 2u : p.xbytes;
+    }
+    const int col = ct * kPfDownCols + 32 * w + (lane & 31);
+    const uint32_t roff = (uint32_t)(col < p.nrows ? col : p.nrows - 1) * (uint32_t)row_bytes_dev<WT>(p.k);
+    f32x16 acc[MB];
+    pf_gemm<WT, MB>(make_rsrc(p.x, p.xbytes), a_off, make_rsrc_dw(p.w, p.wbytes), roff, p.k / kPfStepK, lds, acc);
+    if (col < p.nrows) {
+        float* yc = p.y + (int64_t)row0 * p.ldy + col;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * m + acc_row(lane, r);
+                if (row < rows) yc[(int64_t)row * p.ldy] = acc[m][r];
+            }
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kPfThreads) void dense_kernel(DenseArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kPfStage];
+    const int total = p.ntt * p.nct;
+    const int per_xcd = (total + 7) >> 3;
+    const int lin = (int)(blockIdx.x & 7u) * per_xcd + (int)(blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || lin >= total) return;
+    const int tt = lin / p.nct, ct = lin - tt * p.nct;
+    const int rows = p.ntok - tt * kPfRows < kPfRows ? p.ntok - tt * kPfRows : kPfRows;
+    switch ((rows + 31) >> 5) {
+        case 1: dense_tile<WT, 1>(p, tt, ct, lds); break;
+        case 2: dense_tile<WT, 2>(p, tt, ct, lds); break;
+        case 3: dense_tile<WT, 3>(p, tt, ct, lds); break;
+        case 4: dense_tile<WT, 4>(p, tt, ct, lds); break;
+        case 5: dense_tile<WT, 5>(p, tt, ct, lds); break;
+        case 6: dense_tile<WT, 6>(p, tt, ct, lds); break;
+        case 7: dense_tile<WT, 7>(p, tt, ct, lds); break;
+        case 8: dense_tile<WT, 8>(p, tt, ct, lds); break;
+        default: break;
+    }
+}
+
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 static int64_t max_tiles_of(int nexperts, int64_t nentries) { return (nentries + kPfRows - 1) / kPfRows + nexperts; }
 
@@ -694,4 +788,39 @@ extern "C" int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const voi
         else hipLaunchKernelGGL(pf_down_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
         return launch_status();
     }
+}
+
+extern "C" int qgemm_dense(int wtype, const void* w, int64_t nrows, int64_t k, const uint16_t* x_f16, int64_t ntok,
+                           float* y, int64_t ldy, void* stream) {
+    if (wtype != QMM_Q8_0 && wtype != QMM_IQ4_NL && wtype != QMM_F16) return QMM_EINVAL;
+    if (!w || !x_f16 || !y || nrows < 1 || k < 1 || ntok < 0 || ldy < nrows) return QMM_EINVAL;
+    if (qmm_row_bytes(wtype, k) == 0) return QMM_EINVAL;
+    if (k % kPfStepK) return QMM_EUNSUPPORTED;
+    if (!aligned(w, wtype == QMM_F16 ? 16 : 4) || !aligned(x_f16, 16) || !aligned(y, 4)) return QMM_EALIGN;
+    if (wtype == QMM_F16 && k % 8) return QMM_EALIGN;
+    const uint64_t wbytes = (uint64_t)nrows * (uint64_t)qmm_row_bytes(wtype, k);
+    if (k > kMaxK || nrows > 0x7FFFFFFF || wbytes > kMaxBufferBytes ||
+        (uint64_t)ntok * k * 2 + 2 * (uint64_t)k + 128 > kMaxBufferBytes)
+        return QMM_EUNSUPPORTED;
+    if (ntok == 0) return QMM_OK;
+    DenseArgs a;
+    a.w = (const uint8_t*)w;
+    a.wbytes = (uint32_t)wbytes;
+    a.nrows = (int)nrows;
+    a.k = (int)k;
+    a.ntok = (int)ntok;
+    a.ntt = (int)((ntok + kPfRows - 1) / kPfRows);
+    a.nct = (int)((nrows + kPfDownCols - 1) / kPfDownCols);
+    a.x = x_f16;
+    a.xbytes = (uint32_t)(ntok * k * 2);
+    a.y = y;
+    a.ldy = ldy;
+    const int64_t total = (int64_t)a.ntt * a.nct;
+    if (total > 0x0FFFFFFF) return QMM_EUNSUPPORTED;
+    const dim3 g((unsigned)(8 * ((total + 7) / 8)));
+    const hipStream_t st = as_stream(stream);
+    if (wtype == QMM_Q8_0) hipLaunchKernelGGL(dense_kernel<kQ8_0>, g, dim3(kPfThreads), 0, st, a);
+    else if (wtype == QMM_IQ4_NL) hipLaunchKernelGGL(dense_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
+    else hipLaunchKernelGGL(dense_kernel<kF16>, g, dim3(kPfThreads), 0, st, a);
+    return launch_status();
 }

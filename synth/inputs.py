@@ -26,7 +26,7 @@ __all__ = [
     "Q8_0", "IQ4_NL", "CB3", "BLOCK_VALUES", "BLOCK_BYTES", "Q8_1_BYTES",
     "rng_for", "row_bytes", "fp16_scales", "q8_0_weights", "iq4nl_weights",
     "cb3_weights", "cb3_grid", "weights", "activations", "decode_routing", "decode_routings",
-    "prefill_routing", "prefill_tokens", "SEEDS",
+    "prefill_routing", "prefill_tokens", "router_weights", "token_positions", "SEEDS",
 ]
 
 # seed = 1000 * workload number + copy index
@@ -146,3 +146,17 @@ def prefill_routing(rng: np.random.Generator, ntok: int, nexperts: int, topk: in
 def prefill_tokens(rng: np.random.Generator, ntok: int, hidden: int) -> np.ndarray:
     """[ntok, hidden] fp16 activations ~ N(0, 1) (numpy's conversion to half)."""
     return rng.standard_normal(size=(ntok, hidden)).astype(np.float16)
+
+
+def router_weights(rng: np.random.Generator, ntok: int, topk: int) -> np.ndarray:
+    """[ntok, topk] float32 positive router weights, each row drawn uniformly and scaled to sum
+    to 1 (in float64, then rounded to float32)."""
+    w = rng.random(size=(ntok, topk)) + 1e-3
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def token_positions(sorted_tok: np.ndarray, ntok: int, topk: int) -> np.ndarray:
+    """[ntok, topk] int32: where each token's entries sit in an expert-sorted entry list, in the
+    order of the list (ascending expert).  Every token must have exactly topk entries."""
+    order = np.argsort(np.asarray(sorted_tok), kind="stable")
+    return order.reshape(ntok, topk).astype(np.int32)

@@ -236,3 +236,41 @@ def test_binding_refuses_bad_grouped_and_prefill_tensors():
     with pytest.raises(ValueError):
         M.qgemm_prefill_experts(M.QMM_IQ4_NL, wg, wg, M.QMM_Q8_0, wd, 4, 2560, 1024, F((64, 2560), torch.float16),
                                 st, off, y=F((128, 2560), torch.float32), ws=F((64,), u8))
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 8, 64, FAKE, FAKE, 4, 2, FAKE, 64, None), -1),          # null rows
+    ((FAKE, 8, 64, FAKE, FAKE, 4, 0, FAKE, 64, None), -1),          # topk 0
+    ((FAKE, 8, 64, FAKE, FAKE, 4, 65, FAKE, 64, None), -2),         # topk above 64
+    ((FAKE, 8, 66, FAKE, FAKE, 4, 2, FAKE, 68, None), -2),          # hidden not a multiple of 4
+    ((FAKE, 8, 64, FAKE, FAKE, 4, 2, FAKE, 60, None), -1),          # ldo < hidden
+    ((C.c_void_p(0x100004), 8, 64, FAKE, FAKE, 4, 2, FAKE, 64, None), -3),   # y not 16-byte aligned
+    ((FAKE, 8, 64, FAKE, FAKE, 0, 2, FAKE, 64, None), 0),           # no tokens: no launch
+])
+def test_combine_rejects(args, expect):
+    assert M.lib().qmm_moe_combine(*args) == expect
+
+
+def test_planes_reject():
+    L = M.lib()
+    A16 = C.c_void_p(0x100000)
+    assert L.qgemv_planes(M.QMM_CB3, A16, 64, 2560, FAKE, 1, FAKE, 64, None) == -1    # planes: Q8_0 / IQ4_NL
+    assert L.qgemv_planes(M.QMM_Q8_0, A16, 64, 2592, FAKE, 1, FAKE, 64, None) == -2   # rows of whole tiles
+    assert L.qgemv_planes(M.QMM_Q8_0, C.c_void_p(0x100004), 64, 2560, FAKE, 1, FAKE, 64, None) == -3
+    assert L.qmm_pack_planes(M.QMM_CB3, FAKE, 4, 256, FAKE, None) == -1
+    assert L.qmm_pack_planes(M.QMM_Q8_0, FAKE, 4, 48, FAKE, None) == -1
+    p = C.c_void_p(123)
+    assert L.qmm_planes_alloc(M.QMM_IQ4_NL, None, 4, 64, C.byref(p), None) == -1 and not p.value
+    assert L.qmm_planes_release(None) == 0
+
+
+def test_dense_rejects():
+    L = M.lib()
+    A16 = C.c_void_p(0x100000)
+    assert L.qgemm_dense(M.QMM_CB3, A16, 64, 2560, A16, 8, A16, 64, None) == -1      # no CB3
+    assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2592, A16, 8, A16, 64, None) == -2     # K steps of 64
+    assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2560, C.c_void_p(0x100008), 8, A16, 64, None) == -3
+    assert L.qgemm_dense(M.QMM_F16, C.c_void_p(0x100004), 64, 2560, A16, 8, A16, 64, None) == -3
+    assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2560, A16, 8, A16, 63, None) == -1     # ldy < nrows
+    assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2560, A16, 0, A16, 64, None) == 0      # no tokens
+    assert M.row_bytes(M.QMM_F16, 2560) == 5120
