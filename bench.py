@@ -485,7 +485,7 @@ def prefill_setup(torch, M):
                                 d["st"], d["off"], y=y, ws=ws)
 
     host = dict(wg=wg, wu=wu, wd=wd, x16=x16, st=st, off=off)
-    return call, host, dict(nexp=nexp, ntok=ntok, topk=topk, hidden=hidden, inter=inter, nent=nent)
+    return call, host, dict(nexp=nexp, ntok=ntok, topk=topk, hidden=hidden, inter=inter, nent=nent, dev_inputs=d)
 
 
 def mfma_reference(torch, M, reps):
@@ -583,8 +583,13 @@ def bench_combine(args, torch, M, cpu_s=3.0):
         w = synth.router_weights(rng, ntok, topk)
         di, dw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
         out = torch.empty((ntok, hidden), dtype=torch.float32, device=dev)
-        reps = 10 if ntok > 64 else 200
-        ms = timed_graph(torch, lambda: M.qmm_moe_combine(y, di, dw, out=out), reps, not args.no_graph)
+        # calls per graph: a replay of one graph per short call would time the host's replay rate
+        per = 1 if ntok > 64 else 100
+
+        def calls():
+            for _ in range(per):
+                M.qmm_moe_combine(y, di, dw, out=out)
+        ms = timed_graph(torch, calls, 10, not args.no_graph) / per
         b = combine_bytes(ntok, topk, hidden)
         gbps = b / (ms * 1e-3) / 1e9
         r = {"us_per_call": round(ms * 1e3, 3), "gbps": round(gbps, 1),
@@ -688,11 +693,60 @@ def bench_planes(args, torch, M):
     return res
 
 
+INT8_MFMA_PEAK_TOPS = 5000.0
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9     # non-packed binary32 VALU lane operations per second
+
+
+def bench_mmq(args, torch, M, cpu_s=3.0):
+    """The MMQ-style prefill (int8 MFMA on q8_1 activations, SwiGLU + q8_1 of H fused) on the
+    prefill workload, beside the FP16 path on the same inputs."""
+    import oracle
+    import synth
+    call, h, z = prefill_setup(torch, M)
+    nexp, hidden, inter, nent, ntok = z["nexp"], z["hidden"], z["inter"], z["nent"], z["ntok"]
+    d = z["dev_inputs"]
+    y = torch.empty((nent, hidden), dtype=torch.float32, device=d["wg"].device)
+    ws = torch.empty(M.qgemm_prefill_experts_q8_workspace(nexp, hidden, inter, ntok, nent), dtype=torch.uint8,
+                     device=d["wg"].device)
+
+    def mmq():
+        M.qgemm_prefill_experts_q8(synth.IQ4_NL, d["wg"], d["wu"], synth.Q8_0, d["wd"], nexp, hidden, inter, d["x"],
+                                   d["st"], d["off"], y=y, ws=ws)
+    g = not args.no_graph
+    ms = timed_graph(torch, mmq, max(args.steps, 5), g)
+    ms_f16 = timed_graph(torch, call, max(args.steps, 5), g)
+    flops = 2.0 * nent * 2 * inter * hidden + 2.0 * nent * hidden * inter
+    tops = flops / (ms * 1e-3) / 1e12
+    # the per-block rescale: one conversion and one fma per output and 32-value block
+    valu_ops = 2.0 * nent * (2 * inter * (hidden // 32) + hidden * (inter // 32))
+    r = {"us_per_call": round(ms * 1e3, 2), "tops": round(tops, 1),
+         "fp16_path_us_per_call": round(ms_f16 * 1e3, 2),
+         "valu_floor_us": round(valu_ops / VALU_LANE_OPS_PEAK * 1e6, 1),
+         "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOP/s",
+                      "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_call": flops,
+                      "kernel": "quantize_planes + schedule + mq_gateup_kernel + mq_down_kernel (one call)"},
+         "workload": "prefill 8192 tokens x 2560, top-8 of 128 experts, IQ4_NL gate/up, Q8_0 down; q8_1 activations, "
+                     "int8 MFMA, fp32 MFMA for the block scale products"}
+    if not args.no_cpu:
+        xq = oracle.quantize_q8_1(h["x16"].astype(np.float32))
+        sl = np.arange(16, dtype=np.int64)
+        exps = (np.searchsorted(h["off"], sl, side="right") - 1).astype(np.int32)
+
+        def rows():
+            oracle.grouped(synth.IQ4_NL, h["wg"], h["wu"], synth.Q8_0, h["wd"], hidden, inter, xq, exps,
+                           np.arange(17, dtype=np.int32), h["st"][sl])
+        rate, reps_c, dt = cpu_rate(rows, flops / nent * 16, cpu_s)
+        r["cpu_baseline"] = {"value": round(rate / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(),
+                             "kind": "oracle", "sample": f"the first 16 sorted rows x {reps_c}, {dt:.1f} s"}
+    return r
+
+
 def next_rows(args, torch, M):
-    """The rows after the contract's workloads: MoE combine, dense prompt projections, planes."""
+    """The rows after the contract's workloads: MoE combine, dense prompt projections, planes,
+    the MMQ-style prefill."""
     out = {}
     for name, fn in (("moe_combine", bench_combine), ("dense_prompt_projection", bench_dense),
-                     ("weight_planes_gemv", bench_planes)):
+                     ("weight_planes_gemv", bench_planes), ("mmq_prefill", bench_mmq)):
         t0 = time.perf_counter()
         out[name] = fn(args, torch, M)
         torch.cuda.empty_cache()
@@ -903,7 +957,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill", "next"],
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill", "next", "mmq"],
                     help="all (default): the headline GEMV line with every other workload under 'configs'")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -951,6 +1006,8 @@ def main() -> int:
         print(json.dumps(bench_grouped(args, torch, M)), flush=True)
     elif args.workload == "next":
         print(json.dumps(next_rows(args, torch, M)), flush=True)
+    elif args.workload == "mmq":
+        print(json.dumps(bench_mmq(args, torch, M)), flush=True)
     else:
         print(json.dumps(bench_prefill(args, torch, M)), flush=True)
     return 0

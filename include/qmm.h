@@ -232,6 +232,36 @@ int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const void* w_up,
                           const int32_t* expert_off, int64_t nentries, float* y, void* ws,
                           size_t ws_bytes, unsigned flags, void* stream);
 
+/* Workspace bytes qgemm_prefill_experts_q8 needs (host). */
+size_t qgemm_prefill_experts_q8_workspace(int nexperts, int64_t hidden, int64_t inter, int64_t ntok,
+                                          int64_t nentries, unsigned flags);
+
+/* MMQ-style prefill grouped expert GEMM [DQ, Change: the prefill path on q8_1 activations
+ * against the quantized weights, with SwiGLU and the q8_1 quantization of H fused between
+ * gate/up and down, H never stored in fp32; IQ, What it does: the decode path's per-block
+ * integer dot and float expression].  Computes, over the rows sorted per expert, exactly what
+ * qgemv_grouped_experts computes with groups = experts and entry_col = sorted_tok:
+ *   xq  = q8_1(X16 as binary32) per 32-value block               (the quantizer's arithmetic)
+ *   g,u = per 32-value block b: (d_w d_a) * isum in binary32, summed over b in order
+ *   H   = q8_1(silu(g) * u) per 32 consecutive intermediate values (silu in binary32 with the
+ *         device expf, error <= 1 ulp, and v_rcp_f32)
+ *   y[p*hidden + j] = the same block sum of W_down[e] against H   (binary32; sorted order)
+ * The block dots run on int8 MFMA, the per-block scale products on fp32 MFMA.
+ *   Arguments as qgemm_prefill_experts (Q8_0 or IQ4_NL; hidden, inter multiples of 64).
+ *   ws : qgemm_prefill_experts_q8_workspace() bytes, 16-byte aligned.  Layout (each part at the
+ *        next 16-byte boundary): the tokens' q8_1 as planes (int8 [ntok][hidden], then the
+ *        binary16 scales [ntok][hidden/32]), H as planes (int8 [nentries][inter], then scales
+ *        [nentries][inter/32]), the tile schedule, and with QMM_FLAG_DEBUG_INTERMEDIATES g, u
+ *        as float [nentries][inter].
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_ESPACE. */
+int qgemm_prefill_experts_q8(int wtype_gu, const void* w_gate, const void* w_up,
+                             int64_t gu_expert_stride, int wtype_down, const void* w_down,
+                             int64_t down_expert_stride, int nexperts, int64_t hidden,
+                             int64_t inter, const uint16_t* x_f16, int64_t ntok,
+                             const int32_t* sorted_tok, const int32_t* expert_off,
+                             int64_t nentries, float* y, void* ws, size_t ws_bytes,
+                             unsigned flags, void* stream);
+
 /* Dense prompt projection [DQ, Change: dense Q8_0 / IQ4_XS weights dequantized to FP16 with
  * 16-byte stores for a matrix product over the prompt's tokens; PF, Summary: the FP16 weights the
  * matrix cores get, FP32 sums]:

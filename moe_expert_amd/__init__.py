@@ -52,6 +52,9 @@ SIGNATURES = {
     "qmm_planes_release": (_I32, [_P]),
     "qgemv_planes": (_I32, [_I32, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qgemm_dense": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "qgemm_prefill_experts_q8_workspace": (_SZ, [_I32, _I64, _I64, _I64, _I64, _U32]),
+    "qgemm_prefill_experts_q8": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _I64, _I64, _P, _I64,
+                                        _P, _P, _I64, _P, _P, _SZ, _U32, _P]),
     "qgemm_prefill_experts_workspace": (_SZ, [_I32, _I64, _I64, _U32]),
     "qgemm_prefill_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _I64, _I64, _P, _I64,
                                      _P, _P, _I64, _P, _P, _SZ, _U32, _P]),
@@ -480,3 +483,36 @@ def qgemm_dense(wtype, w, nrows, k, x_f16, y=None, ldy=None, stream=None):
     _check("qgemm_dense", lib().qgemm_dense(wtype, _ptr(w), nrows, k, _ptr(x_f16), ntok, _ptr(y), ldy,
                                            _stream(stream, w.device)))
     return y
+
+
+def qgemm_prefill_experts_q8_workspace(nexperts, hidden, inter, ntok, nentries, flags=0):
+    return int(lib().qgemm_prefill_experts_q8_workspace(nexperts, hidden, inter, ntok, nentries, flags))
+
+
+def qgemm_prefill_experts_q8(wtype_gu, w_gate, w_up, wtype_down, w_down, nexperts, hidden, inter, x_f16, sorted_tok,
+                             expert_off, y=None, ws=None, flags=0, stream=None):
+    """MMQ-style prefill (int8 MFMA, q8_1 activations, SwiGLU + q8_1 of H fused); arguments as
+    qgemm_prefill_experts; returns (y [nentries, hidden] float32, ws)."""
+    import torch
+    if getattr(x_f16, "dim", lambda: 0)() != 2 or x_f16.shape[1] != hidden:
+        raise ValueError("x_f16 must be [ntok, hidden]")
+    dev = x_f16.device
+    ntok = int(x_f16.shape[0])
+    _need(x_f16, "x_f16", "f16", ntok * hidden * 2, dev)
+    gu_stride = inter * _block_multiple(wtype_gu, hidden, "hidden")
+    d_stride = hidden * _block_multiple(wtype_down, inter, "inter")
+    for t, n, s in ((w_gate, "w_gate", gu_stride), (w_up, "w_up", gu_stride), (w_down, "w_down", d_stride)):
+        if t is None or int(t.numel()) * int(t.element_size()) != nexperts * s:
+            raise ValueError(f"{n} must hold {nexperts} expert matrices of {s} bytes")
+        _need(t, n, "u8", nexperts * s, dev)
+    nentries = int(sorted_tok.numel())
+    _need(sorted_tok, "sorted_tok", "i32", 0, dev)
+    _need(expert_off, "expert_off", "i32", (nexperts + 1) * 4, dev)
+    y = _out(y, "y", "f32", nentries * hidden * 4, dev, (nentries, hidden), torch.float32)
+    need = qgemm_prefill_experts_q8_workspace(nexperts, hidden, inter, ntok, nentries, flags)
+    ws = _out(ws, "ws", "u8", need, dev, (max(need, 16),), torch.uint8)
+    _check("qgemm_prefill_experts_q8", lib().qgemm_prefill_experts_q8(
+        wtype_gu, _ptr(w_gate), _ptr(w_up), gu_stride, wtype_down, _ptr(w_down), d_stride, nexperts, hidden, inter,
+        _ptr(x_f16), ntok, _ptr(sorted_tok), _ptr(expert_off), nentries, _ptr(y), _ptr(ws), _nbytes(ws), flags,
+        _stream(stream, dev)))
+    return y, ws

@@ -167,6 +167,14 @@ __device__ __forceinline__ half2_t splat_h2(uint32_t dbits) {
     return half2_t{d, d};
 }
 
+// IQ4_NL: four 4-bit indices (the low 3 bits in i7, the bit-3 selector in i8, as
+// iq4nl_decode_word forms them) -> the four signed int8 levels.
+__device__ __forceinline__ uint32_t iq4nl_lookup_s(uint32_t i7, uint32_t i8) {
+    const uint32_t lo = perm(kv_word(1), kv_word(0), i7);
+    const uint32_t hi = perm(kv_word(3), kv_word(2), i7);
+    return perm(hi, lo, i8);
+}
+
 // IQ4_NL: four 4-bit indices (as for iq4nl_lookup) -> four biased levels.
 __device__ __forceinline__ uint32_t iq4nl_lookup_u(uint32_t i7, uint32_t i8) {
     const uint32_t lo = perm(kvu_word(1), kvu_word(0), i7);

@@ -5,7 +5,8 @@
 // to FP16 matrix math over the token rows sorted per expert; the FP16 weights are the standalone
 // dequantizer's; an expert's partial last tile is masked]:
 //   schedule kernel : expert_off -> (expert, first row, rows) tiles; an expert's rows are split
-//                     into ceil(n/256) tiles of equal size rounded up to 32 rows
+//                     into ceil(n/T) tiles of equal size rounded up to 32 rows (T = 256 here,
+//                     128 in the MMQ-style path)
 //   gate/up kernel  : tile x 128 intermediate columns: G, U = X16[tok] . W16^T for the gate and
 //                     up rows of those columns; epilogue H16 = fp16(silu(G) * U)
 //   down kernel     : tile x 256 output columns: Y = H16 . Wd16^T
@@ -52,7 +53,7 @@ struct Tile {
 // ---------------------------------------------------------------- schedule
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ expert_off, int nexperts, int nentries,
-                                                        int32_t* __restrict__ tiles, int max_tiles) {
+                                                        int32_t* __restrict__ tiles, int max_tiles, int tile_rows) {
     __shared__ int scan[1024];
     __shared__ int base;
     if (threadIdx.x == 0) base = 0;
@@ -69,8 +70,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
         const int rows = o1 - o0;
         int per = 0, n = 0;
         if (rows > 0) {
-            const int t = (rows + kPfRows - 1) / kPfRows;
-            per = ((rows + t - 1) / t + 31) & ~31;  // <= 256, >= rows / t
+            const int t = (rows + tile_rows - 1) / tile_rows;
+            per = ((rows + t - 1) / t + 31) & ~31;  // <= tile_rows, >= rows / t
             n = (rows + per - 1) / per;             // <= t
         }
         scan[threadIdx.x] = n;
@@ -676,8 +677,370 @@ __global__ __launch_bounds__(kPfThreads) void dense_kernel(DenseArgs p) {
     }
 }
 
+// ---------------------------------------------------------------- MMQ-style prefill: int8 MFMA
+//
+// [DQ, Change: the prefill's second path takes q8_1 activations against the quantized weights
+// (MMQ), with SwiGLU and the q8_1 quantization of H fused between gate/up and down, H never in
+// fp32; IQ, What it does: the per-block integer dot and float expression of the decode path]:
+// the grouped decode's arithmetic over the sorted rows of the prefill.  Per 32-value block b of
+// an output (row p, column c):  isum = sum_j w_int[c][32b + j] q_a[p][32b + j]  (exact int32),
+// t = (d_w[c][b] d_a[p][b]) isum,  acc += t  in binary32, blocks in order.
+//   - isum: v_mfma_i32_32x32x32_i8 per 32x32 tile and block (lane l: row or column l % 32,
+//     k = 16 (l / 32) .. + 15 of the block);
+//   - d_w d_a: the tile's 32 x 32 products as a rank-one v_mfma_f32_32x32x2f32 (A = d_a in the
+//     k = 0 lanes, 0 in the k = 1 lanes; B = d_w): exact, a product of two binary16 values, and
+//     on the matrix unit, not the VALU;
+//   - acc = fma(d_w d_a, float(isum), acc): the two VALU operations per output and block that
+//     remain (the per-block scales are what make this path VALU-bound on gfx950).
+// Activations (the tokens' q8_1 and H) are held as planes: int8 values [rows][k] and their
+// binary16 scales [rows][k/32], so a step's 128 rows x 64 values are staged in LDS by 16-byte
+// direct-to-LDS loads like the FP16 path's.  Tiles are at most 128 rows (4 blocks of 32): the
+// per-block rescale keeps two 16-register MFMA results live beside the accumulators, and 8
+// blocks of accumulators would not fit 256 registers.  Each wave owns 32 weight rows as in the
+// FP16 path;
+// a lane pair (l, l + 32) reads its row's two blocks of a step once (one each) and trades halves
+// through v_permlane32_swap.  Three LDS stages, activations and raw weights two steps ahead.
+
+constexpr int kMqRows = 128;                         // rows per tile (4 MFMA blocks of 32)
+constexpr int kMqStageQ = kMqRows * 64;              // int8 values of a step: 8 KiB
+constexpr int kMqStageD = 8 * 256;                   // scales: 256 bytes per wave of 16 rows
+constexpr int kMqStage = kMqStageQ + kMqStageD;      // 10 KiB
+constexpr int kMqStages = 3;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// Stage layout: row r's 16-byte chunk c (k 16 c .. 16 c + 15 of the step) at 64 r + 16 (c ^
+// mq_swz(r)): a fragment read (32 lanes, rows r0 .. r0 + 31, one chunk) puts any 16 consecutive
+// lanes on 16 distinct 16-byte slots of a 256-byte window.  Scales: the two binary16 scales of
+// row r (blocks 2 s, 2 s + 1) at kMqStageQ + 256 (r / 16) + 4 (r % 16) (wave w stages rows
+// 16 w .. 16 w + 15; its 64-lane dword load writes 256 bytes, the rows' 64 and 192 of zeros).
+__device__ __forceinline__ uint32_t mq_swz(uint32_t r) { return (r >> 2) & 3u; }
+
+// A row's raw weights of a step -> the int8 B fragments of its two blocks and their scales.
+template <int WT>
+struct MqB;
+template <>
+struct MqB<kQ8_0> {
+    i32x4 f[2];
+    uint32_t d[2];
+    __device__ __forceinline__ void prepare(const BRow<kQ8_0>& R, uint32_t row, int blk0, uint32_t hh,
+                                            const IQ4Consts&) {
+        const uint32_t o = BRow<kQ8_0>::off(row, blk0, hh);
+        const uint32_t sel = realign_sel(o);
+        const uint32_t raw[9] = {R.a.x, R.a.y, R.a.z, R.a.w, R.b.x, R.b.y, R.b.z, R.b.w, R.c};
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = perm(raw[i + 1], raw[i], sel);
+        // lane l < 32 holds block 0 and needs bytes 0..15 of both blocks; lane l + 32 holds
+        // block 1 and needs bytes 16..31 of both
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t r0, r1;
+            swap32(q[i], q[4 + i], r0, r1);
+            f[0][i] = (int)r0;
+            f[1][i] = (int)r1;
+        }
+        const uint32_t ds = realign_scale(R.a.x, o);
+        swap32(ds, ds, d[0], d[1]);
+    }
+};
+template <>
+struct MqB<kIQ4_NL> {
+    i32x4 f[2];
+    uint32_t d[2];
+    __device__ __forceinline__ void prepare(const BRow<kIQ4_NL>& R, uint32_t row, int blk0, uint32_t hh,
+                                            const IQ4Consts& k) {
+        const uint32_t o = BRow<kIQ4_NL>::off(row, blk0, hh);
+        const uint32_t sel = realign_sel(o);
+        const uint32_t q[4] = {perm(R.a.y, R.a.x, sel), perm(R.a.z, R.a.y, sel), perm(R.a.w, R.a.z, sel),
+                               perm(R.b, R.a.w, sel)};
+        // both lanes of a pair need all 16 index bytes of both blocks: lane l < 32 their low
+        // nibbles (values 0..15), lane l + 32 their high nibbles (values 16..31)
+        const uint32_t shift = 4u * hh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t b0, b1;
+            swap32(q[i], q[i], b0, b1);
+            const uint32_t w0 = b0 >> shift, w1 = b1 >> shift;
+            f[0][i] = (int)iq4nl_lookup_s(w0 & k.m7, ((w0 >> 1) & k.m4) | k.c0123);
+            f[1][i] = (int)iq4nl_lookup_s(w1 & k.m7, ((w1 >> 1) & k.m4) | k.c0123);
+        }
+        const uint32_t ds = realign_scale(R.a.x, o);
+        swap32(ds, ds, d[0], d[1]);
+    }
+};
+
+// acc[m]: rows 32 m .. 32 m + 31 of the tile, this wave's 32 weight rows.  q_off[i] / d_off: byte
+// offsets in the planes of the activation row this thread stages (past the end for rows beyond
+// the tile, which read zeros); b_row: this lane's weight row in the matrix of resource wr.
+template <int WT, int MB>
+__device__ __forceinline__ void mq_gemm(rsrc_t aq, rsrc_t ad, uint32_t q_off, uint32_t d_off, rsrc_t wr,
+                                        uint32_t b_row, int nk, uint8_t* lds, f32x16 (&acc)[MB]) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t hh = lane >> 5;
+    const int last = nk - 1;
+    const IQ4Consts kc;
+    // fill: wave w stages rows 16 w .. 16 w + 15 (lane: row 16 w + lane / 4, slot lane % 4)
+    const uint32_t voff = q_off + (((lane & 3u) ^ mq_swz(16u * wv + (lane >> 2))) * 16u);
+    auto fill = [&](int st, int ks) {
+        uint8_t* base = lds + st * kMqStage;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(aq, (lds_ptr_t)(base + 1024u * wv), 16, voff, (uint32_t)ks * 64u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ad, (lds_ptr_t)(base + kMqStageQ + 256u * wv), 4, d_off,
+                                                 (uint32_t)ks * 4u, 0, 0);
+    };
+    // fragment read addresses (row 32 m + lane % 32, chunk 2 b + lane / 32) and scale reads
+    uint32_t ra[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) ra[b] = (lane & 31u) * 64u + (((2u * b + hh) ^ mq_swz(lane & 31u)) * 16u);
+    const uint32_t rd = kMqStageQ + 256u * ((lane & 31u) >> 4) + 4u * (lane & 15u);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+
+    BRow<WT> R0, R1;
+    fill(0, 0);
+    R0.load(wr, b_row, 0, hh);
+    fill(1, min(1, last));
+    R1.load(wr, b_row, 2 * min(1, last), hh);
+    constexpr int kWait = 2 + BRow<WT>::kLoads;  // the fills and raw weights of the next step
+    // One step; R holds its raw weights and is reloaded with those of step ks + 2.  Steps run in
+    // pairs so the two raw-weight register sets keep fixed roles (a runtime index would put them
+    // in scratch memory).
+    auto step = [&](int ks, BRow<WT>& R) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        fill((ks + 2) % kMqStages, min(ks + 2, last));
+        MqB<WT> B;
+        B.prepare(R, b_row, 2 * ks, hh, kc);
+        R.load(wr, b_row, 2 * min(ks + 2, last), hh);
+        const float dw[2] = {h2f(B.d[0]), h2f(B.d[1])};
+        const uint8_t* st = lds + (ks % kMqStages) * kMqStage;
+        // the step's A fragments and row scales first (pair i = (row block i / 2, block i % 2)),
+        // then a pipeline over the pairs: the two MFMAs of pair i + 1 are issued before the
+        // VALU rescale of pair i, so the matrix unit and the VALU overlap within the wave
+        constexpr int P = 2 * MB;
+        i32x4 a[P];
+        float da[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int m = i >> 1, b = i & 1;
+            a[i] = *(const i32x4*)(st + ra[b] + 2048u * m);
+            uint32_t dbits = *(const uint32_t*)(st + rd + 512u * m);
+            asm volatile("" : "+v"(dbits));  // read by every lane (kept out of a branch)
+            const float v = h2f(b ? dbits >> 16 : dbits);
+            da[i] = hh ? 0.0f : v;           // the k = 1 half of the rank-one product is zero
+        }
+        i32x16 is[2];
+        f32x16 sc[2];
+        auto issue = [&](int i) {
+            is[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], B.f[i & 1], i32x16{}, 0, 0, 0);
+            sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(da[i], dw[i & 1], f32x16{}, 0, 0, 0);
+        };
+        issue(0);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (i + 1 < P) issue(i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int m = i >> 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = __builtin_fmaf(sc[i & 1][r], (float)is[i & 1][r], acc[m][r]);
+                // pinned here: left to itself the compiler sinks these updates into the next
+                // step, holding every pair's result registers live at once
+                asm volatile("" : "+v"(v));
+                acc[m][r] = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+        step(ks, R0);
+        step(ks + 1, R1);
+    }
+    if (ks < nk) step(ks, R0);
+    // the last steps started (clamped) fills: let every wave's land before LDS is reused
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __syncthreads();
+}
+
+// q8_1 planes of rows of binary16 values: one aligned half wave per 32-value block, the q8_1
+// quantizer's arithmetic (quantize_lanes32) on the exact binary32 value of each input.
+__global__ __launch_bounds__(256) void quantize_planes_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                              int8_t* __restrict__ q, uint16_t* __restrict__ d) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t blk = g >> 5;
+    const int j = (int)(g & 31);
+    const bool ok = blk < nblocks;
+    const float v = ok ? h2f(x[blk * 32 + j]) : 0.0f;
+    uint32_t hdr;
+    const int qv = quantize_lanes32(v, hdr);
+    const uint32_t word = pack4_lanes(qv);
+    if (ok) {
+        if ((j & 3) == 0) *(uint32_t*)(q + blk * 32 + j) = word;
+        if (j == 0) d[blk] = (uint16_t)(hdr & 0xFFFFu);
+    }
+}
+
+struct MqGuArgs {
+    const uint8_t* wg;
+    const uint8_t* wu;
+    int64_t stride;
+    uint32_t expert_bytes;
+    int nexperts, hidden, inter, ntok;
+    const int8_t* xq;
+    const uint16_t* xd;
+    uint32_t xq_bytes, xd_bytes;
+    const int32_t* sorted_tok;
+    const int32_t* tiles;
+    int8_t* hq;
+    uint16_t* hd;
+    float* dbg_g;
+    float* dbg_u;
+};
+
+// Gate/up tile: waves 0..3 the gate rows of intermediate columns y 128 + 32 w + 0..31, waves
+// 4..7 the up rows of the same columns.  Epilogue per 64-row quarter: G and U through LDS, then
+// one half wave per (row, 32-column group) forms h = silu(G) U and its q8_1 block (the
+// quantizer's arithmetic), written to the H planes; h is never stored.
+template <int WT, int MB>
+__device__ __forceinline__ void mq_gateup_tile(const MqGuArgs& p, const Tile& t, int y, uint8_t* lds) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nb = p.hidden / 32;
+    uint32_t q_off, d_off;
+    {
+        const int r = 16 * w + (lane >> 2);
+        const int tok = r < t.nrows ? p.sorted_tok[t.row0 + r] : -1;
+        q_off = (tok >= 0 && tok < p.ntok) ? (uint32_t)tok * (uint32_t)p.hidden : p.xq_bytes;
+    }
+    {
+        const int r = 16 * w + (lane & 15);
+        const int tok = (lane < 16 && r < t.nrows) ? p.sorted_tok[t.row0 + r] : -1;
+        d_off = (tok >= 0 && tok < p.ntok) ? (uint32_t)tok * (uint32_t)nb * 2u : p.xd_bytes;
+    }
+    const int col = y * kPfGuCols + 32 * (w & 3) + (lane & 31);
+    const uint32_t roff = (uint32_t)(col < p.inter ? col : p.inter - 1) * (uint32_t)row_bytes_dev<WT>(p.hidden);
+    const rsrc_t wr = make_rsrc_dw((w >= 4 ? p.wu : p.wg) + (int64_t)t.e * p.stride, p.expert_bytes);
+    f32x16 acc[MB];
+    mq_gemm<WT, MB>(make_rsrc(p.xq, p.xq_bytes), make_rsrc(p.xd, p.xd_bytes), q_off, d_off, wr, roff,
+                    p.hidden / kPfStepK, lds, acc);
+
+    float* tile = (float*)lds;
+    const int nbh = p.inter / 32;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+        if (2 * qq >= MB) break;
+        epi_put<MB>(acc, qq, tile);
+        __syncthreads();
+        // 64 rows x 4 groups of 32 columns: 16 half waves per round
+#pragma unroll 1
+        for (int it = (int)(threadIdx.x >> 5); it < 64 * 4; it += kPfThreads / 32) {
+            const int rr = it >> 2, grp = it & 3, j = threadIdx.x & 31;
+            const int row = 64 * qq + rr;
+            const int c = y * kPfGuCols + 32 * grp + j;
+            const bool ok = row < t.nrows && c < p.inter;
+            const float g = tile[rr * kPfEpiLd + 32 * grp + j];
+            const float u = tile[rr * kPfEpiLd + 128 + 32 * grp + j];
+            const float h = ok ? silu_mul_f(g, u) : 0.0f;
+            uint32_t hdr;
+            const int qv = quantize_lanes32(h, hdr);
+            const uint32_t word = pack4_lanes(qv);
+            if (ok) {
+                const int64_t e = t.row0 + row;
+                if ((j & 3) == 0) *(uint32_t*)(p.hq + e * p.inter + c) = word;
+                if (j == 0) p.hd[e * nbh + c / 32] = (uint16_t)(hdr & 0xFFFFu);
+                if (p.dbg_g) {
+                    p.dbg_g[e * p.inter + c] = g;
+                    p.dbg_u[e * p.inter + c] = u;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kPfThreads) void mq_gateup_kernel(MqGuArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMqStages * kMqStage > 64 * kPfEpiLd * 4 ? kMqStages * kMqStage
+                                                                                                 : 64 * kPfEpiLd * 4];
+    static_assert(kMqRows == 128, "the epilogue's quarters of 64 rows cover two of them");
+    Tile t;
+    int y;
+    if (!pf_tile(p.tiles, (p.inter + kPfGuCols - 1) / kPfGuCols, t, y) || t.e < 0 || t.e >= p.nexperts) return;
+    switch ((t.nrows + 31) >> 5) {
+        case 1: mq_gateup_tile<WT, 1>(p, t, y, lds); break;
+        case 2: mq_gateup_tile<WT, 2>(p, t, y, lds); break;
+        case 3: mq_gateup_tile<WT, 3>(p, t, y, lds); break;
+        case 4: mq_gateup_tile<WT, 4>(p, t, y, lds); break;
+        default: break;
+    }
+}
+
+struct MqDownArgs {
+    const uint8_t* wd;
+    int64_t stride;
+    uint32_t expert_bytes;
+    int nexperts, hidden, inter;
+    const int8_t* hq;
+    const uint16_t* hd;
+    uint32_t hq_bytes, hd_bytes;
+    const int32_t* tiles;
+    float* y;
+};
+
+template <int WT, int MB>
+__device__ __forceinline__ void mq_down_tile(const MqDownArgs& p, const Tile& t, int y, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nbh = p.inter / 32;
+    uint32_t q_off, d_off;
+    {
+        const int r = 16 * w + (lane >> 2);
+        q_off = r < t.nrows ? (uint32_t)(t.row0 + r) * (uint32_t)p.inter : p.hq_bytes;
+    }
+    {
+        const int r = 16 * w + (lane & 15);
+        d_off = (lane < 16 && r < t.nrows) ? (uint32_t)(t.row0 + r) * (uint32_t)nbh * 2u : p.hd_bytes;
+    }
+    const int col = y * kPfDownCols + 32 * w + (lane & 31);
+    const uint32_t roff = (uint32_t)(col < p.hidden ? col : p.hidden - 1) * (uint32_t)row_bytes_dev<WT>(p.inter);
+    f32x16 acc[MB];
+    mq_gemm<WT, MB>(make_rsrc(p.hq, p.hq_bytes), make_rsrc(p.hd, p.hd_bytes), q_off, d_off,
+                    make_rsrc_dw(p.wd + (int64_t)t.e * p.stride, p.expert_bytes), roff, p.inter / kPfStepK, lds, acc);
+    if (col < p.hidden) {
+        float* yc = p.y + (int64_t)t.row0 * p.hidden + col;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * m + acc_row(lane, r);
+                if (row < t.nrows) yc[(int64_t)row * p.hidden] = acc[m][r];
+            }
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kPfThreads) void mq_down_kernel(MqDownArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMqStages * kMqStage];
+    Tile t;
+    int y;
+    if (!pf_tile(p.tiles, (p.hidden + kPfDownCols - 1) / kPfDownCols, t, y) || t.e < 0 || t.e >= p.nexperts) return;
+    switch ((t.nrows + 31) >> 5) {
+        case 1: mq_down_tile<WT, 1>(p, t, y, lds); break;
+        case 2: mq_down_tile<WT, 2>(p, t, y, lds); break;
+        case 3: mq_down_tile<WT, 3>(p, t, y, lds); break;
+        case 4: mq_down_tile<WT, 4>(p, t, y, lds); break;
+        default: break;
+    }
+}
+
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
-static int64_t max_tiles_of(int nexperts, int64_t nentries) { return (nentries + kPfRows - 1) / kPfRows + nexperts; }
+static int64_t max_tiles_of(int nexperts, int64_t nentries, int rows = kPfRows) {
+    return (nentries + rows - 1) / rows + nexperts;
+}
 
 struct PfLayout {
     size_t h_off, tiles_off, g_off, u_off, total;
@@ -743,7 +1106,7 @@ extern "C" int qgemm_prefill_experts(int wtype_gu, const void* w_gate, const voi
     if (8 * per_xcd * ny_max > 0x7FFFFFFF) return QMM_EUNSUPPORTED;
 
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, expert_off, nexperts, (int)nentries, tiles,
-                       (int)max_tiles);
+                       (int)max_tiles, kPfRows);
     int rc = launch_status();
     if (rc) return rc;
     {
@@ -823,4 +1186,126 @@ extern "C" int qgemm_dense(int wtype, const void* w, int64_t nrows, int64_t k, c
     else if (wtype == QMM_IQ4_NL) hipLaunchKernelGGL(dense_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
     else hipLaunchKernelGGL(dense_kernel<kF16>, g, dim3(kPfThreads), 0, st, a);
     return launch_status();
+}
+
+// ---------------------------------------------------------------- MMQ-style prefill: entry point
+
+struct MqLayout {
+    size_t xq, xd, hq, hd, tiles, g, u, total;
+};
+static MqLayout mq_layout(int nexperts, int64_t hidden, int64_t inter, int64_t ntok, int64_t nentries, unsigned flags) {
+    MqLayout l;
+    l.xq = 0;
+    l.xd = align16((size_t)ntok * (size_t)hidden);
+    l.hq = align16(l.xd + (size_t)ntok * (size_t)(hidden / 32) * 2);
+    l.hd = align16(l.hq + (size_t)nentries * (size_t)inter);
+    l.tiles = align16(l.hd + (size_t)nentries * (size_t)(inter / 32) * 2);
+    l.g = align16(l.tiles + 4 * (size_t)(1 + 3 * max_tiles_of(nexperts, nentries, kMqRows)));
+    l.u = l.g;
+    l.total = l.g;
+    if (flags & QMM_FLAG_DEBUG_INTERMEDIATES) {
+        l.u = l.g + (size_t)nentries * (size_t)inter * 4;
+        l.total = l.u + (size_t)nentries * (size_t)inter * 4;
+    }
+    return l;
+}
+
+extern "C" size_t qgemm_prefill_experts_q8_workspace(int nexperts, int64_t hidden, int64_t inter, int64_t ntok,
+                                                     int64_t nentries, unsigned flags) {
+    if (nexperts < 1 || hidden < 32 || inter < 32 || ntok < 0 || nentries < 0) return 0;
+    return mq_layout(nexperts, hidden, inter, ntok, nentries, flags).total;
+}
+
+extern "C" int qgemm_prefill_experts_q8(int wtype_gu, const void* w_gate, const void* w_up, int64_t gu_expert_stride,
+                                        int wtype_down, const void* w_down, int64_t down_expert_stride, int nexperts,
+                                        int64_t hidden, int64_t inter, const uint16_t* x_f16, int64_t ntok,
+                                        const int32_t* sorted_tok, const int32_t* expert_off, int64_t nentries,
+                                        float* y, void* ws, size_t ws_bytes, unsigned flags, void* stream) {
+    if (!valid_wtype(wtype_gu) || !valid_wtype(wtype_down)) return QMM_EINVAL;
+    if (!w_gate || !w_up || !w_down || !x_f16 || !sorted_tok || !expert_off || !y || !ws) return QMM_EINVAL;
+    if (nexperts < 1 || hidden < 32 || inter < 32 || ntok < 1 || nentries < 0) return QMM_EINVAL;
+    if (qmm_row_bytes(wtype_gu, hidden) == 0 || qmm_row_bytes(wtype_down, inter) == 0) return QMM_EINVAL;
+    if (wtype_gu == QMM_CB3 || wtype_down == QMM_CB3) return QMM_EUNSUPPORTED;
+    if (hidden % kPfStepK || inter % kPfStepK) return QMM_EUNSUPPORTED;
+    const int64_t gu_bytes = inter * qmm_row_bytes(wtype_gu, hidden);
+    const int64_t d_bytes = hidden * qmm_row_bytes(wtype_down, inter);
+    if (gu_expert_stride < gu_bytes || down_expert_stride < d_bytes) return QMM_EINVAL;
+    if (gu_expert_stride % 4 || down_expert_stride % 4) return QMM_EALIGN;
+    if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(x_f16, 4) || !aligned(y, 4) ||
+        !aligned(ws, 16))
+        return QMM_EALIGN;
+    // planes read at their end plus up to a row of values (or of scales) must not wrap 4 GiB
+    if ((uint64_t)ntok * hidden + (uint64_t)hidden + 64 > kMaxBufferBytes ||
+        (uint64_t)nentries * inter + (uint64_t)inter + 64 > kMaxBufferBytes || gu_bytes > (int64_t)kMaxBufferBytes ||
+        d_bytes > (int64_t)kMaxBufferBytes || nentries > 0x7FFFFFFF || hidden > kMaxK || inter > kMaxK)
+        return QMM_EUNSUPPORTED;
+    const MqLayout lay = mq_layout(nexperts, hidden, inter, ntok, nentries, flags);
+    if (ws_bytes < lay.total) return QMM_ESPACE;
+    if (nentries == 0) return QMM_OK;
+    const hipStream_t st = as_stream(stream);
+    uint8_t* wsb = (uint8_t*)ws;
+    int8_t* xq = (int8_t*)(wsb + lay.xq);
+    uint16_t* xd = (uint16_t*)(wsb + lay.xd);
+    int8_t* hq = (int8_t*)(wsb + lay.hq);
+    uint16_t* hd = (uint16_t*)(wsb + lay.hd);
+    int32_t* tiles = (int32_t*)(wsb + lay.tiles);
+    const int64_t max_tiles = max_tiles_of(nexperts, nentries, kMqRows);
+    const int64_t per_xcd = (max_tiles + 7) / 8;
+    const int64_t ny_max = std::max((inter + kPfGuCols - 1) / kPfGuCols, (hidden + kPfDownCols - 1) / kPfDownCols);
+    if (8 * per_xcd * ny_max > 0x7FFFFFFF) return QMM_EUNSUPPORTED;
+
+    const int64_t xblocks = ntok * (hidden / 32);
+    hipLaunchKernelGGL(quantize_planes_kernel, dim3((unsigned)((xblocks * 32 + 255) / 256)), dim3(256), 0, st, x_f16,
+                       xblocks, xq, xd);
+    int rc = launch_status();
+    if (rc) return rc;
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, expert_off, nexperts, (int)nentries, tiles,
+                       (int)max_tiles, kMqRows);
+    rc = launch_status();
+    if (rc) return rc;
+    {
+        MqGuArgs a;
+        a.wg = (const uint8_t*)w_gate;
+        a.wu = (const uint8_t*)w_up;
+        a.stride = gu_expert_stride;
+        a.expert_bytes = (uint32_t)gu_bytes;
+        a.nexperts = nexperts;
+        a.hidden = (int)hidden;
+        a.inter = (int)inter;
+        a.ntok = (int)ntok;
+        a.xq = xq;
+        a.xd = xd;
+        a.xq_bytes = (uint32_t)(ntok * hidden);
+        a.xd_bytes = (uint32_t)(ntok * (hidden / 32) * 2);
+        a.sorted_tok = sorted_tok;
+        a.tiles = tiles;
+        a.hq = hq;
+        a.hd = hd;
+        a.dbg_g = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.g) : nullptr;
+        a.dbg_u = (flags & QMM_FLAG_DEBUG_INTERMEDIATES) ? (float*)(wsb + lay.u) : nullptr;
+        const dim3 g((unsigned)(8 * per_xcd * ((inter + kPfGuCols - 1) / kPfGuCols)));
+        if (wtype_gu == QMM_Q8_0) hipLaunchKernelGGL(mq_gateup_kernel<kQ8_0>, g, dim3(kPfThreads), 0, st, a);
+        else hipLaunchKernelGGL(mq_gateup_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
+        rc = launch_status();
+        if (rc) return rc;
+    }
+    {
+        MqDownArgs a;
+        a.wd = (const uint8_t*)w_down;
+        a.stride = down_expert_stride;
+        a.expert_bytes = (uint32_t)d_bytes;
+        a.nexperts = nexperts;
+        a.hidden = (int)hidden;
+        a.inter = (int)inter;
+        a.hq = hq;
+        a.hd = hd;
+        a.hq_bytes = (uint32_t)(nentries * inter);
+        a.hd_bytes = (uint32_t)(nentries * (inter / 32) * 2);
+        a.tiles = tiles;
+        a.y = y;
+        const dim3 g((unsigned)(8 * per_xcd * ((hidden + kPfDownCols - 1) / kPfDownCols)));
+        if (wtype_down == QMM_Q8_0) hipLaunchKernelGGL(mq_down_kernel<kQ8_0>, g, dim3(kPfThreads), 0, st, a);
+        else hipLaunchKernelGGL(mq_down_kernel<kIQ4_NL>, g, dim3(kPfThreads), 0, st, a);
+        return launch_status();
+    }
 }

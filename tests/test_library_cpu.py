@@ -274,3 +274,16 @@ def test_dense_rejects():
     assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2560, A16, 8, A16, 63, None) == -1     # ldy < nrows
     assert L.qgemm_dense(M.QMM_Q8_0, A16, 64, 2560, A16, 0, A16, 64, None) == 0      # no tokens
     assert M.row_bytes(M.QMM_F16, 2560) == 5120
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(wtype_down=9), -1),
+    (dict(wtype_gu=M.QMM_CB3, gu_stride=1024 * 1100), -2),    # no codebook argument
+    (dict(hidden=2560 + 32), -2),                              # K steps of 64
+    (dict(ws_bytes=64), -5),
+    (dict(nentries=0, ws_bytes=1 << 30), 0),                   # nothing to do: no launch
+    (dict(ntok=1677722), -2),                                  # token planes of 4 GiB or more
+])
+def test_mmq_rejects(kw, expect):
+    assert M.lib().qgemm_prefill_experts_q8(*_pf_args(**kw)) == expect
+    assert M.lib().qgemm_prefill_experts_q8_workspace(4, 2560, 1024, 64, 128, 0) >= 64 * 2560 + 128 * 1024
