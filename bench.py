@@ -207,23 +207,28 @@ def fused_bytes(wtype, nrows, k, n):
 
 def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
     """The same cold rotation read by the library's plain streaming-read kernel (one launch per
-    copy, no compute): the best per-launch time over a few grid sizes, the reference for what
-    one launch reading this many bytes can reach."""
+    copy, no compute): the best per-launch time over a sweep of launch shapes (workgroups, their
+    size, loads in flight per thread), the reference for what one launch reading this many bytes
+    can reach."""
     n16 = nbytes // 16 * 16
     best = None
-    for grid in (256, 512, 1024, 2048):
-        out = torch.empty(grid * 256, dtype=torch.int32, device=copies[0].device)
+    for threads, unroll in ((256, 4), (256, 8), (512, 4), (512, 8), (1024, 4), (256, 16)):
+        for grid in (256, 512, 1024, 2048):
+            if grid * threads * unroll * 16 > 8 * n16:
+                continue
+            out = torch.empty(grid * threads, dtype=torch.int32, device=copies[0].device)
 
-        def batch():
-            for w in copies:
-                M.qmm_debug_stream_read(w, n16, grid, out=out)
-        t = timed_graph(torch, batch, reps, use_graph) * 1e3 / len(copies)
-        if best is None or t < best[0]:
-            best = (t, grid)
-    us, grid = best
+            def batch():
+                for w in copies:
+                    M.qmm_debug_stream_read(w, n16, grid, threads=threads, unroll=unroll, out=out)
+            t = timed_graph(torch, batch, reps, use_graph) * 1e3 / len(copies)
+            if best is None or t < best[0]:
+                best = (t, grid, threads, unroll)
+    us, grid, threads, unroll = best
     gbps = n16 / (us * 1e-6) / 1e9
     return {"bytes": n16, "us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBS, 4),
-            "grid": grid, "kernel": "qmm_debug_stream_read (16-byte loads, 8 in flight per thread)"}
+            "grid": grid, "threads": threads, "unroll": unroll,
+            "kernel": "stream_read_kernel (16-byte raw-buffer loads, contiguous runs per workgroup), best launch shape"}
 
 
 def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndistinct=6, cpu=True, cpu_s=10.0):

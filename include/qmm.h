@@ -127,14 +127,16 @@ int qgemv_dense_f32(int wtype, const void* w, const uint8_t* grid, int64_t nrows
 int qmm_debug_block_sums(int wtype, const void* w, const uint8_t* grid, int64_t nrows, int64_t k,
                          const void* xq, int ncols, int32_t* sums, void* stream);
 
-/* Measurement hook: a plain streaming read of nbytes from p in one launch of `grid`
- * workgroups of 256 threads (16-byte loads, eight in flight per thread, no other work): the
- * reference for the HBM time of the decode kernels at the same byte count.  Thread t writes the
- * XOR of the words it read to out[t].
- *   p    : device, 16-byte aligned; nbytes a multiple of 16.
- *   out  : device uint32 [grid * 256], 4-byte aligned.
- * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EHIP. */
-int qmm_debug_stream_read(const void* p, uint64_t nbytes, uint32_t* out, int grid, void* stream);
+/* Measurement hook: a plain streaming read of nbytes from p in one launch of `grid` workgroups
+ * of `threads` threads (256, 512 or 1024): workgroup w reads the w-th of grid contiguous runs,
+ * `unroll` (4, 8 or 16) 16-byte raw-buffer loads in flight per thread, no other work.  The
+ * reference for the HBM time of the decode kernels at the same byte count.  Thread t of
+ * workgroup w writes the XOR of the words it read to out[w * threads + t].
+ *   p    : device, 16-byte aligned; nbytes a multiple of 16, below 4 GiB.
+ *   out  : device uint32 [grid * threads], 4-byte aligned.
+ * Errors: QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED (other threads / unroll), QMM_EHIP. */
+int qmm_debug_stream_read(const void* p, uint64_t nbytes, uint32_t* out, int grid, int threads,
+                          int unroll, void* stream);
 
 /* Measurement hook: `grid` workgroups of 256 threads, each wave running 8 independent fp16 MFMA
  * accumulators (v_mfma_f32_32x32x16_f16, 32768 FLOP each) for `iters` rounds from registers

@@ -38,7 +38,7 @@ SIGNATURES = {
     "qgemv_dense": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qgemv_dense_f32": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "qmm_debug_block_sums": (_I32, [_I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
-    "qmm_debug_stream_read": (_I32, [_P, _U64, _P, _I32, _P]),
+    "qmm_debug_stream_read": (_I32, [_P, _U64, _P, _I32, _I32, _I32, _P]),
     "qmm_debug_mfma_loop": (_I32, [_P, _I32, _I32, _P]),
     "qgemv_grouped_experts_workspace": (_SZ, [_I64, _I32, _U32]),
     "qgemv_grouped_experts": (_I32, [_I32, _P, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _I32,
@@ -244,15 +244,16 @@ def qmm_debug_block_sums(wtype, w, nrows, k, xq, ncols, grid=None, out=None, str
     return out
 
 
-def qmm_debug_stream_read(p, nbytes, grid, out=None, stream=None):
+def qmm_debug_stream_read(p, nbytes, grid, threads=256, unroll=8, out=None, stream=None):
     """Plain streaming read of the first nbytes of device tensor p in one launch of `grid`
-    256-thread workgroups (the HBM reference); returns out (uint32 [grid * 256])."""
+    workgroups of `threads` threads, `unroll` 16-byte loads in flight per thread, contiguous runs
+    per workgroup (the HBM reference); returns out (uint32 [grid * threads])."""
     import torch
     if grid < 1:
         raise ValueError("grid must be positive")
     _need(p, "p", "u8", nbytes)
-    out = _out(out, "out", "i32", grid * 256 * 4, p.device, (grid * 256,), torch.int32)
-    _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid,
+    out = _out(out, "out", "i32", grid * threads * 4, p.device, (grid * threads,), torch.int32)
+    _check("qmm_debug_stream_read", lib().qmm_debug_stream_read(_ptr(p), nbytes, _ptr(out), grid, threads, unroll,
                                                                _stream(stream, p.device)))
     return out
 

@@ -204,21 +204,23 @@ def test_ldy_padding():
     check_tol(yh[:, :50], ref, a)
 
 
-def test_stream_read_reference():
-    """The streaming-read reference kernel reads every 16-byte chunk once: thread t's word is the
-    XOR of the chunks t, t + T, t + 2T, ... (T = grid * 256 threads)."""
-    import torch
-    print("stream read reference", flush=True)
+@pytest.mark.parametrize("threads,unroll", [(256, 8), (512, 4), (1024, 16)])
+def test_stream_read_reference(threads, unroll):
+    """The streaming-read reference kernel reads every 16-byte chunk once: thread t of workgroup
+    w XORs chunks w R + t, w R + t + threads, ... of its run of R = ceil(chunks / grid)."""
+    print(f"stream read reference threads={threads} unroll={unroll}", flush=True)
     rng = np.random.default_rng(5)
     nbytes, grid = 3 * 65536 + 48, 3
     buf = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
-    out = host(M.qmm_debug_stream_read(dev(buf), nbytes, grid)).view(np.uint32)
+    out = host(M.qmm_debug_stream_read(dev(buf), nbytes, grid, threads=threads, unroll=unroll)).view(np.uint32)
     words = buf.view(np.uint32).reshape(-1, 4)
     chunk = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
-    nt = grid * 256
-    ref = np.zeros(nt, np.uint32)
-    for t in range(nt):
-        ref[t] = np.bitwise_xor.reduce(chunk[t::nt]) if t < chunk.size else 0
+    run = -(-chunk.size // grid)
+    ref = np.zeros(grid * threads, np.uint32)
+    for w in range(grid):
+        seg = chunk[w * run:(w + 1) * run]
+        for t in range(threads):
+            ref[w * threads + t] = np.bitwise_xor.reduce(seg[t::threads]) if t < seg.size else 0
     assert np.array_equal(out, ref)
 
 
