@@ -50,7 +50,10 @@ DIGEST_SOURCES = {
     "gemv": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_gemv.hip"),
     "grouped": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_grouped.hip"),
     "prefill": ("qmm_host.h", "qmm_device.h", "qmm_gemv.h", "qmm_prefill.hip"),
+    "combine": ("qmm_host.h", "qmm_device.h", "qmm_combine.hip"),
 }
+DIGEST_SOURCES["q8_0"] = DIGEST_SOURCES["planes"] = DIGEST_SOURCES["gemv"]
+DIGEST_SOURCES["dense"] = DIGEST_SOURCES["mmq"] = DIGEST_SOURCES["prefill"]
 
 
 def source_digest(files=None):
@@ -567,39 +570,54 @@ def combine_bytes(ntok, topk, hidden):
     return ntok * topk * hidden * 4 + ntok * topk * 8 + ntok * hidden * 4
 
 
+COMBINE_SHAPES = (("prefill_8192tok_top8", 8192, 8, None), ("decode_8tok_top16", 8, 16, 128))
+
+
+def combine_setup(torch, M, rng, ntok, topk, nrows, hidden=2560):
+    """Inputs of one combine workload: expert rows y, the tokens' row indices and router weights
+    (the prefill shape's indices from its sorted routing, the decode shape's token-major);
+    returns (call, host index, host weights, y)."""
+    import synth
+    dev = torch.device("cuda", 0)
+    if nrows is None:
+        st, _ = synth.prefill_routing(rng, ntok, 128, topk)
+        idx = synth.token_positions(st, ntok, topk)
+        nrows = st.size
+    else:
+        idx = (np.arange(topk)[None, :] * ntok + np.arange(ntok)[:, None]).astype(np.int32)
+    y = torch.randn((nrows, hidden), dtype=torch.float32, device=dev)
+    w = synth.router_weights(rng, ntok, topk)
+    di, dw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+    out = torch.empty((ntok, hidden), dtype=torch.float32, device=dev)
+    return (lambda: M.qmm_moe_combine(y, di, dw, out=out)), idx, w, y
+
+
 def bench_combine(args, torch, M, cpu_s=3.0):
     """MoE combine on the prefill workload (8192 tokens, top-8 of 128, hidden 2560: the sorted
     entry rows are 671 MB, over twice the memory-side cache, so every call reads them from HBM)
     and on the decode shape (8 tokens x 16 experts)."""
     import oracle
     import synth
-    dev = torch.device("cuda", 0)
     rng = synth.rng_for(synth.SEEDS["prefill"] + 10)
     res = {}
-    for name, ntok, topk, nrows in (("prefill_8192tok_top8", 8192, 8, None), ("decode_8tok_top16", 8, 16, 128)):
+    for name, ntok, topk, nrows in COMBINE_SHAPES:
         hidden = 2560
-        if nrows is None:
-            st, _ = synth.prefill_routing(rng, ntok, 128, topk)
-            idx = synth.token_positions(st, ntok, topk)
-            nrows = st.size
-        else:
-            idx = (np.arange(topk)[None, :] * ntok + np.arange(ntok)[:, None]).astype(np.int32)
-        y = torch.randn((nrows, hidden), dtype=torch.float32, device=dev)
-        w = synth.router_weights(rng, ntok, topk)
-        di, dw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
-        out = torch.empty((ntok, hidden), dtype=torch.float32, device=dev)
+        call, idx, w, y = combine_setup(torch, M, rng, ntok, topk, nrows, hidden)
+        nrows = y.shape[0]
         # calls per graph: a replay of one graph per short call would time the host's replay rate
         per = 1 if ntok > 64 else 100
 
         def calls():
             for _ in range(per):
-                M.qmm_moe_combine(y, di, dw, out=out)
+                call()
         ms = timed_graph(torch, calls, 10, not args.no_graph) / per
         b = combine_bytes(ntok, topk, hidden)
         gbps = b / (ms * 1e-3) / 1e9
+        rec = recorded_traffic("combine")
         r = {"us_per_call": round(ms * 1e3, 3), "gbps": round(gbps, 1),
              "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbps / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": b,
+                          "traffic": rec["bytes_per_launch"].get(name) if rec else None,
                           "kernel": "combine_kernel"},
              "workload": f"{ntok} tokens x top-{topk}, hidden {hidden}, {nrows} rows of y ({nrows * hidden * 4 / 1e6:.0f} MB)"}
         if not args.no_cpu:
@@ -612,30 +630,56 @@ def bench_combine(args, torch, M, cpu_s=3.0):
     return res
 
 
+def dense_specs():
+    """The dense projections' matrices: (weight type, rows, seed key); K = 2560."""
+    import synth
+    return ((synth.IQ4_NL, 8192, "iq4nl_8192x2560"), (synth.Q8_0, 12288, "q8_0_12288x2560"))
+
+
+def dense_tokens(torch, ntok, k):
+    """The prompt tokens of the dense projections (binary16), host and device."""
+    import synth
+    x16 = synth.prefill_tokens(synth.rng_for(synth.SEEDS["prefill"] + 20), ntok, k)
+    return x16, torch.from_numpy(x16.view(np.uint16)).to(torch.device("cuda", 0))
+
+
+def dense_name(wt, nrows, k):
+    import synth
+    return f"{'iq4_nl' if wt == synth.IQ4_NL else 'q8_0'}_{nrows}x{k}_8192tok"
+
+
+def dense_setup(torch, M, wt, nrows, k, key, xd):
+    """Weights and output of one dense projection; returns (host weights, device weights, y,
+    the fused call)."""
+    import synth
+    dev = torch.device("cuda", 0)
+    w = synth.weights(wt, synth.rng_for(synth.SEEDS[key]), nrows, k)
+    wd = torch.from_numpy(w).to(dev)
+    y = torch.empty((xd.shape[0], nrows), dtype=torch.float32, device=dev)
+    return w, wd, y, (lambda: M.qgemm_dense(wt, wd, nrows, k, xd, y=y))
+
+
 def bench_dense(args, torch, M, cpu_s=3.0):
     """Dense prompt projections: 8192 prompt tokens through the decode workloads' matrices
     (IQ4_NL 8192 x 2560 and Q8_0 12288 x 2560), fused (weights converted to FP16 inside the
     GEMM) and in two steps (qmm_dequant_f16 with 16-byte stores, then the GEMM on FP16 weights)."""
     import oracle
     import synth
-    dev = torch.device("cuda", 0)
     ntok, k = 8192, 2560
-    x16 = synth.prefill_tokens(synth.rng_for(synth.SEEDS["prefill"] + 20), ntok, k)
-    xd = torch.from_numpy(x16.view(np.uint16)).to(dev)
+    x16, xd = dense_tokens(torch, ntok, k)
     res = {}
-    for wt, nrows, key in ((synth.IQ4_NL, 8192, "iq4nl_8192x2560"), (synth.Q8_0, 12288, "q8_0_12288x2560")):
-        w = synth.weights(wt, synth.rng_for(synth.SEEDS[key]), nrows, k)
-        wd = torch.from_numpy(w).to(dev)
-        w16 = torch.empty((nrows, k), dtype=torch.float16, device=dev)
-        y = torch.empty((ntok, nrows), dtype=torch.float32, device=dev)
+    for wt, nrows, key in dense_specs():
+        w, wd, y, fused_call = dense_setup(torch, M, wt, nrows, k, key, xd)
+        w16 = torch.empty((nrows, k), dtype=torch.float16, device=wd.device)
         g = not args.no_graph
-        fused = timed_graph(torch, lambda: M.qgemm_dense(wt, wd, nrows, k, xd, y=y), 10, g)
+        fused = timed_graph(torch, fused_call, 10, g)
         deq = timed_graph(torch, lambda: M.qmm_dequant_f16(wt, wd, nrows, k, out=w16), 50, g)
         f16 = timed_graph(torch, lambda: M.qgemm_dense(M.QMM_F16, w16, nrows, k, xd, y=y), 10, g)
         flops = 2.0 * ntok * nrows * k
         tf = flops / (fused * 1e-3) / 1e12
         deq_bytes = nrows * synth.row_bytes(wt, k) + nrows * k * 2
-        name = f"{'iq4_nl' if wt == synth.IQ4_NL else 'q8_0'}_{nrows}x{k}_8192tok"
+        name = dense_name(wt, nrows, k)
+        rec = recorded_traffic("dense")
         r = {"us_per_call": round(fused * 1e3, 2), "tflops": round(tf, 1),
              "two_step": {"dequant_us": round(deq * 1e3, 2), "dequant_gbps": round(deq_bytes / (deq * 1e-3) / 1e9, 1),
                           "f16_gemm_us": round(f16 * 1e3, 2),
@@ -643,6 +687,7 @@ def bench_dense(args, torch, M, cpu_s=3.0):
                           "total_us": round((deq + f16) * 1e3, 2)},
              "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                          "traffic": rec["bytes_per_launch"].get(name) if rec else None,
                           "kernel": "dense_kernel (weights converted to FP16 in registers, fp16 MFMA 32x32x16)"},
              "workload": f"8192 tokens x {nrows}x{k} {'IQ4_NL' if wt == synth.IQ4_NL else 'Q8_0'}"}
         if not args.no_cpu:
@@ -656,6 +701,14 @@ def bench_dense(args, torch, M, cpu_s=3.0):
     return res
 
 
+def planes_specs():
+    """The planes GEMVs: (weight type, rows, K, column counts, seed key)."""
+    import synth
+    return ((synth.IQ4_NL, 8192, 2560, (1, 4, 8), "iq4nl_8192x2560"),
+            (synth.Q8_0, 12288, 2560, (1, 2, 4), "q8_0_12288x2560"),
+            (synth.Q8_0, 2560, 6144, (7, 8), "q8_0_2560x6144"))
+
+
 def bench_planes(args, torch, M):
     """The decode GEMVs on weight planes against the same GEMVs on the GGUF blocks, each over a
     cold rotation of copies, in the same run; plus the time of one repack."""
@@ -663,9 +716,7 @@ def bench_planes(args, torch, M):
     dev = torch.device("cuda", 0)
     res = {}
     g = not args.no_graph
-    for wt, nrows, k, cols, key in ((synth.IQ4_NL, 8192, 2560, (1, 4, 8), "iq4nl_8192x2560"),
-                                    (synth.Q8_0, 12288, 2560, (1, 2, 4), "q8_0_12288x2560"),
-                                    (synth.Q8_0, 2560, 6144, (7, 8), "q8_0_2560x6144")):
+    for wt, nrows, k, cols, key in planes_specs():
         wbytes = nrows * synth.row_bytes(wt, k)
         host_w = [synth.weights(wt, synth.rng_for(synth.SEEDS[key] + i), nrows, k) for i in range(6)]
         nc = cold_copies(wbytes)
@@ -690,8 +741,12 @@ def bench_planes(args, torch, M):
             tot_b += b
             tot_t += tp
         ach = tot_b / (tot_t * 1e-6) / 1e9
+        rec = recorded_traffic(f"planes:{wt}:{nrows}x{k}")
         r["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": f"gemv_kernel on planes, columns {list(cols)}"}
+                         "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": round(tot_b / len(cols)),
+                         "traffic": round(sum(rec["bytes_per_launch"][str(n)] for n in cols) / len(cols)) if rec else None,
+                         "kernel": f"gemv_kernel on planes, columns {list(cols)}"}
         res[f"{'iq4_nl' if wt == synth.IQ4_NL else 'q8_0'}_{nrows}x{k}"] = r
         del blocks, planes
         torch.cuda.empty_cache()
@@ -702,10 +757,9 @@ INT8_MFMA_PEAK_TOPS = 5000.0
 VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9     # non-packed binary32 VALU lane operations per second
 
 
-def bench_mmq(args, torch, M, cpu_s=3.0):
-    """The MMQ-style prefill (int8 MFMA on q8_1 activations, SwiGLU + q8_1 of H fused) on the
-    prefill workload, beside the FP16 path on the same inputs."""
-    import oracle
+def mmq_setup(torch, M):
+    """The prefill workload's inputs with the MMQ-style call beside the FP16 one; returns
+    (MMQ call, FP16 call, host data, sizes)."""
     import synth
     call, h, z = prefill_setup(torch, M)
     nexp, hidden, inter, nent, ntok = z["nexp"], z["hidden"], z["inter"], z["nent"], z["ntok"]
@@ -717,6 +771,16 @@ def bench_mmq(args, torch, M, cpu_s=3.0):
     def mmq():
         M.qgemm_prefill_experts_q8(synth.IQ4_NL, d["wg"], d["wu"], synth.Q8_0, d["wd"], nexp, hidden, inter, d["x"],
                                    d["st"], d["off"], y=y, ws=ws)
+    return mmq, call, h, z
+
+
+def bench_mmq(args, torch, M, cpu_s=3.0):
+    """The MMQ-style prefill (int8 MFMA on q8_1 activations, SwiGLU + q8_1 of H fused) on the
+    prefill workload, beside the FP16 path on the same inputs."""
+    import oracle
+    import synth
+    mmq, call, h, z = mmq_setup(torch, M)
+    nexp, hidden, inter, nent = z["nexp"], z["hidden"], z["inter"], z["nent"]
     g = not args.no_graph
     ms = timed_graph(torch, mmq, max(args.steps, 5), g)
     ms_f16 = timed_graph(torch, call, max(args.steps, 5), g)
@@ -724,11 +788,13 @@ def bench_mmq(args, torch, M, cpu_s=3.0):
     tops = flops / (ms * 1e-3) / 1e12
     # the per-block rescale: one conversion and one fma per output and 32-value block
     valu_ops = 2.0 * nent * (2 * inter * (hidden // 32) + hidden * (inter // 32))
+    rec = recorded_traffic("mmq")
     r = {"us_per_call": round(ms * 1e3, 2), "tops": round(tops, 1),
          "fp16_path_us_per_call": round(ms_f16 * 1e3, 2),
          "valu_floor_us": round(valu_ops / VALU_LANE_OPS_PEAK * 1e6, 1),
          "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOP/s",
                       "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_call": flops,
+                      "traffic": rec["bytes_per_launch"]["call"] if rec else None,
                       "kernel": "quantize_planes + schedule + mq_gateup_kernel + mq_down_kernel (one call)"},
          "workload": "prefill 8192 tokens x 2560, top-8 of 128 experts, IQ4_NL gate/up, Q8_0 down; q8_1 activations, "
                      "int8 MFMA, fp32 MFMA for the block scale products"}
@@ -787,7 +853,9 @@ def pmc_probe(torch, M, workload):
     """Three plain device copies of CALIB_BYTES, then one cold pass of `workload` with no graphs,
     so that every launch is a dispatch of its own: the headline GEMV once per weight copy at 1, 4
     and 8 columns (the Q8_0 GEMVs likewise at their column counts); the grouped decode once per
-    rotation slot at m = 1, 4, 8; the prefill call twice."""
+    rotation slot at m = 1, 4, 8; the prefill call twice (FP16 or MMQ-style); the prefill-shape
+    combine three times; each dense projection twice; the planes GEMVs once per weight copy at
+    their column counts."""
     import synth
     dev = torch.device("cuda", 0)
     if workload == "gemv":
@@ -839,6 +907,43 @@ def pmc_probe(torch, M, workload):
         def run():
             call()
             call()
+    elif workload == "mmq":
+        call = mmq_setup(torch, M)[0]
+
+        def run():
+            call()
+            call()
+    elif workload == "combine":
+        _, ntok, topk, nrows = COMBINE_SHAPES[0]
+        call = combine_setup(torch, M, synth.rng_for(synth.SEEDS["prefill"] + 10), ntok, topk, nrows)[0]
+
+        def run():
+            for _ in range(3):
+                call()
+    elif workload == "dense":
+        _, xd = dense_tokens(torch, 8192, 2560)
+        calls = [dense_setup(torch, M, wt, nrows, 2560, key, xd)[3] for wt, nrows, key in dense_specs()]
+
+        def run():
+            for c in calls:
+                c()
+                c()
+    elif workload == "planes":
+        sets = []
+        for wt, nrows, k, cols, key in planes_specs():
+            host = [synth.weights(wt, synth.rng_for(synth.SEEDS[key] + i), nrows, k) for i in range(6)]
+            planes = [M.qmm_pack_planes(wt, torch.from_numpy(host[i % 6]).to(dev), nrows, k)
+                      for i in range(cold_copies(nrows * synth.row_bytes(wt, k)))]
+            xs = synth.activations(synth.rng_for(synth.SEEDS[key] + 100), max(cols), k)
+            xq = {n: M.qmm_quantize_q8_1(torch.from_numpy(xs[:n].copy()).to(dev)) for n in cols}
+            y = torch.empty((max(cols), nrows), dtype=torch.float32, device=dev)
+            sets.append((wt, nrows, k, cols, planes, xq, y))
+
+        def run():
+            for wt, nrows, k, cols, planes, xq, y in sets:
+                for n in cols:
+                    for p in planes:
+                        M.qgemv_planes(wt, p, nrows, k, xq[n], n, y=y)
     else:
         raise SystemExit(f"no counter probe for workload {workload}")
     src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -862,7 +967,11 @@ def pmc_summary(workload, fetch_csv, write_csv):
     pattern = {"gemv": r"gemv_f32_kernel<\d+, \d+, (\d+),|gemv_kernel<\d+, false, (\d+),",
                "q8_0": r"gemv_kernel<\d+, false, (\d+),",
                "grouped": r"(gu_kernel|down_kernel)",
-               "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)"}[workload]
+               "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)",
+               "planes": r"gemv_kernel<[45], false, (\d+),",
+               "combine": r"(combine_kernel)",
+               "dense": r"(dense_kernel)",
+               "mmq": r"(quantize_planes_kernel|schedule_kernel|mq_gateup_kernel|mq_down_kernel)"}[workload]
 
     def tag(name):   # the first group the pattern matched: column count or kernel name
         return next(g for g in re.search(pattern, name).groups() if g is not None)
@@ -887,24 +996,30 @@ def pmc_summary(workload, fetch_csv, write_csv):
         return sum(v) / len(v)
 
     rec = {"fetch_scale": round(ff, 4), "write_scale": round(wf, 4), "calibration_bytes": CALIB_BYTES}
-    if workload == "q8_0":
+    if workload in ("q8_0", "planes"):
         # dispatch order: per matrix, per column count, one launch per weight copy
+        if workload == "q8_0":
+            specs, prefix = [(synth.Q8_0, nrows, k, cols) for nrows, k, cols, _ in Q8_SPECS], "gemv"
+        else:
+            specs, prefix = [sp[:4] for sp in planes_specs()], "planes"
         i = 0
-        for nrows, k, cols, _ in Q8_SPECS:
-            nc = cold_copies(nrows * synth.row_bytes(synth.Q8_0, k))
+        for wt, nrows, k, cols in specs:
+            nc = cold_copies(nrows * synth.row_bytes(wt, k))
             r = dict(rec)
             fetch, write = {}, {}
             for n in cols:
+                if len({g for g, _ in fk[i:i + nc]}) != 1:   # one kernel (pass width) per column count
+                    raise SystemExit(f"dispatch order: expected {nc} launches of one kernel for {n} columns at {i}")
                 fetch[n] = mean([v for _, v in fk[i:i + nc]])
                 write[n] = mean([v for _, v in wk[i:i + nc]])
                 i += nc
-            r["algorithmic_bytes"] = {str(n): gemv_bytes(synth.Q8_0, nrows, k, n) for n in cols}
+            r["algorithmic_bytes"] = {str(n): gemv_bytes(wt, nrows, k, n) for n in cols}
             r["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
             r["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
             r["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in cols}
-            r["sources"] = list(DIGEST_SOURCES["gemv"])
+            r["sources"] = list(DIGEST_SOURCES[workload])
             r["source_sha256"] = source_digest(r["sources"])
-            store_traffic(f"gemv:{synth.Q8_0}:{nrows}x{k}", r)
+            store_traffic(f"{prefix}:{wt}:{nrows}x{k}", r)
         if i != len(fk) or len(fk) != len(wk):
             raise SystemExit(f"expected {i} GEMV dispatches, found {len(fk)} / {len(wk)}")
         return
@@ -923,24 +1038,44 @@ def pmc_summary(workload, fetch_csv, write_csv):
             return {m: mean(per_call[i * c:(i + 1) * c]) for i, m in enumerate(GROUPED_M)}
         fetch, write = by_m(fk), by_m(wk)
         key = "grouped"
+    elif workload == "combine":
+        # three launches of the prefill-shape combine
+        name, ntok, topk, _ = COMBINE_SHAPES[0]
+        fetch, write = {name: mean([v for _, v in fk])}, {name: mean([v for _, v in wk])}
+        rec["algorithmic_bytes"] = {name: combine_bytes(ntok, topk, 2560)}
+        key = "combine"
+    elif workload == "dense":
+        # two launches per matrix, in the order of dense_specs()
+        fetch, write = {}, {}
+        rec["flops"] = {}
+        for j, (wt, nrows, _) in enumerate(dense_specs()):
+            name = dense_name(wt, nrows, 2560)
+            fetch[name] = mean([v for _, v in fk[2 * j:2 * j + 2]])
+            write[name] = mean([v for _, v in wk[2 * j:2 * j + 2]])
+            rec["flops"][name] = 2 * 8192 * nrows * 2560
+        key = "dense"
     else:
+        last = "pf_down_kernel" if workload == "prefill" else "mq_down_kernel"
+
         def per_call(lst):
             calls, cur = [], 0.0
             for g, v in lst:
                 cur += v
-                if g == "pf_down_kernel":
+                if g == last:
                     calls.append(cur)
                     cur = 0.0
             return {"call": mean(calls[1:] or calls)}
         fetch, write = per_call(fk), per_call(wk)
-        for name in ("pf_gateup_kernel", "pf_down_kernel"):
+        names = (("pf_gateup_kernel", "pf_down_kernel") if workload == "prefill"
+                 else ("quantize_planes_kernel", "mq_gateup_kernel", "mq_down_kernel"))
+        for name in names:
             rec[f"{name}_bytes"] = round((mean([v for g, v in fk if g == name]) * ff
                                           + mean([v for g, v in wk if g == name]) * wf) * 1024)
-        key = "prefill"
+        key = workload
     rec["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
     rec["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
     rec["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in fetch}
-    rec["sources"] = list(DIGEST_SOURCES["gemv" if workload == "gemv" else workload])
+    rec["sources"] = list(DIGEST_SOURCES[workload])
     rec["source_sha256"] = source_digest(rec["sources"])
     store_traffic(key, rec)
 
@@ -963,7 +1098,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill", "next", "mmq"],
+                    choices=["all", "gemv", "tiny", "q8_0", "grouped", "prefill", "next", "mmq", "combine", "dense",
+                             "planes"],
                     help="all (default): the headline GEMV line with every other workload under 'configs'")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -1013,6 +1149,9 @@ def main() -> int:
         print(json.dumps(next_rows(args, torch, M)), flush=True)
     elif args.workload == "mmq":
         print(json.dumps(bench_mmq(args, torch, M)), flush=True)
+    elif args.workload in ("combine", "dense", "planes"):
+        fn = {"combine": bench_combine, "dense": bench_dense, "planes": bench_planes}[args.workload]
+        print(json.dumps(fn(args, torch, M)), flush=True)
     else:
         print(json.dumps(bench_prefill(args, torch, M)), flush=True)
     return 0

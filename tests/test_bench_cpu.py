@@ -80,6 +80,48 @@ def test_gemv_summary_and_lookup(tmp_path, traffic_file):
     assert bench.recorded_traffic(key) is None
 
 
+def test_mmq_summary_sums_each_call(tmp_path, traffic_file):
+    """The MMQ-style prefill's launches group into calls ending at the down kernel; the first
+    call (cold) is left out of the mean, and each kernel's own bytes are kept beside it."""
+    rows_f, rows_w = _copies(32768.0), _copies(65536.0)
+    kernels = ("qmm::quantize_planes_kernel(x)", "qmm::schedule_kernel(x)", "qmm::mq_gateup_kernel(MqGuArgs)",
+               "qmm::mq_down_kernel(MqDownArgs)")
+    for call, scale in ((0, 3.0), (1, 1.0)):
+        for j, name in enumerate(kernels):
+            rows_f.append((name, scale * 100.0 * (j + 1)))
+            rows_w.append((name, 10.0 * (j + 1)))
+    _write(tmp_path / "f.csv", "FETCH_SIZE", rows_f)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", rows_w)
+    bench.pmc_summary("mmq", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = bench.recorded_traffic("mmq")
+    assert rec["bytes_per_launch"]["call"] == round((1000.0 * 2.0 + 100.0) * 1024)
+    assert rec["mq_down_kernel_bytes"] == round(((1200.0 + 400.0) / 2 * 2.0 + 40.0) * 1024)
+
+
+def test_dense_and_combine_summaries(tmp_path, traffic_file):
+    """Dense projections: two launches per matrix in the probe's order, each matrix under its
+    own name; the combine: the mean of its launches."""
+    rows_f, rows_w = _copies(32768.0), _copies(65536.0)
+    for j in range(4):
+        rows_f.append(("qmm::dense_kernel(DenseArgs)", 1000.0 * (j // 2 + 1)))
+        rows_w.append(("qmm::dense_kernel(DenseArgs)", 5.0))
+    _write(tmp_path / "f.csv", "FETCH_SIZE", rows_f)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", rows_w)
+    bench.pmc_summary("dense", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = bench.recorded_traffic("dense")
+    names = [bench.dense_name(wt, nrows, 2560) for wt, nrows, _ in bench.dense_specs()]
+    assert [rec["bytes_per_launch"][n] for n in names] == [round((2000.0 + 5.0) * 1024),
+                                                           round((4000.0 + 5.0) * 1024)]
+    rows_f, rows_w = _copies(32768.0), _copies(65536.0)
+    rows_f += [("void qmm::combine_kernel<3>(x)", v) for v in (300.0, 330.0, 360.0)]
+    rows_w += [("void qmm::combine_kernel<3>(x)", 80.0)] * 3
+    _write(tmp_path / "f.csv", "FETCH_SIZE", rows_f)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", rows_w)
+    bench.pmc_summary("combine", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = bench.recorded_traffic("combine")
+    assert rec["bytes_per_launch"][bench.COMBINE_SHAPES[0][0]] == round((660.0 + 80.0) * 1024)
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        cwd=ROOT, timeout=120)
