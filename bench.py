@@ -210,13 +210,13 @@ def fused_bytes(wtype, nrows, k, n):
 
 def stream_read_reference(torch, M, copies, nbytes, use_graph, reps):
     """The same cold rotation read by the library's plain streaming-read kernel (one launch per
-    copy, no compute): the best per-launch time over a sweep of launch shapes (workgroups, their
-    size, loads in flight per thread), the reference for what one launch reading this many bytes
-    can reach."""
+    copy, no compute): the best per-launch time over a sweep of launch shapes (256 to 3072
+    workgroups of 256, 512 or 1024 threads, 4, 8 or 16 loads in flight per thread), the reference
+    for what one launch reading this many bytes can reach."""
     n16 = nbytes // 16 * 16
     best = None
-    for threads, unroll in ((256, 4), (256, 8), (512, 4), (512, 8), (1024, 4), (256, 16)):
-        for grid in (256, 512, 1024, 2048):
+    for threads in (256, 512, 1024):
+        for unroll, grid in ((u, g) for u in (4, 8, 16) for g in (256, 384, 512, 768, 1024, 1536, 2048, 3072)):
             if grid * threads * unroll * 16 > 8 * n16:
                 continue
             out = torch.empty(grid * threads, dtype=torch.int32, device=copies[0].device)

@@ -254,6 +254,8 @@ template <int WT, int NC, bool SUMS, int U, bool MULTI, int LPR = kGemvLanesPerR
           int BUDGET = 100, bool SGRID = false>
 struct RowEngine {
     static constexpr int RAW = Unit<WT>::RAW;
+    static constexpr int kWT = WT;
+    static constexpr bool kMulti = MULTI, kSignedGrid = SGRID;
     static constexpr int CGMAX = pick_cg<WT, NC, U, MULTI, BUDGET>();
     static constexpr int G = NC >= 4 ? 4 : NC;  // scales per slot group in LDS
     static constexpr uint32_t kSlotQ = 32u * LPR * NC, kColQ = 32u * LPR, kSlotD = 4u * LPR * NC;

@@ -5,11 +5,12 @@
 // entry of a group; DQ, Change: swiglu, then q8_1 of H for the down product, H never stored in
 // fp32]:
 //   gate/up kernel : workgroup (t, g) takes intermediate rows [32t, 32t + 32) of expert
-//                    group_expert[g], both its gate and its up row for each index (a DPP row of
-//                    16 lanes per index), and every entry of the group in passes of 8.  Each
-//                    weight block is loaded once and applied to all entries of the pass.  The
-//                    32 x 8 gate and up sums go through LDS to a half wave per entry, which
-//                    forms h = silu(g) * u and quantizes the 32 values to one q8_1 block of H.
+//                    group_expert[g], both its gate and its up row for each index (one DPP row
+//                    of 16 lanes per index runs both), and every entry of the group in passes
+//                    of 8.  Each weight block is loaded once and applied to all entries of the
+//                    pass.  The 32 x 8 gate and up sums go through LDS to a half wave per
+//                    entry, which forms h = silu(g) * u and quantizes the 32 values to one q8_1
+//                    block of H.
 //   down kernel    : the decode GEMV tile over W_down[e] with the group's H blocks (the entries
 //                    of a group are consecutive, so their H blocks are too).
 // silu(z) = z / (1 + e^-z) in binary32 (expf within 1 ulp, IEEE division).
@@ -44,11 +45,19 @@ struct GroupInfo {
     }
 };
 
-// gate/up workgroup: 1024 threads, 16 waves (4 per SIMD; 128 registers per lane, so the row
-// engine reads each column's activations just before use).  Waves 0..7 run the gate rows and
-// waves 8..15 the up rows of the 32 intermediate indices of one q8_1 block of H (4 indices per
-// wave, a DPP row of 16 lanes each), so each lane holds one row engine.
-constexpr int kGuThreads = 1024;
+// gate/up workgroup.  CB3 rows: 512 threads, 8 waves, two workgroups per CU (4 waves per
+// SIMD, 128 registers per lane, so the row engines read each column's activations just before
+// use), which keeps the grid of inter / 32 x groups workgroups (512 for 16 groups of a 1024-row
+// expert) resident at once.  Wave w takes intermediate indices 4w .. 4w + 3 of the 32 of one
+// q8_1 block of H, a DPP row of 16 lanes each, and each lane holds two row engines, the gate
+// and the up row of its index, whose loads are all issued before either computes.  The other
+// types, whose raw blocks do not fit twice in those registers: 1024 threads, one workgroup per
+// CU, waves 0..7 on the gate rows and 8..15 on the up rows, one row engine per lane.
+template <int WT>
+constexpr bool gu_pair() { return WT == kCB3; }
+template <int WT>
+constexpr int gu_threads() { return gu_pair<WT>() ? 512 : 1024; }
+static int gu_threads_of(int wtype) { return wtype == QMM_CB3 ? 512 : 1024; }
 
 // v_perm selector taking byte k from the second operand (k) or, where bit k of n is set, from
 // the first (k + 4).
@@ -73,18 +82,21 @@ __device__ __forceinline__ uint32_t* cb3_signed_lds() {
 // State of one gate/up workgroup and one pass over entries [c0, c0 + 8) of its group.
 template <int WT, int U, bool MULTI, int NS>
 struct GuWorkgroup {
-    using Stage = ActStage<NS, kGroupPass, kGemvLanesPerRow, kGuThreads>;
+    static constexpr bool PAIR = gu_pair<WT>();
+    static constexpr int TH = gu_threads<WT>();
+    using Stage = ActStage<NS, kGroupPass, kGemvLanesPerRow, TH>;
     const ActLds act;
     float* gl;  // [8][32] gate sums
     float* ul;  // [8][32] up sums
     const uint32_t* sgrid;
     int l16, rg, i, inter, hidden, xq_cols, nbh, k1;
     uint32_t rb, xqbytes;
-    rsrc_t xr, wr;
+    rsrc_t xr, wgr, wur;  // activations, the expert's gate rows, its up rows
+    bool up;              // one row per lane: this wave runs up rows
     const uint8_t* grid;
     const int32_t* entry_col;
     uint8_t* hq;
-    float *sums, *dbg;
+    float *dbg_g, *dbg_u;
 
     // FIRST: the workgroup's first pass (builds the signed codebook from gword); VAR: the row
     // engine's straight-line copies per pass width (the later passes, rare, take the full-width
@@ -100,8 +112,13 @@ struct GuWorkgroup {
         // The row engine is rebuilt each pass from values the compiler cannot see through, so
         // per-pass address arithmetic is not hoisted out of the pass loop (which would hold it
         // in registers, or spill it, across the whole loop).
-        RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, VAR, 0, true> eng(
-            wr, IQ4Consts::opaque_u((uint32_t)i * rb), hidden, (int)IQ4Consts::opaque_u((uint32_t)l16));
+        using Eng = RowEngine<WT, kGroupPass, false, U, MULTI, kGemvLanesPerRow, VAR, 0, true>;
+        // (the gate and up rows sit at the same offset of their matrices: one set of lane
+        // offsets serves both engines; with one row per lane, eg runs this wave's row)
+        const uint32_t roff = IQ4Consts::opaque_u((uint32_t)i * rb);
+        const int lo = (int)IQ4Consts::opaque_u((uint32_t)l16);
+        Eng eg(PAIR || !up ? wgr : wur, roff, hidden, lo);
+        Eng eu(wur, roff, hidden, lo);
         Stage own;
         int ecol[kGroupPass];  // DENSE: the pass's entry columns, read now, needed after the staging
         if constexpr (DENSE) {
@@ -112,22 +129,30 @@ struct GuWorkgroup {
         }
         Stage& stage = DENSE ? pre : own;
         __builtin_amdgcn_sched_barrier(0);
-        eng.load_first();  // every pass (a later pass re-reads the group's rows from L2)
+        // every pass loads the rows (a later pass re-reads the group's rows from L2); the up
+        // row's loads go out once the staged activations have left their registers
+        eg.load_first();
         __builtin_amdgcn_sched_barrier(0);
         stage.store(act);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PAIR) eu.load_first();
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (WT == kCB3 && FIRST) {
             // variant n: byte k negated where bit k of n is set; with every byte of the entry
             // non-zero, ~g + 0x01010101 negates all four bytes without carries, and one v_perm
-            // picks each byte from g or from it.  Thread t writes variants 8 (t mod 2) + n:
-            // selector sign_select(n) with bit 26 for the odd threads.
+            // picks each byte from g or from it.  The 16 variants of entry e are words 16 e ..
+            // 16 e + 15: thread t writes VPT of them (selector sign_select(n mod 8), with bit 26
+            // for n >= 8).
+            constexpr int VPT = kCB3SignedWords / TH;
+            static_assert(VPT == 8 || VPT == 16, "a thread writes half or all of one entry's variants");
             const uint32_t neg = ~gword + 0x01010101u;
-            const uint32_t hsel = (threadIdx.x & 1u) << 26;
-            uint32_t v[8];
+            const int n0 = VPT == 8 ? 8 * (int)(threadIdx.x & 1u) : 0;
+            uint32_t v[VPT];
 #pragma unroll
-            for (int n = 0; n < 8; ++n) v[n] = perm(neg, gword, sign_select(n) | hsel);
-            u32x4* dst = (u32x4*)(cb3_signed_lds() + 8 * threadIdx.x);
-            dst[0] = u32x4{v[0], v[1], v[2], v[3]};
-            dst[1] = u32x4{v[4], v[5], v[6], v[7]};
+            for (int n = 0; n < VPT; ++n) v[n] = perm(neg, gword, sign_select(n & 7) | (n0 + n >= 8 ? 1u << 26 : 0u));
+            u32x4* dst = (u32x4*)(cb3_signed_lds() + VPT * threadIdx.x);
+#pragma unroll
+            for (int j = 0; j < VPT / 4; ++j) dst[j] = u32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
         }
         lds_barrier();
         if constexpr (DENSE) {
@@ -152,15 +177,30 @@ struct GuWorkgroup {
         }
         __builtin_amdgcn_sched_barrier(0);  // decode after the barrier
 
+        // the gate row, then (pair) the up row, with one set of accumulators; the up row's
+        // loads stay in flight while the gate row computes
         float acc[kGroupPass];
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
-        eng.run(act_view<kGroupPass>(act, l16), ncp, sgrid, acc, nullptr, 0, true);
-        const float sum = row16_sums<kGroupPass>(acc, l16);
+        eg.run(act_view<kGroupPass>(act, l16), ncp, sgrid, acc, nullptr, 0, true);
+        const float sg = row16_sums<kGroupPass>(acc, l16);
+        float su = 0.0f;
+        if constexpr (PAIR) {
+#pragma unroll
+            for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
+            eu.run(act_view<kGroupPass>(act, l16), ncp, sgrid, acc, nullptr, 0, true);
+            su = row16_sums<kGroupPass>(acc, l16);
+        }
         const int c = row_col<kGroupPass>(l16);
         if ((l16 & 1) == 0 && c < ncp) {
-            sums[c * 32 + rg] = sum;
-            if (dbg) dbg[(int64_t)(c0 + c) * inter + i] = sum;
+            if (PAIR || !up) {
+                gl[c * 32 + rg] = sg;
+                if (dbg_g) dbg_g[(int64_t)(c0 + c) * inter + i] = sg;
+            }
+            if (PAIR || up) {
+                ul[c * 32 + rg] = PAIR ? su : sg;
+                if (dbg_u) dbg_u[(int64_t)(c0 + c) * inter + i] = PAIR ? su : sg;
+            }
         }
         lds_barrier();
         // SwiGLU -> q8_1: one half wave per entry (waves 0..3), value j = intermediate 32t + j
@@ -181,21 +221,21 @@ struct GuWorkgroup {
 };
 
 template <int WT, int U, bool MULTI, int NS, bool DENSE>
-__global__ __launch_bounds__(kGuThreads) void gu_kernel(
+__global__ __launch_bounds__(gu_threads<WT>(), gu_pair<WT>() ? 4 : 1) void gu_kernel(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
     int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
     uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
     const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
     float* __restrict__ dbg_u) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    static_assert(WT != kCB3 || kCB3SignedWords == 8 * kGuThreads, "eight codebook words per thread");
-    const ActLds act = act_lds_layout<kGroupPass, NS, kGuThreads>(lds, hidden);
+    using WG = GuWorkgroup<WT, U, MULTI, NS>;
+    const ActLds act = act_lds_layout<kGroupPass, NS, WG::TH>(lds, hidden);
     // Loads that need nothing from the group first (their latency then overlaps the group
     // lookup's): with at most 8 activation columns (DENSE), all of them; the codebook entry.
-    typename GuWorkgroup<WT, U, MULTI, NS>::Stage pre;
+    typename WG::Stage pre;
     if constexpr (DENSE) pre.load(make_rsrc(xq, xqbytes), act, 0, xq_cols, xqbytes);
     uint32_t gword = 0;
-    if constexpr (WT == kCB3) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x >> 1));
+    if constexpr (WT == kCB3) gword = ld32(make_rsrc(grid, 2048), 4u * (threadIdx.x / (WG::TH / 512)));
     __builtin_amdgcn_sched_barrier(0);
     GroupInfo gi;
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) {
@@ -205,21 +245,19 @@ __global__ __launch_bounds__(kGuThreads) void gu_kernel(
         return;
     }
 
-    float* gl = (float*)act_lds_end<NS, kGuThreads>(act);
+    float* gl = (float*)act_lds_end<NS, WG::TH>(act);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const bool up = wave >= 8;
     const int rg = (wave & 7) * 4 + (lane >> 4);  // 0..31
-    GuWorkgroup<WT, U, MULTI, NS> w{act, gl, gl + kGroupPass * 32,
-                                    // CB3: the signed codebook (16 sign variants of each entry),
-                                    // built in the first pass: thread t loads entry t / 2 with
-                                    // the activations and, once the weight loads are issued,
-                                    // writes its sign variants 8 (t mod 2) .. 8 (t mod 2) + 7
-                                    WT == kCB3 ? cb3_signed_lds() : nullptr,
-                                    lane & 15, rg, (int)blockIdx.x * 32 + rg, inter, hidden, xq_cols, inter / 32,
-                                    gi.k1, (uint32_t)row_bytes_dev<WT>(hidden), xqbytes, make_rsrc(xq, xqbytes),
-                                    make_rsrc_dw((up ? wu : wg) + gi.e * gu_stride, expert_bytes), grid, entry_col,
-                                    hq, up ? gl + kGroupPass * 32 : gl, up ? dbg_u : dbg_g};
+    WG w{act, gl, gl + kGroupPass * 32,
+         // CB3: the signed codebook (16 sign variants of each entry), built in the first pass:
+         // each thread loads its entry with the activations and, once the weight loads are
+         // issued, writes its share of the entry's variants
+         WT == kCB3 ? cb3_signed_lds() : nullptr,
+         lane & 15, rg, (int)blockIdx.x * 32 + rg, inter, hidden, xq_cols, inter / 32,
+         gi.k1, (uint32_t)row_bytes_dev<WT>(hidden), xqbytes, make_rsrc(xq, xqbytes),
+         make_rsrc_dw(wg + gi.e * gu_stride, expert_bytes), make_rsrc_dw(wu + gi.e * gu_stride, expert_bytes),
+         !WG::PAIR && wave >= 8, grid, entry_col, hq, dbg_g, dbg_u};
     // The first pass outside the loop: its loads start with nothing outstanding.  Later passes
     // first wait for the previous pass's memory operations (which the compiler would otherwise
     // count as outstanding across the loop) and LDS reads.
@@ -253,7 +291,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
 }
 
 // UM: chunk of the double-buffered (MULTI) instance, for rows of more than 6 blocks per lane
-// (2 in the 1024-thread gate/up kernel, whose lanes have 128 registers).
+// (2 in the gate/up kernels, whose lanes have 128 registers).
 template <int WT, int UM = 6, typename F>
 static void dispatch_u_ns(Chunk ch, int ns, F&& go) {
     auto by_u = [&](auto ns_c) {
@@ -282,20 +320,20 @@ struct GroupedArgs {
 
 static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nentries * (size_t)(inter / 32) * 36; }
 
-// Chunks, LDS and staging slots of the two kernels (gate/up: 1024 threads, double-buffered
+// Chunks, LDS and staging slots of the two kernels (gate/up: 512 or 1024 threads, double-buffered
 // chunks of 2 for long rows; down: 512 threads).
 static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
 static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
 // (dynamic LDS: activations and the gate/up sums; the signed CB3 codebook is static)
-static size_t gu_lds_bytes(int64_t hidden) {
-    return act_lds_bytes(hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, kGuThreads) +
+static size_t gu_lds_bytes(int wt, int64_t hidden) {
+    return act_lds_bytes(hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, gu_threads_of(wt)) +
            2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
     return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u, kGemvThreads);
 }
-static int gu_slots(int64_t hidden) {
-    return stage_slots(hidden, kGroupPass, kGuThreads, kGemvLanesPerRow, gu_chunk(hidden).u);
+static int gu_slots(int wt, int64_t hidden) {
+    return stage_slots(hidden, kGroupPass, gu_threads_of(wt), kGemvLanesPerRow, gu_chunk(hidden).u);
 }
 static int down_slots(int64_t inter) {
     return stage_slots(inter, kGroupPass, kGemvThreads, kGemvLanesPerRow, down_chunk(inter).u);
@@ -314,18 +352,18 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     const uint32_t xqbytes = (uint32_t)((uint64_t)a.xq_cols * (a.hidden / 32) * 36);
     {
-        const size_t lds = gu_lds_bytes(a.hidden);
+        const size_t lds = gu_lds_bytes(a.wtype_gu, a.hidden);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
         // at most 8 activation columns: load them all before the group lookup
         const bool dense = a.xq_cols <= kGroupPass;
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
             auto kern = dense ? gu_kernel<WT, U, MULTI, NS, true> : gu_kernel<WT, U, MULTI, NS, false>;
-            hipLaunchKernelGGL(kern, grid_dim, dim3(kGuThreads), lds, a.st, a.w_gate, a.w_up, a.gu_stride, gu_bytes,
+            hipLaunchKernelGGL(kern, grid_dim, dim3(gu_threads<WT>()), lds, a.st, a.w_gate, a.w_up, a.gu_stride, gu_bytes,
                                a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes, a.xq_cols,
                                a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
         const Chunk ch = gu_chunk(a.hidden);
-        const int ns = gu_slots(a.hidden);
+        const int ns = gu_slots(a.wtype_gu, a.hidden);
         if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0, 2>(ch, ns, go);
         else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL, 2>(ch, ns, go);
         else dispatch_u_ns<kCB3, 2>(ch, ns, go);
@@ -408,8 +446,8 @@ static int grouped_call(int wtype_gu, const void* w_gate, const void* w_up, int6
         !aligned(ws, 16))
         return QMM_EALIGN;
     // a pass of 8 entries must fit the workgroup's LDS and staging slots
-    if (gu_lds_bytes(hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
-        gu_slots(hidden) == 0 || down_slots(inter) == 0)
+    if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
+        gu_slots(wtype_gu, hidden) == 0 || down_slots(inter) == 0)
         return QMM_EUNSUPPORTED;
     if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxActBytes || grouped_h_bytes(inter, nentries) > kMaxActBytes)
         return QMM_EUNSUPPORTED;
