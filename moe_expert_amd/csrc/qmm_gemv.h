@@ -278,8 +278,14 @@ struct RowEngine {
         float d[CG];
     };
 
-    __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l_)
-        : wr(wr_), row_off(row_off_), nunits(K / 32), niter((K / 32 + LPR - 1) / LPR), l16(l_) {
+    RowEngine() = default;
+    __device__ __forceinline__ RowEngine(rsrc_t wr_, uint32_t row_off_, int K, int l_) { init(wr_, row_off_, K, l_); }
+    __device__ __forceinline__ void init(rsrc_t wr_, uint32_t row_off_, int K, int l_) {
+        wr = wr_;
+        row_off = row_off_;
+        nunits = K / 32;
+        niter = (K / 32 + LPR - 1) / LPR;
+        l16 = l_;
         // (CB3: the sub-block of the lane's first block; planes: the lane's position in its tiles)
         fr = Unit<WT>::frame(unit_off(l16), WT == kCB3 ? (l16 & 7) : l16);
     }

@@ -269,8 +269,70 @@ __global__ __launch_bounds__(gu_threads<WT>(), gu_pair<WT>() ? 4 : 1) void gu_ke
     }
 }
 
+// Down kernel: workgroups of kDownThreads threads take down_sets<U, MULTI>() sets of
+// kDownRowsPerSet consecutive rows (4 rows per wave and set); a workgroup stages the group's H
+// columns once and issues every set's weight loads before any set computes.  For short rows
+// (at most 2 blocks per lane; Q8_0 and IQ4_NL) small workgroups with at most 96 registers per
+// lane keep five per CU resident (5 waves per SIMD), so that the 16 groups x 2560 rows of the
+// decode workload (1280 workgroups of 2 sets) run in one round; the others take one set and two
+// waves per SIMD.
+constexpr int kDownThreads = 256;
+constexpr int kDownRowsPerSet = kDownThreads / 16;
+template <int WT, int U, bool MULTI>
+constexpr bool down_short() { return U <= 2 && !MULTI && WT != kCB3; }
+template <int WT, int U, bool MULTI>
+constexpr int down_sets_of() { return down_short<WT, U, MULTI>() ? 2 : 1; }
+template <int WT, int U, bool MULTI>
+constexpr int down_waves_per_simd() { return down_short<WT, U, MULTI>() ? 5 : 2; }
+static int down_sets_host(int wt, Chunk ch) { return ch.u <= 2 && !ch.multi && wt != QMM_CB3 ? 2 : 1; }
+
+// One pass (columns [col0, col0 + ncp) of H) over the R row sets from row0: the decode GEMV
+// tile's steps (H loads, weight loads, H into LDS, barrier, decode and apply, row sums) with R
+// row engines per lane.  Each row's sum is the single-set tile's, bitwise.
+template <int WT, int U, int NS, int R>
+__device__ __forceinline__ void down_sets(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t hr,
+                                          uint32_t hbytes, int col0, int ncp, float* y, int64_t ldy, int row0,
+                                          uint32_t* lds) {
+    constexpr int TH = kDownThreads;
+    const ActLds act = act_lds_layout<kGroupPass, NS, TH>(lds, K);
+    uint32_t* lds_grid = act_lds_end<NS, TH>(act);
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int rbase = row0 + (int)(threadIdx.x >> 6) * 4 + (lane >> 4);
+    ActStage<NS, kGroupPass, kGemvLanesPerRow, TH> stage;
+    stage.load(hr, act, col0, ncp, hbytes);
+    GridStage<TH> gstage;
+    if constexpr (WT == kCB3) gstage.load(grid);
+    __builtin_amdgcn_sched_barrier(0);
+    using Eng = RowEngine<WT, kGroupPass, false, U, false, kGemvLanesPerRow, true, R == 1 ? 40 : 0>;
+    Eng eng[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rbase + kDownRowsPerSet * r;
+        const int rowc = row < nrows ? row : nrows - 1;
+        eng[r].init(wr, IQ4Consts::opaque_u((uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K)), K, l16);
+        eng[r].load_first();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    stage.store(act);
+    if constexpr (WT == kCB3) gstage.store(lds_grid);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rbase + kDownRowsPerSet * r;
+        float acc[kGroupPass];
+#pragma unroll
+        for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
+        eng[r].run(act_view<kGroupPass>(act, l16), ncp, lds_grid, acc, nullptr, 0, row < nrows);
+        const float sum = row_sums<kGroupPass, kGemvLanesPerRow>(acc, l16);
+        const int c = row_col<kGroupPass>(l16);
+        if (row < nrows && (l16 & 1) == 0 && c < ncp) y[(int64_t)(col0 + c) * ldy + row] = sum;
+    }
+}
+
 template <int WT, int U, bool MULTI, int NS>
-__global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
+__global__ __launch_bounds__(kDownThreads, (down_waves_per_simd<WT, U, MULTI>())) void down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
                                                             uint32_t expert_bytes, int nexperts,
                                                             const uint8_t* __restrict__ grid, int hidden, int inter,
                                                             const uint8_t* __restrict__ hq, uint32_t hqbytes,
@@ -282,11 +344,18 @@ __global__ __launch_bounds__(kGemvThreads) void down_kernel(const uint8_t* __res
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
     const rsrc_t wr = make_rsrc_dw(wd + gi.e * d_stride, expert_bytes);
     const rsrc_t hr = make_rsrc(hq, hqbytes);
+    constexpr int R = down_sets_of<WT, U, MULTI>();
     for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
         if (c0 != gi.k0) __syncthreads();
-        gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kGemvThreads, true, 40>(
-            wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kGemvRowsPerWG, lds);
+        if constexpr (MULTI) {
+            // (long rows: the decode GEMV tile with its double-buffered engine)
+            gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kDownThreads, true, 40>(
+                wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kDownRowsPerSet, lds);
+        } else {
+            down_sets<WT, U, NS, R>(wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden,
+                                    blockIdx.x * R * kDownRowsPerSet, lds);
+        }
     }
 }
 
@@ -321,7 +390,7 @@ struct GroupedArgs {
 static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nentries * (size_t)(inter / 32) * 36; }
 
 // Chunks, LDS and staging slots of the two kernels (gate/up: 512 or 1024 threads, double-buffered
-// chunks of 2 for long rows; down: 512 threads).
+// chunks of 2 for long rows; down: 256 threads).
 static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
 static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
 // (dynamic LDS: activations and the gate/up sums; the signed CB3 codebook is static)
@@ -330,13 +399,13 @@ static size_t gu_lds_bytes(int wt, int64_t hidden) {
            2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
-    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u, kGemvThreads);
+    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u, kDownThreads);
 }
 static int gu_slots(int wt, int64_t hidden) {
     return stage_slots(hidden, kGroupPass, gu_threads_of(wt), kGemvLanesPerRow, gu_chunk(hidden).u);
 }
 static int down_slots(int64_t inter) {
-    return stage_slots(inter, kGroupPass, kGemvThreads, kGemvLanesPerRow, down_chunk(inter).u);
+    return stage_slots(inter, kGroupPass, kDownThreads, kGemvLanesPerRow, down_chunk(inter).u);
 }
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
@@ -372,9 +441,10 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     {
         const size_t lds = down_lds_bytes(a.wtype_down, a.inter);
-        const dim3 grid_dim((unsigned)((a.hidden + kGemvRowsPerWG - 1) / kGemvRowsPerWG), (unsigned)a.ngroups);
+        const int rows_wg = down_sets_host(a.wtype_down, down_chunk(a.inter)) * kDownRowsPerSet;
+        const dim3 grid_dim((unsigned)((a.hidden + rows_wg - 1) / rows_wg), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
-            hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kGemvThreads), lds, a.st, a.w_down,
+            hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kDownThreads), lds, a.st, a.w_down,
                                a.d_stride, d_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.ws,
                                (uint32_t)hbytes, a.group_expert, a.group_off, a.nentries, a.y);
         };
