@@ -511,6 +511,14 @@ def mfma_reference(torch, M, reps):
             "kernel": "qmm_debug_mfma_loop (v_mfma_f32_32x32x16_f16, 8 accumulators per wave, registers only)"}
 
 
+def prefill_bytes(h, z):
+    """Algorithmic bytes of one prefill call: every expert's weights, the tokens and the routing
+    read once, H written and read once (fp16), Y written once (fp32)."""
+    w = h["wg"].nbytes + h["wu"].nbytes + h["wd"].nbytes
+    ids = h["st"].nbytes + h["off"].nbytes
+    return int(w + h["x16"].nbytes + ids + 2 * z["nent"] * z["inter"] * 2 + z["nent"] * z["hidden"] * 4)
+
+
 def bench_prefill(args, torch, M, cpu_s=10.0):
     import numpy as np
 
@@ -535,6 +543,7 @@ def bench_prefill(args, torch, M, cpu_s=10.0):
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                              "traffic": rec["bytes_per_launch"]["call"] if rec else None,
+                             "algorithmic_bytes_per_call": prefill_bytes(h, z),
                              "kernel": "schedule + pf_gateup_kernel + pf_down_kernel (one call)"}})
     if not args.no_cpu:
         import oracle

@@ -269,31 +269,30 @@ __global__ __launch_bounds__(gu_threads<WT>(), gu_pair<WT>() ? 4 : 1) void gu_ke
     }
 }
 
-// Down kernel: workgroups of kDownThreads threads take down_sets<U, MULTI>() sets of
-// kDownRowsPerSet consecutive rows (4 rows per wave and set); a workgroup stages the group's H
-// columns once and issues every set's weight loads before any set computes.  For short rows
-// (at most 2 blocks per lane; Q8_0 and IQ4_NL) small workgroups with at most 96 registers per
-// lane keep five per CU resident (5 waves per SIMD), so that the 16 groups x 2560 rows of the
-// decode workload (1280 workgroups of 2 sets) run in one round; the others take one set and two
-// waves per SIMD.
-constexpr int kDownThreads = 256;
-constexpr int kDownRowsPerSet = kDownThreads / 16;
+// Down kernel: a workgroup takes 32 consecutive rows of one group.  Rows of at most 2 blocks
+// per lane (Q8_0, IQ4_NL; the decode workload's 1024-value rows): 256 threads in two sets of 16
+// rows (4 rows per wave and set); the workgroup stages the group's H columns once and issues
+// both sets' weight loads before either computes, and at most 96 registers per lane keep five
+// workgroups per CU resident (5 waves per SIMD), so that the 16 groups x 2560 rows of the
+// workload (1280 workgroups) run in one round.  Other rows: 512 threads, one set of 32 rows
+// (the staging of longer rows needs the wider workgroup).
 template <int WT, int U, bool MULTI>
 constexpr bool down_short() { return U <= 2 && !MULTI && WT != kCB3; }
 template <int WT, int U, bool MULTI>
-constexpr int down_sets_of() { return down_short<WT, U, MULTI>() ? 2 : 1; }
+constexpr int down_threads() { return down_short<WT, U, MULTI>() ? 256 : 512; }
 template <int WT, int U, bool MULTI>
 constexpr int down_waves_per_simd() { return down_short<WT, U, MULTI>() ? 5 : 2; }
-static int down_sets_host(int wt, Chunk ch) { return ch.u <= 2 && !ch.multi && wt != QMM_CB3 ? 2 : 1; }
+constexpr int kDownRows = 32;  // rows per workgroup
+static int down_threads_host(int wt, Chunk ch) { return ch.u <= 2 && !ch.multi && wt != QMM_CB3 ? 256 : 512; }
 
 // One pass (columns [col0, col0 + ncp) of H) over the R row sets from row0: the decode GEMV
 // tile's steps (H loads, weight loads, H into LDS, barrier, decode and apply, row sums) with R
 // row engines per lane.  Each row's sum is the single-set tile's, bitwise.
-template <int WT, int U, int NS, int R>
+template <int WT, int U, int NS, int TH>
 __device__ __forceinline__ void down_sets(rsrc_t wr, int nrows, int K, const uint8_t* grid, rsrc_t hr,
                                           uint32_t hbytes, int col0, int ncp, float* y, int64_t ldy, int row0,
                                           uint32_t* lds) {
-    constexpr int TH = kDownThreads;
+    constexpr int R = kDownRows / (TH / 16);  // row sets
     const ActLds act = act_lds_layout<kGroupPass, NS, TH>(lds, K);
     uint32_t* lds_grid = act_lds_end<NS, TH>(act);
     const int lane = threadIdx.x & 63;
@@ -308,7 +307,7 @@ __device__ __forceinline__ void down_sets(rsrc_t wr, int nrows, int K, const uin
     Eng eng[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = rbase + kDownRowsPerSet * r;
+        const int row = rbase + (TH / 16) * r;
         const int rowc = row < nrows ? row : nrows - 1;
         eng[r].init(wr, IQ4Consts::opaque_u((uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K)), K, l16);
         eng[r].load_first();
@@ -320,7 +319,7 @@ __device__ __forceinline__ void down_sets(rsrc_t wr, int nrows, int K, const uin
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = rbase + kDownRowsPerSet * r;
+        const int row = rbase + (TH / 16) * r;
         float acc[kGroupPass];
 #pragma unroll
         for (int c = 0; c < kGroupPass; ++c) acc[c] = 0.0f;
@@ -332,7 +331,7 @@ __device__ __forceinline__ void down_sets(rsrc_t wr, int nrows, int K, const uin
 }
 
 template <int WT, int U, bool MULTI, int NS>
-__global__ __launch_bounds__(kDownThreads, (down_waves_per_simd<WT, U, MULTI>())) void down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
+__global__ __launch_bounds__((down_threads<WT, U, MULTI>()), (down_waves_per_simd<WT, U, MULTI>())) void down_kernel(const uint8_t* __restrict__ wd, int64_t d_stride,
                                                             uint32_t expert_bytes, int nexperts,
                                                             const uint8_t* __restrict__ grid, int hidden, int inter,
                                                             const uint8_t* __restrict__ hq, uint32_t hqbytes,
@@ -344,17 +343,17 @@ __global__ __launch_bounds__(kDownThreads, (down_waves_per_simd<WT, U, MULTI>())
     if (!gi.load(group_expert, group_off, blockIdx.y, nexperts, nentries)) return;
     const rsrc_t wr = make_rsrc_dw(wd + gi.e * d_stride, expert_bytes);
     const rsrc_t hr = make_rsrc(hq, hqbytes);
-    constexpr int R = down_sets_of<WT, U, MULTI>();
+    constexpr int TH = down_threads<WT, U, MULTI>();
     for (int c0 = gi.k0; c0 < gi.k1; c0 += kGroupPass) {
         const int ncp = gi.k1 - c0 < kGroupPass ? gi.k1 - c0 : kGroupPass;
         if (c0 != gi.k0) __syncthreads();
         if constexpr (MULTI) {
             // (long rows: the decode GEMV tile with its double-buffered engine)
-            gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, kDownThreads, true, 40>(
-                wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kDownRowsPerSet, lds);
+            gemv_tile<WT, false, kGroupPass, U, MULTI, NS, kGemvLanesPerRow, TH, true, 40>(
+                wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, nullptr, blockIdx.x * kDownRows, lds);
         } else {
-            down_sets<WT, U, NS, R>(wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden,
-                                    blockIdx.x * R * kDownRowsPerSet, lds);
+            down_sets<WT, U, NS, TH>(wr, hidden, inter, grid, hr, hqbytes, c0, ncp, y, hidden, blockIdx.x * kDownRows,
+                                     lds);
         }
     }
 }
@@ -399,13 +398,15 @@ static size_t gu_lds_bytes(int wt, int64_t hidden) {
            2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
-    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u, kDownThreads);
+    return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u,
+                          down_threads_host(wt, down_chunk(inter)));
 }
 static int gu_slots(int wt, int64_t hidden) {
     return stage_slots(hidden, kGroupPass, gu_threads_of(wt), kGemvLanesPerRow, gu_chunk(hidden).u);
 }
-static int down_slots(int64_t inter) {
-    return stage_slots(inter, kGroupPass, kDownThreads, kGemvLanesPerRow, down_chunk(inter).u);
+static int down_slots(int wt, int64_t inter) {
+    return stage_slots(inter, kGroupPass, down_threads_host(wt, down_chunk(inter)), kGemvLanesPerRow,
+                       down_chunk(inter).u);
 }
 static size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
@@ -441,15 +442,15 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     {
         const size_t lds = down_lds_bytes(a.wtype_down, a.inter);
-        const int rows_wg = down_sets_host(a.wtype_down, down_chunk(a.inter)) * kDownRowsPerSet;
-        const dim3 grid_dim((unsigned)((a.hidden + rows_wg - 1) / rows_wg), (unsigned)a.ngroups);
+        const dim3 grid_dim((unsigned)((a.hidden + kDownRows - 1) / kDownRows), (unsigned)a.ngroups);
         auto go = [&]<int WT, int U, bool MULTI, int NS>() {
-            hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(kDownThreads), lds, a.st, a.w_down,
+            hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(down_threads<WT, U, MULTI>()), lds, a.st,
+                               a.w_down,
                                a.d_stride, d_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.ws,
                                (uint32_t)hbytes, a.group_expert, a.group_off, a.nentries, a.y);
         };
         const Chunk ch = down_chunk(a.inter);
-        const int ns = down_slots(a.inter);
+        const int ns = down_slots(a.wtype_down, a.inter);
         if (a.wtype_down == QMM_Q8_0) dispatch_u_ns<kQ8_0>(ch, ns, go);
         else if (a.wtype_down == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL>(ch, ns, go);
         else dispatch_u_ns<kCB3>(ch, ns, go);
@@ -517,7 +518,7 @@ static int grouped_call(int wtype_gu, const void* w_gate, const void* w_up, int6
         return QMM_EALIGN;
     // a pass of 8 entries must fit the workgroup's LDS and staging slots
     if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
-        gu_slots(wtype_gu, hidden) == 0 || down_slots(inter) == 0)
+        gu_slots(wtype_gu, hidden) == 0 || down_slots(wtype_down, inter) == 0)
         return QMM_EUNSUPPORTED;
     if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxActBytes || grouped_h_bytes(inter, nentries) > kMaxActBytes)
         return QMM_EUNSUPPORTED;

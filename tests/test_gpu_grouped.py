@@ -112,6 +112,20 @@ def test_grouped_long_rows():
     run_case(ex, ge, go, ec, 6, 852)
 
 
+@pytest.mark.parametrize("wt_down,inter", [(M.QMM_IQ4_NL, 4096), (M.QMM_CB3, 512), (M.QMM_Q8_0, 256)])
+def test_grouped_down_shapes(wt_down, inter):
+    """The down kernel's instances: long rows (inter 4096, the double-buffered tile), CB3 rows
+    (one row set per workgroup), short Q8_0 rows (two row sets per workgroup); IQ4_NL gate/up
+    (one row per lane, 1024-thread workgroups)."""
+    hidden = 288 if wt_down != M.QMM_CB3 else 512
+    print(f"grouped down shapes: down {wt_down}, inter {inter}, hidden {hidden}", flush=True)
+    ex = Experts(860 + inter, 3, hidden, inter, wt_gu=M.QMM_IQ4_NL, wt_down=wt_down)
+    ge = np.array([1, 2, 0], np.int32)
+    go = np.array([0, 3, 4, 9], np.int32)
+    ec = synth.rng_for(861 + inter).integers(0, 4, size=9).astype(np.int32)
+    run_case(ex, ge, go, ec, 4, 862 + inter)
+
+
 @pytest.fixture(scope="module")
 def full_experts():
     """The grouped decode workload: 128 experts, hidden 2560, CB3 gate/up 2560->1024, IQ4_NL
