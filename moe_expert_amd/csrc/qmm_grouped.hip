@@ -45,19 +45,19 @@ struct GroupInfo {
     }
 };
 
-// gate/up workgroup.  CB3 rows: 512 threads, 8 waves, two workgroups per CU (4 waves per
-// SIMD, 128 registers per lane, so the row engines read each column's activations just before
-// use), which keeps the grid of inter / 32 x groups workgroups (512 for 16 groups of a 1024-row
-// expert) resident at once.  Wave w takes intermediate indices 4w .. 4w + 3 of the 32 of one
-// q8_1 block of H, a DPP row of 16 lanes each, and each lane holds two row engines, the gate
-// and the up row of its index, whose loads are all issued before either computes.  The other
-// types, whose raw blocks do not fit twice in those registers: 1024 threads, one workgroup per
-// CU, waves 0..7 on the gate rows and 8..15 on the up rows, one row engine per lane.
-template <int WT>
-constexpr bool gu_pair() { return WT == kCB3; }
-template <int WT>
-constexpr int gu_threads() { return gu_pair<WT>() ? 512 : 1024; }
-static int gu_threads_of(int wtype) { return wtype == QMM_CB3 ? 512 : 1024; }
+// gate/up workgroup.  PAIR (CB3 rows whose pass fits two workgroups per CU): 512 threads, 8
+// waves, two workgroups per CU (4 waves per SIMD, 128 registers per lane, so the row engines
+// read each column's activations just before use), which keeps the grid of inter / 32 x groups
+// workgroups (512 for 16 groups of a 1024-row expert) resident at once.  Wave w takes
+// intermediate indices 4w .. 4w + 3 of the 32 of one q8_1 block of H, a DPP row of 16 lanes
+// each, and each lane holds two row engines, the gate and the up row of its index, whose loads
+// are all issued before either computes.  Otherwise (Q8_0 and IQ4_NL, whose raw blocks do not
+// fit twice in those registers, and CB3 rows too long for the 512-thread staging): 1024
+// threads, one workgroup per CU, waves 0..7 on the gate rows and 8..15 on the up rows, one row
+// engine per lane.
+template <bool PAIR>
+constexpr int gu_threads() { return PAIR ? 512 : 1024; }
+constexpr size_t kGuPairLds = 48 << 10;  // dynamic LDS that leaves room for two per CU
 
 // v_perm selector taking byte k from the second operand (k) or, where bit k of n is set, from
 // the first (k + 4).
@@ -80,10 +80,10 @@ __device__ __forceinline__ uint32_t* cb3_signed_lds() {
 }
 
 // State of one gate/up workgroup and one pass over entries [c0, c0 + 8) of its group.
-template <int WT, int U, bool MULTI, int NS>
+template <int WT, int U, bool MULTI, int NS, bool PAIR_>
 struct GuWorkgroup {
-    static constexpr bool PAIR = gu_pair<WT>();
-    static constexpr int TH = gu_threads<WT>();
+    static constexpr bool PAIR = PAIR_;
+    static constexpr int TH = gu_threads<PAIR>();
     using Stage = ActStage<NS, kGroupPass, kGemvLanesPerRow, TH>;
     const ActLds act;
     float* gl;  // [8][32] gate sums
@@ -220,15 +220,15 @@ struct GuWorkgroup {
     }
 };
 
-template <int WT, int U, bool MULTI, int NS, bool DENSE>
-__global__ __launch_bounds__(gu_threads<WT>(), gu_pair<WT>() ? 4 : 1) void gu_kernel(
+template <int WT, int U, bool MULTI, int NS, bool DENSE, bool PAIR>
+__global__ __launch_bounds__(gu_threads<PAIR>(), PAIR ? 4 : 1) void gu_kernel(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t gu_stride, uint32_t expert_bytes,
     int nexperts, const uint8_t* __restrict__ grid, int hidden, int inter, const uint8_t* __restrict__ xq,
     uint32_t xqbytes, int xq_cols, const int32_t* __restrict__ group_expert, const int32_t* __restrict__ group_off,
     const int32_t* __restrict__ entry_col, int nentries, uint8_t* __restrict__ hq, float* __restrict__ dbg_g,
     float* __restrict__ dbg_u) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    using WG = GuWorkgroup<WT, U, MULTI, NS>;
+    using WG = GuWorkgroup<WT, U, MULTI, NS, PAIR>;
     const ActLds act = act_lds_layout<kGroupPass, NS, WG::TH>(lds, hidden);
     // Loads that need nothing from the group first (their latency then overlaps the group
     // lookup's): with at most 8 activation columns (DENSE), all of them; the codebook entry.
@@ -393,16 +393,23 @@ static size_t grouped_h_bytes(int64_t inter, int nentries) { return (size_t)nent
 static Chunk gu_chunk(int64_t hidden) { return gemv_chunk(lane_blocks(hidden, kGemvLanesPerRow), kGemvLanesPerRow, false, 2); }
 static Chunk down_chunk(int64_t inter) { return gemv_chunk(lane_blocks(inter, kGemvLanesPerRow), kGemvLanesPerRow, false); }
 // (dynamic LDS: activations and the gate/up sums; the signed CB3 codebook is static)
-static size_t gu_lds_bytes(int wt, int64_t hidden) {
-    return act_lds_bytes(hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, gu_threads_of(wt)) +
+static size_t gu_lds_bytes(bool pair, int64_t hidden) {
+    return act_lds_bytes(hidden, kGroupPass, kGemvLanesPerRow, gu_chunk(hidden).u, pair ? 512 : 1024) +
            2 * kGroupPass * 32 * sizeof(float);
 }
 static size_t down_lds_bytes(int wt, int64_t inter) {
     return gemv_lds_bytes(wt, inter, kGroupPass, kGemvLanesPerRow, down_chunk(inter).u,
                           down_threads_host(wt, down_chunk(inter)));
 }
-static int gu_slots(int wt, int64_t hidden) {
-    return stage_slots(hidden, kGroupPass, gu_threads_of(wt), kGemvLanesPerRow, gu_chunk(hidden).u);
+static int gu_slots(bool pair, int64_t hidden) {
+    return stage_slots(hidden, kGroupPass, pair ? 512 : 1024, kGemvLanesPerRow, gu_chunk(hidden).u);
+}
+// CB3 rows whose pass the 512-thread workgroup stages, two workgroups per CU, and whose two
+// engines fit the registers (chunks of at most 5 blocks, or double-buffered chunks of 2)
+static bool gu_pair_host(int wt, int64_t hidden) {
+    const Chunk ch = gu_chunk(hidden);
+    return wt == QMM_CB3 && (ch.multi || ch.u <= 5) && gu_slots(true, hidden) != 0 &&
+           gu_lds_bytes(true, hidden) <= kGuPairLds;
 }
 static int down_slots(int wt, int64_t inter) {
     return stage_slots(inter, kGroupPass, down_threads_host(wt, down_chunk(inter)), kGemvLanesPerRow,
@@ -422,18 +429,29 @@ static int launch_grouped(const GroupedArgs& a) {
     }
     const uint32_t xqbytes = (uint32_t)((uint64_t)a.xq_cols * (a.hidden / 32) * 36);
     {
-        const size_t lds = gu_lds_bytes(a.wtype_gu, a.hidden);
+        const bool pair = gu_pair_host(a.wtype_gu, a.hidden);
+        const size_t lds = gu_lds_bytes(pair, a.hidden);
         const dim3 grid_dim((unsigned)(a.inter / 32), (unsigned)a.ngroups);
         // at most 8 activation columns: load them all before the group lookup
         const bool dense = a.xq_cols <= kGroupPass;
-        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
-            auto kern = dense ? gu_kernel<WT, U, MULTI, NS, true> : gu_kernel<WT, U, MULTI, NS, false>;
-            hipLaunchKernelGGL(kern, grid_dim, dim3(gu_threads<WT>()), lds, a.st, a.w_gate, a.w_up, a.gu_stride, gu_bytes,
+        auto launch = [&](auto kern, int threads) {
+            hipLaunchKernelGGL(kern, grid_dim, dim3(threads), lds, a.st, a.w_gate, a.w_up, a.gu_stride, gu_bytes,
                                a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes, a.xq_cols,
                                a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
+        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
+            if constexpr (WT == kCB3 && (MULTI || U <= 5)) {
+                if (pair) {
+                    launch(dense ? gu_kernel<WT, U, MULTI, NS, true, true> : gu_kernel<WT, U, MULTI, NS, false, true>,
+                           gu_threads<true>());
+                    return;
+                }
+            }
+            launch(dense ? gu_kernel<WT, U, MULTI, NS, true, false> : gu_kernel<WT, U, MULTI, NS, false, false>,
+                   gu_threads<false>());
+        };
         const Chunk ch = gu_chunk(a.hidden);
-        const int ns = gu_slots(a.wtype_gu, a.hidden);
+        const int ns = gu_slots(pair, a.hidden);
         if (a.wtype_gu == QMM_Q8_0) dispatch_u_ns<kQ8_0, 2>(ch, ns, go);
         else if (a.wtype_gu == QMM_IQ4_NL) dispatch_u_ns<kIQ4_NL, 2>(ch, ns, go);
         else dispatch_u_ns<kCB3, 2>(ch, ns, go);
@@ -517,8 +535,9 @@ static int grouped_call(int wtype_gu, const void* w_gate, const void* w_up, int6
         !aligned(ws, 16))
         return QMM_EALIGN;
     // a pass of 8 entries must fit the workgroup's LDS and staging slots
-    if (gu_lds_bytes(wtype_gu, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
-        gu_slots(wtype_gu, hidden) == 0 || down_slots(wtype_down, inter) == 0)
+    const bool pair = gu_pair_host(wtype_gu, hidden);
+    if (gu_lds_bytes(pair, hidden) > kLdsCap || down_lds_bytes(wtype_down, inter) > kLdsCap ||
+        gu_slots(pair, hidden) == 0 || down_slots(wtype_down, inter) == 0)
         return QMM_EUNSUPPORTED;
     if ((uint64_t)xq_cols * (hidden / 32) * 36 > kMaxActBytes || grouped_h_bytes(inter, nentries) > kMaxActBytes)
         return QMM_EUNSUPPORTED;

@@ -101,11 +101,13 @@ def test_grouped_other_formats(wt_gu, wt_down):
     run_case(ex, ge, go, ec, 2, 822)
 
 
-def test_grouped_long_rows():
-    """hidden 4096 (8 blocks per lane: the double-buffered gate/up chunks) with 11 entries in a
-    group (two passes)."""
-    print("grouped long rows: 3 experts 4096 -> 64, groups of 11 and 2 entries", flush=True)
-    ex = Experts(850, 3, 4096, 64, wt_gu=M.QMM_CB3, wt_down=M.QMM_Q8_0)
+@pytest.mark.parametrize("hidden", [3072, 4096])
+def test_grouped_long_rows(hidden):
+    """Long CB3 gate/up rows with 11 entries in a group (two passes): 3072 (6 blocks per lane,
+    the 1024-thread workgroup with one row per lane) and 4096 (8 blocks per lane: the
+    double-buffered chunks, two rows per lane)."""
+    print(f"grouped long rows: 3 experts {hidden} -> 64, groups of 11 and 2 entries", flush=True)
+    ex = Experts(850, 3, hidden, 64, wt_gu=M.QMM_CB3, wt_down=M.QMM_Q8_0)
     ge = np.array([2, 0], np.int32)
     go = np.array([0, 11, 13], np.int32)
     ec = synth.rng_for(851).integers(0, 6, size=13).astype(np.int32)
