@@ -191,15 +191,21 @@ struct GuWorkgroup {
             eu.run(act_view<kGroupPass>(act, l16), ncp, sgrid, acc, nullptr, 0, true);
             su = row16_sums<kGroupPass>(acc, l16);
         }
-        const int c = row_col<kGroupPass>(l16);
-        if ((l16 & 1) == 0 && c < ncp) {
+        // (the lane's index and row, recomputed from the thread index: kept across the row
+        // engines' runs they would take registers the runs need)
+        const uint32_t tid = IQ4Consts::opaque_u(threadIdx.x);
+        const int lb = (int)(tid & 15u);
+        const int rgb = (int)(((tid >> 6) & 7u) * 4u + ((tid & 63u) >> 4));
+        const int ib = (int)blockIdx.x * 32 + rgb;
+        const int c = row_col<kGroupPass>(lb);
+        if ((lb & 1) == 0 && c < ncp) {
             if (PAIR || !up) {
-                gl[c * 32 + rg] = sg;
-                if (dbg_g) dbg_g[(int64_t)(c0 + c) * inter + i] = sg;
+                gl[c * 32 + rgb] = sg;
+                if (dbg_g) dbg_g[(int64_t)(c0 + c) * inter + ib] = sg;
             }
             if (PAIR || up) {
-                ul[c * 32 + rg] = PAIR ? su : sg;
-                if (dbg_u) dbg_u[(int64_t)(c0 + c) * inter + i] = PAIR ? su : sg;
+                ul[c * 32 + rgb] = PAIR ? su : sg;
+                if (dbg_u) dbg_u[(int64_t)(c0 + c) * inter + ib] = PAIR ? su : sg;
             }
         }
         lds_barrier();
