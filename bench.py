@@ -250,7 +250,7 @@ def bench_gemv(args, torch, M, wtype, nrows, k, cols, seed, metric, name, ndisti
     torch.cuda.synchronize()
     use_graph = not args.no_graph
     # the calls that quantize inside the GEMV (rows of at most 96 blocks)
-    fused = set() if args.unfused or k > 3072 else {n for n in cols if n in FUSED_COLS}
+    fused = set() if args.unfused else fused_cols_of(k, cols)
 
     def step(slot):
         w = copies[slot % ncopies]
@@ -851,6 +851,13 @@ FUSED_COLS = (1,)
 GROUPED_M = (1, 4, 8)
 # the Q8_0 workloads: (rows, k, columns, seed key)
 Q8_SPECS = ((12288, 2560, (1, 2, 3, 4), "q8_0_12288x2560"), (2560, 6144, (7, 8), "q8_0_2560x6144"))
+# the Q8_0 counter probe: those and the 512-row matrix
+Q8_PROBE_SPECS = Q8_SPECS + ((512, 2560, (1,), "q8_0_tiny"),)
+
+
+def fused_cols_of(k, cols):
+    """Column counts the benchmark step runs as fused calls (q8_1 formed in the GEMV)."""
+    return {n for n in cols if n in FUSED_COLS} if k <= 3072 else set()
 
 
 def cold_copies(wbytes):
@@ -888,21 +895,25 @@ def pmc_probe(torch, M, workload):
     elif workload == "q8_0":
         wt = synth.Q8_0
         sets = []
-        for nrows, k, cols, key in Q8_SPECS:
+        for nrows, k, cols, key in Q8_PROBE_SPECS:
             wbytes = nrows * synth.row_bytes(wt, k)
             host = [synth.weights(wt, synth.rng_for(synth.SEEDS[key] + i), nrows, k) for i in range(6)]
             copies = [torch.from_numpy(host[i % 6]).to(dev) for i in range(cold_copies(wbytes))]
             rng = synth.rng_for(synth.SEEDS[key] + 100)
             xs = synth.activations(rng, max(cols), k)
-            xq = {n: M.qmm_quantize_q8_1(torch.from_numpy(xs[:n].copy()).to(dev)) for n in cols}
+            xf = {n: torch.from_numpy(xs[:n].copy()).to(dev) for n in cols}
+            xq = {n: M.qmm_quantize_q8_1(xf[n]) for n in cols}
             y = {n: torch.empty((n, nrows), dtype=torch.float32, device=dev) for n in cols}
-            sets.append((nrows, k, cols, copies, xq, y))
+            sets.append((nrows, k, cols, copies, xf, xq, y))
 
-        def run():
-            for nrows, k, cols, copies, xq, y in sets:
+        def run():   # as the benchmark step: fused where it fuses
+            for nrows, k, cols, copies, xf, xq, y in sets:
                 for n in cols:
                     for w in copies:
-                        M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
+                        if n in fused_cols_of(k, cols):
+                            M.qgemv_dense_f32(wt, w, nrows, k, xf[n], n, y=y[n])
+                        else:
+                            M.qgemv_dense(wt, w, nrows, k, xq[n], n, y=y[n])
     elif workload == "grouped":
         slots, _, call, _, _, _ = grouped_setup(torch, M)
 
@@ -974,7 +985,7 @@ def pmc_summary(workload, fetch_csv, write_csv):
 
     import synth
     pattern = {"gemv": r"gemv_f32_kernel<\d+, \d+, (\d+),|gemv_kernel<\d+, false, (\d+),",
-               "q8_0": r"gemv_kernel<\d+, false, (\d+),",
+               "q8_0": r"gemv_f32_kernel<\d+, \d+, (\d+),|gemv_kernel<\d+, false, (\d+),",
                "grouped": r"(gu_kernel|down_kernel)",
                "prefill": r"(schedule_kernel|pf_gateup_kernel|pf_down_kernel)",
                "planes": r"gemv_kernel<[45], false, (\d+),",
@@ -1008,7 +1019,7 @@ def pmc_summary(workload, fetch_csv, write_csv):
     if workload in ("q8_0", "planes"):
         # dispatch order: per matrix, per column count, one launch per weight copy
         if workload == "q8_0":
-            specs, prefix = [(synth.Q8_0, nrows, k, cols) for nrows, k, cols, _ in Q8_SPECS], "gemv"
+            specs, prefix = [(synth.Q8_0, nrows, k, cols) for nrows, k, cols, _ in Q8_PROBE_SPECS], "gemv"
         else:
             specs, prefix = [sp[:4] for sp in planes_specs()], "planes"
         i = 0
@@ -1022,7 +1033,10 @@ def pmc_summary(workload, fetch_csv, write_csv):
                 fetch[n] = mean([v for _, v in fk[i:i + nc]])
                 write[n] = mean([v for _, v in wk[i:i + nc]])
                 i += nc
-            r["algorithmic_bytes"] = {str(n): gemv_bytes(wt, nrows, k, n) for n in cols}
+            fc = fused_cols_of(k, cols) if workload == "q8_0" else set()
+            r["algorithmic_bytes"] = {str(n): fused_bytes(wt, nrows, k, n) if n in fc else gemv_bytes(wt, nrows, k, n)
+                                      for n in cols}
+            r["fused_columns"] = sorted(fc)
             r["fetch_kib"] = {str(n): round(v, 1) for n, v in fetch.items()}
             r["write_kib"] = {str(n): round(v, 1) for n, v in write.items()}
             r["bytes_per_launch"] = {str(n): round((fetch[n] * ff + write[n] * wf) * 1024) for n in cols}

@@ -39,11 +39,12 @@ def test_q8_0_summary_groups_dispatches_in_order(tmp_path, traffic_file):
     back under the right keys, scaled by the copy calibration."""
     rows_f, rows_w = _copies(32768.0), _copies(65536.0)
     expect = {}
-    for nrows, k, cols, _ in bench.Q8_SPECS:
+    for nrows, k, cols, _ in bench.Q8_PROBE_SPECS:
         nc = bench.cold_copies(nrows * synth.row_bytes(synth.Q8_0, k))
         for n in cols:
             nc_pass = 1 << (n - 1).bit_length()
-            name = f"void qmm::gemv_kernel<1, false, {nc_pass}, 5, false, 1, 16, 256>(x)"
+            name = (f"void qmm::gemv_f32_kernel<1, 5, {n}, 512>(x)" if n in bench.fused_cols_of(k, cols) else
+                    f"void qmm::gemv_kernel<1, false, {nc_pass}, 5, false, 1, 16, 256>(x)")
             rows_f += [(name, 1000.0 * n + nrows)] * nc
             rows_w += [(name, 10.0 * n)] * nc
             expect[(nrows, k, n)] = round(((1000.0 * n + nrows) * 2.0 + 10.0 * n) * 1024)
@@ -55,6 +56,8 @@ def test_q8_0_summary_groups_dispatches_in_order(tmp_path, traffic_file):
         r = rec[f"gemv:{synth.Q8_0}:{nrows}x{k}"]
         assert r["bytes_per_launch"][str(n)] == b
         assert r["source_sha256"] == bench.source_digest(r["sources"])
+        assert r["fused_columns"] == sorted(bench.fused_cols_of(k, [n for nn, kk, cols, _ in bench.Q8_PROBE_SPECS
+                                                                    if (nn, kk) == (nrows, k) for n in cols]))
 
 
 def test_gemv_summary_and_lookup(tmp_path, traffic_file):
