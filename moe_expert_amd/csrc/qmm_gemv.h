@@ -470,11 +470,15 @@ __device__ __forceinline__ float row_sums(const float (&acc)[NC], int l) {
 // order), d = amax / 127 and q = x / d rounded half away from zero, IEEE binary32, clamped to
 // +-127, so the staged bytes equal the ones the standalone quantizer writes; only d (as fp16)
 // is staged.
-template <int NC, int TH>
+// Only the first SB blocks of each column are staged: the row engine reads no others (SB = 16
+// lanes x its chunk); the tasks of the blocks beyond skip their loads, their arithmetic and their
+// LDS writes (whole waves of them in the last pass).
+template <int NC, int TH, int SB = 96>
 struct F32Stage {
     static constexpr int kLogN = NC == 8 ? 3 : NC == 4 ? 2 : NC == 2 ? 1 : 0;
     static constexpr int kBlocks = TH / 8;                            // block tasks per pass
-    static constexpr int kPass = (NC * 96 + kBlocks - 1) / kBlocks;  // rows of at most 96 blocks
+    static constexpr int kPass = (NC * SB + kBlocks - 1) / kBlocks;  // rows of at most SB blocks
+    static_assert(SB <= 96, "rows of at most 96 blocks");
     u32x4 v[kPass];
     __device__ __forceinline__ void load(rsrc_t xr, int nb, int K, uint32_t zero_off) {
         const uint32_t j = threadIdx.x & 7u, h = threadIdx.x >> 3;
@@ -482,7 +486,7 @@ struct F32Stage {
         for (int p = 0; p < kPass; ++p) {
             const uint32_t bt = (uint32_t)p * kBlocks + h;
             const uint32_t c = bt & (NC - 1), b = bt >> kLogN;
-            v[p] = ld128(xr, b < (uint32_t)nb ? (c * (uint32_t)K + b * 32u) * 4u + 16u * j : zero_off);
+            if (b < (uint32_t)SB) v[p] = ld128(xr, b < (uint32_t)nb ? (c * (uint32_t)K + b * 32u) * 4u + 16u * j : zero_off);
         }
     }
     template <int NS, int LPR>
@@ -493,6 +497,7 @@ struct F32Stage {
         for (int p = 0; p < kPass; ++p) {
             const uint32_t bt = (uint32_t)p * kBlocks + h;
             const uint32_t c = bt & (NC - 1), b = bt >> kLogN;
+            if (b >= (uint32_t)SB) continue;
             const uint32_t ts = ((b >> 4) << (4 + kLogN)) | (c << 4) | (b & 15u);
             // (each element copied out first: __builtin_bit_cast of a vector element in place
             // reads element 0 with this compiler)
@@ -552,7 +557,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     const uint32_t row_off = IQ4Consts::opaque_u((uint32_t)rowc * (uint32_t)row_bytes_dev<WT>(K));
 
     ActStage<NS, NC, LPR, TH> stage;
-    F32Stage<NC, TH> fstage;
+    F32Stage<NC, TH, (LPR * U < 96 ? LPR * U : 96)> fstage;
     if constexpr (F32) fstage.load(xr, act.nb, K, xbytes);
     else stage.load(xr, act, col0, ncp, xbytes);
     GridStage<TH> gstage;
