@@ -38,6 +38,27 @@ def test_quantize_extreme_blocks():
     assert np.array_equal(got, ref), f"{(got != ref).sum()} bytes differ"
 
 
+def test_quantize_near_ties():
+    """Quotients x / d within a few binary32 ulp of half-integers (and exactly on them), for
+    scales d that are not powers of two, where the quotient's rounding decides the byte: the
+    quantizer's bytes equal the oracle's (its division) on every value."""
+    print("quantize near ties", flush=True)
+    rng = synth.rng_for(7)
+    nblk = 6000
+    amax = np.exp2(rng.uniform(-30, 30, nblk)).astype(np.float32) * rng.uniform(1, 2, nblk).astype(np.float32)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    k = rng.integers(-127, 127, size=(nblk, 31)).astype(np.float64) + 0.5
+    rel = rng.choice(np.array([0.0, 1e-7, -1e-7, 3e-7, -3e-7, 2e-6, -2e-6, 1.5e-5, -1.5e-5, 3e-5, -3e-5]), size=(nblk, 31))
+    x = np.empty((nblk, 32), np.float32)
+    x[:, 0] = amax * np.where(rng.random(nblk) < 0.5, 1, -1).astype(np.float32)
+    x[:, 1:] = (k * (1.0 + rel) * d[:, None].astype(np.float64)).astype(np.float32)
+    x[:, 1:] = np.clip(x[:, 1:], -amax[:, None], amax[:, None])
+    x = x.reshape(1, -1)
+    ref = oracle.quantize_q8_1(x)
+    got = host(M.qmm_quantize_q8_1(dev(x)))
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} bytes differ"
+
+
 def test_quantize_rejects_ldx():
     assert M.lib().qmm_quantize_q8_1(None, 64, 1, 64, None, None) == -1
 
