@@ -684,6 +684,9 @@ def bench_dense(args, torch, M, cpu_s=3.0):
         fused = timed_graph(torch, fused_call, 10, g)
         deq = timed_graph(torch, lambda: M.qmm_dequant_f16(wt, wd, nrows, k, out=w16), 50, g)
         f16 = timed_graph(torch, lambda: M.qgemm_dense(M.QMM_F16, w16, nrows, k, xd, y=y), 10, g)
+        # reference: the vendor BLAS (torch.mm on the same FP16 operands, fp32 output)
+        xh = xd.view(torch.float16)
+        vendor = timed_graph(torch, lambda: torch.mm(xh, w16.t(), out_dtype=torch.float32), 10, g)
         flops = 2.0 * ntok * nrows * k
         tf = flops / (fused * 1e-3) / 1e12
         deq_bytes = nrows * synth.row_bytes(wt, k) + nrows * k * 2
@@ -694,6 +697,9 @@ def bench_dense(args, torch, M, cpu_s=3.0):
                           "f16_gemm_us": round(f16 * 1e3, 2),
                           "f16_gemm_tflops": round(flops / (f16 * 1e-3) / 1e12, 1),
                           "total_us": round((deq + f16) * 1e3, 2)},
+             "vendor_gemm_reference": {"us": round(vendor * 1e3, 2),
+                                       "tflops": round(flops / (vendor * 1e-3) / 1e12, 1),
+                                       "what": "torch.mm on the same FP16 operands, fp32 output (the vendor BLAS)"},
              "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops,
                           "traffic": rec["bytes_per_launch"].get(name) if rec else None,
