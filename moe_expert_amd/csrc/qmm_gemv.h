@@ -303,10 +303,10 @@ struct RowEngine {
     // address (clamped to the row's last block), computed just before its loads: on cold
     // weights the loads issued this way, a few instructions apart, finished ~0.2 us sooner
     // per call than the same loads issued back to back (the reverse held for Q8_0).
-    template <int N>
+    template <int N, int U0 = 0, int U1 = N>
     __device__ __forceinline__ void load(uint32_t (&buf)[N][RAW], int i0) {
 #pragma unroll
-        for (int u = 0; u < N; ++u) {
+        for (int u = U0; u < U1; ++u) {
             if constexpr (WT == kIQ4_NL) {
                 const int s = l16 + LPR * (i0 + u);
                 Unit<WT>::load(wr, Unit<WT>::frame(unit_off(s < nunits ? s : nunits - 1), 0), 0, buf[u]);
@@ -316,7 +316,14 @@ struct RowEngine {
         }
     }
 
-    __device__ __forceinline__ void load_first() { load(A, 0); }
+    // FIRST < U (single chunk only): blocks 0 .. FIRST - 1 now, the others once block 0 has been
+    // applied (run<FIRST>); the first blocks then land sooner and the last loads are issued
+    // while block 0 computes.
+    template <int FIRST = U>
+    __device__ __forceinline__ void load_first() {
+        if constexpr (MULTI || FIRST >= U) load(A, 0);
+        else load<U, 0, FIRST>(A, 0);
+    }
 
     // LDS reads of columns g CG .. g CG + CG - 1 of slot i (addresses relative to the chunk's
     // slot 0)
@@ -349,7 +356,7 @@ struct RowEngine {
         }
     }
 
-    template <int NCP, int N>
+    template <int NCP, int FIRST = U, int N>
     __device__ __forceinline__ void compute(const uint32_t (&buf)[N][RAW], int i0, const ActView& av, int ncp,
                                             const uint32_t* grid, float (&acc)[NC], int32_t* srow, int64_t scol,
                                             bool row_ok) {
@@ -403,16 +410,19 @@ struct RowEngine {
                     acc[c] = __builtin_fmaf(dwf * a.d[k], (float)isum, acc[c]);
                 }
             }
+            if constexpr (!MULTI && FIRST < U) {
+                if (n == NG - 1) load<U, FIRST, U>(A, 0);
+            }
             // keeps the reads of later groups from being hoisted here (two buffers at most)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    template <int NCP>
+    template <int NCP, int FIRST>
     __device__ __forceinline__ void run_pass(const ActView& av, int ncp, const uint32_t* grid, float (&acc)[NC],
                                              int32_t* srow, int64_t scol, bool row_ok) {
         if constexpr (!MULTI) {
-            compute<NCP>(A, 0, av, ncp, grid, acc, srow, scol, row_ok);
+            compute<NCP, FIRST>(A, 0, av, ncp, grid, acc, srow, scol, row_ok);
         } else {
             for (int i0 = 0; i0 < niter; i0 += 2 * U) {
                 const bool more = i0 + U < niter;
@@ -426,23 +436,24 @@ struct RowEngine {
         }
     }
 
-    // All of the lane's blocks; the first chunk must already be loaded (load_first).
+    // All of the lane's blocks; the first chunk must already be loaded (load_first<FIRST>).
+    template <int FIRST = U>
     __device__ __forceinline__ void run(const ActView& av, int ncp, const uint32_t* grid, float (&acc)[NC],
                                         int32_t* srow, int64_t scol, bool row_ok) {
         if constexpr (!VAR || NC == 1) {
-            run_pass<NC>(av, ncp, grid, acc, srow, scol, row_ok);
+            run_pass<NC, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
         } else {
-            if (ncp > NC / 2) run_pass<NC>(av, ncp, grid, acc, srow, scol, row_ok);
+            if (ncp > NC / 2) run_pass<NC, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
             else if constexpr (NC >= 4) {
-                if (ncp > NC / 4) run_pass<NC / 2>(av, ncp, grid, acc, srow, scol, row_ok);
+                if (ncp > NC / 4) run_pass<NC / 2, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
                 else if constexpr (NC >= 8) {
-                    if (ncp > 1) run_pass<2>(av, ncp, grid, acc, srow, scol, row_ok);
-                    else run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
+                    if (ncp > 1) run_pass<2, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
+                    else run_pass<1, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
                 } else {
-                    run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
+                    run_pass<1, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
                 }
             } else {
-                run_pass<1>(av, ncp, grid, acc, srow, scol, row_ok);
+                run_pass<1, FIRST>(av, ncp, grid, acc, srow, scol, row_ok);
             }
         }
     }
@@ -564,7 +575,10 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
     RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR, BUDGET> eng(wr, row_off, K, l16);
-    eng.load_first();
+    // fp32 columns: the workgroup's first weight loads are split (measured: one column of
+    // IQ4_NL 8192 x 2560 on cold weights 5.0 -> 4.6 us; the q8_1-input calls are not faster so)
+    constexpr int kFirst = F32 && !MULTI ? (U + 1) / 2 : U;
+    eng.template load_first<kFirst>();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (F32) fstage.template store<NS, LPR>(act);
     else stage.store(act);
@@ -583,7 +597,7 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
         srow = sums + ((int64_t)col0 * nrows + rowc) * act.nb;
         scol = (int64_t)nrows * act.nb;
     }
-    eng.run(act_view<NC>(act, l16), ncp, lds_grid, acc, srow, scol, row_ok);
+    eng.template run<kFirst>(act_view<NC>(act, l16), ncp, lds_grid, acc, srow, scol, row_ok);
     if constexpr (!SUMS) {
         const float s = row_sums<NC, LPR>(acc, l16);
         const int c = row_col<NC>(l16 & 15);
