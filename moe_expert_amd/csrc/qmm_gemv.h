@@ -575,9 +575,10 @@ __device__ __forceinline__ void gemv_tile(rsrc_t wr, int nrows, int K, const uin
     if constexpr (WT == kCB3) gstage.load(grid);
     __builtin_amdgcn_sched_barrier(0);
     RowEngine<WT, NC, SUMS, U, MULTI, LPR, VAR, BUDGET> eng(wr, row_off, K, l16);
-    // fp32 columns: the workgroup's first weight loads are split (measured: one column of
-    // IQ4_NL 8192 x 2560 on cold weights 5.0 -> 4.6 us; the q8_1-input calls are not faster so)
-    constexpr int kFirst = F32 && !MULTI ? (U + 1) / 2 : U;
+    // IQ4_NL on fp32 columns: the lane's weight loads are split (measured, one column on cold
+    // weights, same box: IQ4_NL 8192 x 2560 5.04 -> 4.58 us; not taken where it measured slower:
+    // the q8_1-input calls, 4.47 -> 4.70 us, and Q8_0 12288 x 2560, 8.49 -> 8.98 us)
+    constexpr int kFirst = F32 && !MULTI && WT == kIQ4_NL ? (U + 1) / 2 : U;
     eng.template load_first<kFirst>();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (F32) fstage.template store<NS, LPR>(act);
