@@ -371,19 +371,21 @@ __global__ __launch_bounds__((down_threads<WT, U, MULTI>()), (down_waves_per_sim
 
 // UM: chunk of the double-buffered (MULTI) instance, for rows of more than 6 blocks per lane
 // (2 in the gate/up kernels, whose lanes have 128 registers).
+// go(WT, U, MULTI, NS) receives the instance as std::integral_constant tags.
+template <int V>
+using IntC = std::integral_constant<int, V>;
 template <int WT, int UM = 6, typename F>
 static void dispatch_u_ns(Chunk ch, int ns, F&& go) {
     auto by_u = [&](auto ns_c) {
-        constexpr int NS = decltype(ns_c)::value;
-        if (ch.multi) go.template operator()<WT, UM, true, NS>();
-        else if (ch.u == 2) go.template operator()<WT, 2, false, NS>();
-        else if (ch.u == 5) go.template operator()<WT, 5, false, NS>();
-        else go.template operator()<WT, 6, false, NS>();
+        if (ch.multi) go(IntC<WT>{}, IntC<UM>{}, std::true_type{}, ns_c);
+        else if (ch.u == 2) go(IntC<WT>{}, IntC<2>{}, std::false_type{}, ns_c);
+        else if (ch.u == 5) go(IntC<WT>{}, IntC<5>{}, std::false_type{}, ns_c);
+        else go(IntC<WT>{}, IntC<6>{}, std::false_type{}, ns_c);
     };
-    if (ns == 1) by_u(std::integral_constant<int, 1>{});
-    else if (ns == 2) by_u(std::integral_constant<int, 2>{});
-    else if (ns == 3) by_u(std::integral_constant<int, 3>{});
-    else by_u(std::integral_constant<int, 4>{});
+    if (ns == 1) by_u(IntC<1>{});
+    else if (ns == 2) by_u(IntC<2>{});
+    else if (ns == 3) by_u(IntC<3>{});
+    else by_u(IntC<4>{});
 }
 
 struct GroupedArgs {
@@ -450,7 +452,9 @@ static int launch_grouped(const GroupedArgs& a) {
                                a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.xq, xqbytes, a.xq_cols,
                                a.group_expert, a.group_off, a.entry_col, a.nentries, a.ws, dbg_g, dbg_u);
         };
-        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
+        auto go = [&](auto wt_c, auto u_c, auto multi_c, auto ns_c) {
+            constexpr int WT = decltype(wt_c)::value, U = decltype(u_c)::value, NS = decltype(ns_c)::value;
+            constexpr bool MULTI = decltype(multi_c)::value;
             if constexpr (WT == kCB3 && (MULTI || U <= 5)) {
                 if (pair) {
                     launch(dense ? gu_kernel<WT, U, MULTI, NS, true, true> : gu_kernel<WT, U, MULTI, NS, false, true>,
@@ -472,7 +476,9 @@ static int launch_grouped(const GroupedArgs& a) {
     {
         const size_t lds = down_lds_bytes(a.wtype_down, a.inter);
         const dim3 grid_dim((unsigned)((a.hidden + kDownRows - 1) / kDownRows), (unsigned)a.ngroups);
-        auto go = [&]<int WT, int U, bool MULTI, int NS>() {
+        auto go = [&](auto wt_c, auto u_c, auto multi_c, auto ns_c) {
+            constexpr int WT = decltype(wt_c)::value, U = decltype(u_c)::value, NS = decltype(ns_c)::value;
+            constexpr bool MULTI = decltype(multi_c)::value;
             hipLaunchKernelGGL((down_kernel<WT, U, MULTI, NS>), grid_dim, dim3(down_threads<WT, U, MULTI>()), lds, a.st,
                                a.w_down,
                                a.d_stride, d_bytes, a.nexperts, a.grid, (int)a.hidden, (int)a.inter, a.ws,
