@@ -114,6 +114,20 @@ def test_grouped_long_rows(hidden):
     run_case(ex, ge, go, ec, 6, 852)
 
 
+@pytest.mark.parametrize("wt_gu,hidden", [(M.QMM_IQ4_NL, 2560), (M.QMM_Q8_0, 2560), (M.QMM_IQ4_NL, 3072),
+                                          (M.QMM_Q8_0, 1536)])
+def test_grouped_gate_up_rows(wt_gu, hidden):
+    """IQ4_NL and Q8_0 gate/up rows of 5, 6 and 3 blocks per lane (1024-thread workgroups, one row
+    per lane, the first blocks loaded before the staging and the rest after block 0), with a
+    group of 9 entries (two passes) and one of 1."""
+    print(f"grouped gate/up rows: gu={wt_gu}, hidden {hidden}, groups of 9 and 1 entries", flush=True)
+    ex = Experts(870 + hidden + wt_gu, 3, hidden, 96, wt_gu=wt_gu, wt_down=M.QMM_IQ4_NL)
+    ge = np.array([2, 0], np.int32)
+    go = np.array([0, 9, 10], np.int32)
+    ec = synth.rng_for(871 + hidden).integers(0, 5, size=10).astype(np.int32)
+    run_case(ex, ge, go, ec, 5, 872 + hidden)
+
+
 @pytest.mark.parametrize("wt_down,inter", [(M.QMM_IQ4_NL, 4096), (M.QMM_CB3, 512), (M.QMM_Q8_0, 256)])
 def test_grouped_down_shapes(wt_down, inter):
     """The down kernel's instances: long rows (inter 4096, the double-buffered tile), CB3 rows
